@@ -1,0 +1,94 @@
+"""Tie-free conditioning of seeded indexer inputs (oracle side; tests only).
+
+The top-k set is compared bit for bit, but a GPU accumulates the indexer score
+in fp32 in an order of its own choosing.  This module certifies, per query, that
+no fp32 evaluation order can change the set: every selected entry beats every
+unselected one by more than the worst-case accumulation error.
+
+Error bound: with exact products (a bf16 x bf16 product, and an FP4-decoded x
+bf16 product, both fit in fp32) the fp32 value of
+s_j = sum_h w_h ReLU(sum_c q_hc k_jc) differs from the exact one by at most
+E_j = (d_I + H_I + 4) * 2**-23 * T_j,  T_j = sum_h |w_h| sum_c |q_hc k_jc|
+for any summation order and for round-to-nearest or round-toward-zero adds
+(the classical bound gamma_n * sum|terms| with unit 2**-23 and ReLU being
+1-Lipschitz).
+
+Procedure for a query: take S = the oracle's top-k set.  Any unselected j with
+s_j + E_j >= min_{i in S}(s_i - E_i) has its source bf16 key row halved (exact in
+bf16; the ReLU form makes the score halve as well), the row is re-encoded in the
+cache format, and the check repeats until it holds.  The adjusted keys are then
+the test input for both the oracle and the GPU.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import formats
+from .decode import indexer_scores, topk_indices
+
+
+def _decode_keys(bits: np.ndarray, fmt: str) -> np.ndarray:
+    vals = formats.bf16_bits_to_f64(bits)
+    if fmt == "bf16":
+        return vals
+    if fmt == "fp4":
+        codes, scales = formats.fp4_quantize(vals)
+        return formats.fp4_dequantize(codes, scales)
+    raise ValueError(fmt)
+
+
+def make_tie_free(key_bits, q_idx, w_idx, top_k: int, fmt: str, max_iter: int = 64):
+    """Return (adjusted key bf16 bits [B][N_c][d_I], certificates list).
+
+    key_bits: uint16 bf16 bit patterns [B][N_c][d_I]; q_idx: [B][H_I][d_I] values;
+    w_idx: [B][H_I] values; fmt: "bf16" or "fp4" (the stored key format).
+    """
+    keys = np.array(key_bits, dtype=np.uint16, copy=True)
+    q_all = np.asarray(q_idx, dtype=np.float64)
+    w_all = np.asarray(w_idx, dtype=np.float64)
+    B, n_c, d_i = keys.shape
+    h_i = q_all.shape[1]
+    c_err = (d_i + h_i + 4) * 2.0 ** -23
+    certs = []
+    for b in range(B):
+        q = q_all[b]
+        w = w_all[b]
+        kd = _decode_keys(keys[b], fmt)
+        s = indexer_scores(q, w, kd)
+        t = (np.abs(kd) @ np.abs(q).T) @ np.abs(w)
+        halved = 0
+        for _ in range(max_iter):
+            if n_c <= top_k:
+                break
+            sel = topk_indices(s, top_k)
+            in_s = np.zeros(n_c, dtype=bool)
+            in_s[sel] = True
+            e = c_err * t
+            lo = np.min(s[in_s] - e[in_s])
+            bad = np.nonzero((~in_s) & (s + e >= lo))[0]
+            if bad.size == 0:
+                break
+            vals = formats.bf16_bits_to_f64(keys[b, bad]) * 0.5
+            keys[b, bad] = formats.f64_to_bf16_bits(vals)
+            kd_bad = _decode_keys(keys[b, bad], fmt)
+            kd[bad] = kd_bad
+            s[bad] = indexer_scores(q, w, kd_bad)
+            t[bad] = (np.abs(kd_bad) @ np.abs(q).T) @ np.abs(w)
+            halved += bad.size
+        else:
+            raise RuntimeError(f"query {b}: no tie-free certificate after {max_iter} rounds")
+        if n_c > top_k:
+            sel = topk_indices(s, top_k)
+            in_s = np.zeros(n_c, dtype=bool)
+            in_s[sel] = True
+            e = c_err * t
+            lo = float(np.min(s[in_s] - e[in_s]))
+            hi = float(np.max(s[~in_s] + e[~in_s]))
+            if not lo > 0.0:
+                raise RuntimeError(f"query {b}: selection boundary not above zero")
+            certs.append({"query": b, "rows_halved": int(halved), "low_selected": lo,
+                          "high_unselected": hi})
+        else:
+            certs.append({"query": b, "rows_halved": 0, "low_selected": None,
+                          "high_unselected": None})
+    return keys, certs
