@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""CSA decode benchmark on one MI355X: query-tokens/s and achieved HBM GB/s.
+
+A step is one pass of the decode hot path over one batch: the indexer scores every
+compressed entry of each query's sequence, keeps the top-512, and attends over those
+entries plus the 128-row sliding window (csa_decode, FULL mode).  The default workload
+is the 1M-token context with mixed FP8/BF16 shared-KV rows and FP4 indexer keys,
+B = 4 query tokens.  Inputs are synthetic and seed-generated, and resident in HBM
+before timing starts; R replicas of every cache (>= 1 GiB in all) rotate across steps
+so that the 256 MB Infinity Cache cannot serve a step from the previous one.
+
+Output: one JSON line (rank 0).  `roofline` reports the dominant stage (the indexer
+scan + top-k, csa_select_topk) timed with HIP events on the stream it runs on;
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "CSA decode query-tokens/s + achieved HBM GB/s, top-512 @1M ctx, 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 1 << 30
+
+WORKLOADS = {
+    # name: B, N_c, window, H_q, H_I, top_k, kv format, indexer format, seed
+    "csa_mixed_1m": dict(B=4, n_c=262144, window=128, hq=64, hi=64, top_k=512, kv="mixed",
+                         idx="fp4", seed=4, context=1 << 20),
+    "csa_bf16_131k": dict(B=32, n_c=32768, window=128, hq=64, hi=64, top_k=512, kv="bf16",
+                          idx="bf16", seed=2, context=131072),
+    "csa_fp4_1m": dict(B=8, n_c=262144, window=128, hq=64, hi=64, top_k=512, kv="fp4",
+                       idx="fp4", seed=5, context=1 << 20),
+}
+KV_ROW_BYTES = {"bf16": 1024, "mixed": 576, "fp4": 256 + 32}
+IDX_ROW_BYTES = {"bf16": 256, "fp4": 64 + 8}
+
+
+def algorithmic_bytes(w: dict) -> dict:
+    """Bytes the method itself moves per step (no workspace, re-reads or padding)."""
+    B, n_c, k = w["B"], w["n_c"], w["top_k"]
+    rows = min(k, n_c) + w["window"]
+    idx = B * (n_c * IDX_ROW_BYTES[w["idx"]] + w["hi"] * 128 * 2 + w["hi"] * 4 + k * 4)
+    attn = B * (rows * KV_ROW_BYTES[w["kv"]] + 2 * w["hq"] * 512 * 2)
+    return {"indexer": idx, "attention": attn, "step": idx + attn}
+
+
+def build_inputs(w: dict, replicas: int):
+    import torch
+    import compressed_sparse_kv_csa_amd as ck
+    import seedgen
+
+    dev = "cuda"
+    T = seedgen.TID
+    B, n_c, W = w["B"], w["n_c"], w["window"]
+    rows = W + n_c
+    # One set of caches, generated and quantised on the GPU, then copied per replica.
+    keys16 = seedgen.bf16_normal(w["seed"], seedgen.tid(T.IDX_KEYS), (B, n_c, 128), dev)
+    if w["idx"] == "fp4":
+        k_codes = torch.empty((B, n_c, 64), dtype=torch.uint8, device=dev)
+        k_scales = torch.empty((B, n_c, 8), dtype=torch.uint8, device=dev)
+        ck.kv_quantize_fp4(keys16, B * n_c, 128, k_codes, k_scales)
+    else:
+        k_codes, k_scales = keys16, None
+    kv16 = seedgen.kv_rows_bf16(w["seed"], seedgen.tid(T.KV), (B, rows, 512), dev)
+    if w["kv"] == "mixed":
+        kv_codes, kv_scales = torch.empty((B, rows, 576), dtype=torch.uint8, device=dev), None
+        ck.kv_quantize_fp8(kv16, B * rows, 512, 448, kv_codes)
+    elif w["kv"] == "fp4":
+        kv_codes = torch.empty((B, rows, 256), dtype=torch.uint8, device=dev)
+        kv_scales = torch.empty((B, rows, 32), dtype=torch.uint8, device=dev)
+        ck.kv_quantize_fp4(kv16, B * rows, 512, kv_codes, kv_scales)
+    else:
+        kv_codes, kv_scales = kv16, None
+    torch.cuda.synchronize()
+    del kv16
+    if w["idx"] == "fp4":
+        del keys16
+    kv_fmt = {"bf16": ck.KV_BF16, "mixed": ck.KV_FP8_MIXED, "fp4": ck.KV_FP4}[w["kv"]]
+    idx_fmt = {"bf16": ck.IDX_BF16, "fp4": ck.IDX_FP4}[w["idx"]]
+    reps = []
+    for r in range(replicas):
+        def cp(t):
+            return None if t is None else (t if r == 0 else t.clone())
+        rep = dict(kc=cp(k_codes), ks=cp(k_scales), vc=cp(kv_codes), vs=cp(kv_scales))
+        # Distinct queries per replica (their own top-k rows).
+        s = w["seed"] * 1000 + r
+        rep["q"] = seedgen.bf16_normal(s, seedgen.tid(T.Q), (B, w["hq"], 512), dev)
+        rep["qi"] = seedgen.bf16_normal(s, seedgen.tid(T.Q_IDX), (B, w["hi"], 128), dev)
+        rep["w"] = seedgen.uniform01(s, seedgen.tid(T.W_IDX), (B, w["hi"]), dev)
+        rep["kv"] = ck.cache(kv_fmt, rep["vc"], rows, rows, rep["vs"])
+        rep["idx"] = ck.cache(idx_fmt, rep["kc"], n_c, n_c, rep["ks"])
+        rep["topk"] = torch.empty((B, w["top_k"]), dtype=torch.int32, device=dev)
+        rep["out"] = torch.empty((B, w["hq"], 512), dtype=torch.bfloat16, device=dev)
+        reps.append(rep)
+    torch.cuda.synchronize()
+    return reps
+
+
+def run_gpu(w: dict, steps: int, warmup: int, replicas: int | None):
+    import torch
+    import compressed_sparse_kv_csa_amd as ck
+
+    nbytes = algorithmic_bytes(w)
+    R = replicas or max(2, math.ceil(MALL_BYTES / nbytes["step"]))
+    reps = build_inputs(w, R)
+    p = ck.CsaParams(w["B"], w["hq"], w["hi"], w["top_k"], w["window"], ck.MODE_FULL,
+                     1.0 / math.sqrt(512), 0)
+    ws_bytes = ck.csa_decode_workspace_bytes(p, w["n_c"])
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def step(i):
+        r = reps[i % R]
+        ck.csa_decode(p, r["kv"], r["idx"], r["q"], r["qi"], r["w"], r["topk"], r["out"], ws,
+                      ws_bytes, stream=sh)
+
+    def select(i):
+        r = reps[i % R]
+        ck.csa_select_topk(p, r["idx"], r["qi"], r["w"], r["topk"], ws, ws_bytes, stream=sh)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1) / steps
+
+    # Dominant stage: indexer scan + top-k, one event pair per launch on its stream.
+    for i in range(warmup):
+        select(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        select(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    sel_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    return dict(ms=ms, wall=wall, sel_ms=sel_ms, replicas=R, bytes=nbytes)
+
+
+def run_cpu_baseline(w: dict, queries: int):
+    """The oracle, untuned, on `queries` query tokens of the same workload (seed, shapes)."""
+    import numpy as np
+    import torch
+    import seedgen
+    from oracle import decode as OD, formats as OF
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    T = seedgen.TID
+    n_c, W, k = w["n_c"], w["window"], w["top_k"]
+    dev = "cuda" if torch.cuda.is_available() else "cpu"
+    s = w["seed"] * 1000           # replica 0's queries
+    q = seedgen.bf16_normal(s, seedgen.tid(T.Q), (w["B"], w["hq"], 512), dev)[:queries]
+    qi = seedgen.bf16_normal(s, seedgen.tid(T.Q_IDX), (w["B"], w["hi"], 128), dev)[:queries]
+    wv = seedgen.uniform01(s, seedgen.tid(T.W_IDX), (w["B"], w["hi"]), dev)[:queries]
+    q = q.float().cpu().double().numpy()
+    qi = qi.float().cpu().double().numpy()
+    wv = wv.cpu().double().numpy()
+
+    def bits(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    # Untimed preparation by the oracle's own encoders: every indexer key, and the KV rows
+    # the decode reads (window + the oracle's own top-k); unread rows stay zero.
+    keys = bits(seedgen.bf16_normal(w["seed"], seedgen.tid(T.IDX_KEYS), (w["B"], n_c, 128), dev)[:queries])
+    caches = []
+    kv_all = seedgen.kv_rows_bf16(w["seed"], seedgen.tid(T.KV), (w["B"], W + n_c, 512), dev)
+    for b in range(queries):
+        vals = OF.bf16_bits_to_f64(keys[b])
+        if w["idx"] == "fp4":
+            kc = OF.fp4_quantize(vals)
+            kd = OF.fp4_dequantize(*kc)
+        else:
+            kc, kd = keys[b], vals
+        sel = OD.topk_indices(OD.indexer_scores(qi[b], wv[b], kd), k)
+        need = np.concatenate([np.arange(W), W + sel[sel >= 0]])
+        row_bits = bits(kv_all[b, torch.from_numpy(need).to(kv_all.device)])
+        if w["kv"] == "mixed":
+            enc = OF.mixed_quantize(row_bits)
+            full = np.zeros((W + n_c, 576), dtype=np.uint8)
+        elif w["kv"] == "fp4":
+            c, sc = OF.fp4_quantize(OF.bf16_bits_to_f64(row_bits))
+            enc = (c, sc)
+            full = (np.zeros((W + n_c, 256), np.uint8), np.zeros((W + n_c, 32), np.uint8))
+        else:
+            enc, full = row_bits, np.zeros((W + n_c, 512), dtype=np.uint16)
+        if isinstance(full, tuple):
+            full[0][need], full[1][need] = enc
+        else:
+            full[need] = enc
+        caches.append((kc, full))
+    del kv_all
+
+    def decode_rows(full, idx):
+        if w["kv"] == "mixed":
+            return OF.mixed_dequantize(full[idx])
+        if w["kv"] == "fp4":
+            return OF.fp4_dequantize(full[0][idx], full[1][idx])
+        return OF.bf16_bits_to_f64(full[idx])
+
+    t0 = time.perf_counter()
+    for b in range(queries):
+        kc, full = caches[b]
+        kd = OF.fp4_dequantize(*kc) if w["idx"] == "fp4" else OF.bf16_bits_to_f64(kc)
+        sel = OD.topk_indices(OD.indexer_scores(qi[b], wv[b], kd), k)
+        rows = decode_rows(full, np.concatenate([np.arange(W), W + sel[sel >= 0]]))
+        OD.attention(q[b], rows, 1.0 / math.sqrt(512))
+    dt = time.perf_counter() - t0
+    return {"value": round(queries / dt, 4), "unit": "query-tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{queries} of the {w['B']} query tokens of one step (same seeds and shapes): "
+                      f"{n_c} {w['idx']} indexer keys each, then {W}+{k} {w['kv']} rows; "
+                      f"numpy fp64, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="csa_mixed_1m", choices=sorted(WORKLOADS))
+    ap.add_argument("--replicas", type=int, default=None)
+    ap.add_argument("--cpu-queries", type=int, default=None,
+                    help="query tokens in the oracle sample (default: one step's batch)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (HIP device) to run.", file=sys.stderr)
+        sys.exit(1)
+    w = WORKLOADS[args.workload]
+    g = run_gpu(w, args.steps, args.warmup, args.replicas)
+    B = w["B"]
+    tok_s = B / (g["ms"] * 1e-3)
+    step_gbps = g["bytes"]["step"] / (g["ms"] * 1e-3) / 1e9
+    sel_gbps = g["bytes"]["indexer"] / (g["sel_ms"] * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = run_cpu_baseline(w, args.cpu_queries or B)
+    line = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(g["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "context_tokens": w["context"],
+                   "n_compressed": w["n_c"], "top_k": w["top_k"], "window": w["window"],
+                   "q_heads": w["hq"], "idx_heads": w["hi"], "kv_format": w["kv"],
+                   "idx_format": w["idx"], "replicas": g["replicas"]},
+        "hbm_gbps": round(step_gbps, 1),
+        "algorithmic_bytes_per_step": g["bytes"]["step"],
+        "roofline": {"bound": "hbm", "achieved": round(sel_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(sel_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "indexer stage (csa_select_topk)",
+                     "avg_launch_us": round(g["sel_ms"] * 1e3, 2),
+                     "algorithmic_bytes_per_launch": g["bytes"]["indexer"]},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,274 @@
+// C ABI of the csakv library: argument validation, workspace layout, dispatch.
+// Every check runs on the host before any launch; a rejected call enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/csakv.h"
+#include "csakv_launch.h"
+
+namespace {
+
+constexpr int kKvDim = 512;
+constexpr int kNopeDim = 448;
+constexpr size_t kWsAlign = 256;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+csakv_status hip_status(hipError_t e) { return e == hipSuccess ? CSAKV_OK : CSAKV_ERR_HIP; }
+
+// Checks a cache descriptor: format, row counts, pointers and alignment.
+csakv_status check_cache(const csakv_cache* c, bool is_kv) {
+  if (!c || c->reserved != 0) return CSAKV_ERR_INVALID;
+  const int nfmt = is_kv ? 3 : 2;
+  if (c->fmt < 0 || c->fmt >= nfmt) return CSAKV_ERR_INVALID;
+  if (c->n_rows < 0 || c->seq_stride_rows < c->n_rows) return CSAKV_ERR_INVALID;
+  // A cache without rows may have null pointers; any pointer given must be aligned.
+  const bool empty = c->n_rows == 0;
+  if ((!empty && !c->codes) || !aligned(c->codes, 16)) return CSAKV_ERR_INVALID;
+  const bool fp4 = is_kv ? c->fmt == CSAKV_KV_FP4 : c->fmt == CSAKV_IDX_FP4;
+  if (fp4) {
+    if ((!empty && !c->scales) || !aligned(c->scales, 16)) return CSAKV_ERR_INVALID;
+  } else if (c->scales) {
+    return CSAKV_ERR_INVALID;
+  }
+  return CSAKV_OK;
+}
+
+struct CsaLayout {
+  csakv::IndexerPlan idx;
+  csakv::AttnPlan attn;
+  size_t idx_bytes, attn_offset, total;
+};
+
+CsaLayout csa_layout(const csakv_csa_params* p, int64_t n_c) {
+  CsaLayout L{};
+  L.idx_bytes = 0;
+  if (p->mode == CSAKV_MODE_FULL) {
+    L.idx = csakv::plan_indexer(p->batch, n_c, p->top_k);
+    L.idx_bytes = round_up(csakv::indexer_workspace_bytes(p->batch, L.idx), kWsAlign);
+  }
+  L.attn = csakv::plan_attention(p->batch, (int64_t)p->window + p->top_k, true);
+  L.attn_offset = L.idx_bytes;
+  L.total = L.idx_bytes + round_up(csakv::attention_workspace_bytes(p->batch, p->n_q_heads, L.attn), kWsAlign);
+  return L;
+}
+
+// Parameters the indexer stage reads (FULL mode).
+csakv_status check_select_params(const csakv_csa_params* p) {
+  if (p->reserved != 0 || p->batch < 1 || p->top_k < 1 || p->n_idx_heads < 1)
+    return CSAKV_ERR_INVALID;
+  if (p->top_k > csakv::kMaxTopK || p->n_idx_heads > 64) return CSAKV_ERR_UNSUPPORTED;
+  return CSAKV_OK;
+}
+
+csakv_status check_csa_params(const csakv_csa_params* p) {
+  if (!p || p->reserved != 0) return CSAKV_ERR_INVALID;
+  if (p->batch < 1 || p->window < 0 || !std::isfinite(p->softmax_scale)) return CSAKV_ERR_INVALID;
+  if (p->mode != CSAKV_MODE_FULL && p->mode != CSAKV_MODE_REUSE) return CSAKV_ERR_INVALID;
+  if (p->top_k < 1 || p->n_q_heads < 1) return CSAKV_ERR_INVALID;
+  if (p->top_k > csakv::kMaxTopK) return CSAKV_ERR_UNSUPPORTED;
+  if (p->n_q_heads % 16 != 0 || p->n_q_heads > 64) return CSAKV_ERR_UNSUPPORTED;
+  if (p->mode == CSAKV_MODE_FULL) return check_select_params(p);
+  return CSAKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csakv_status_string(int32_t status) {
+  switch (status) {
+    case CSAKV_OK: return "ok";
+    case CSAKV_ERR_INVALID: return "invalid argument";
+    case CSAKV_ERR_UNSUPPORTED: return "unsupported shape or format";
+    case CSAKV_ERR_WORKSPACE: return "workspace too small";
+    case CSAKV_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t csa_decode_workspace_bytes(const csakv_csa_params* p, int64_t n_compressed) {
+  if (check_csa_params(p) != CSAKV_OK || n_compressed < 0) return 0;
+  return csa_layout(p, n_compressed).total;
+}
+
+csakv_status csa_decode(const csakv_csa_params* p, const csakv_cache* kv,
+                        const csakv_cache* idx_keys, const uint16_t* q, const uint16_t* q_idx,
+                        const float* w_idx, int32_t* topk, uint16_t* out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  csakv_status st = check_csa_params(p);
+  if (st != CSAKV_OK) return st;
+  if ((st = check_cache(kv, true)) != CSAKV_OK) return st;
+  if (kv->n_rows < p->window) return CSAKV_ERR_INVALID;
+  const int64_t n_c = kv->n_rows - p->window;
+  if (n_c > INT32_MAX) return CSAKV_ERR_UNSUPPORTED;
+  if (!q || !out || !topk || !aligned(q, 16) || !aligned(out, 16) || !aligned(topk, 4))
+    return CSAKV_ERR_INVALID;
+  const bool full = p->mode == CSAKV_MODE_FULL;
+  if (full) {
+    if ((st = check_cache(idx_keys, false)) != CSAKV_OK) return st;
+    if (idx_keys->n_rows != n_c) return CSAKV_ERR_INVALID;
+    if (!q_idx || !w_idx || !aligned(q_idx, 16) || !aligned(w_idx, 4)) return CSAKV_ERR_INVALID;
+  } else if (idx_keys || q_idx || w_idx) {
+    return CSAKV_ERR_INVALID;
+  }
+  const CsaLayout L = csa_layout(p, n_c);
+  if (full && (int64_t)L.idx.n_slices * L.idx.prefix > csakv::kMergeCap) return CSAKV_ERR_UNSUPPORTED;
+  if (workspace_bytes < L.total) return CSAKV_ERR_WORKSPACE;
+  if (L.total > 0 && (!workspace || !aligned(workspace, kWsAlign))) return CSAKV_ERR_INVALID;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  if (full) {
+    hipError_t e = csakv::launch_indexer(
+        idx_keys->fmt, static_cast<const uint8_t*>(idx_keys->codes), idx_keys->scales,
+        idx_keys->seq_stride_rows, n_c, q_idx, w_idx, p->batch, p->n_idx_heads, p->top_k, L.idx,
+        ws, topk, s);
+    if (e != hipSuccess) return CSAKV_ERR_HIP;
+  }
+  return hip_status(csakv::launch_attention(
+      kv->fmt, true, static_cast<const uint8_t*>(kv->codes), kv->scales, kv->seq_stride_rows,
+      kv->n_rows, q, p->batch, p->n_q_heads, p->softmax_scale, topk, p->top_k, p->window, L.attn,
+      ws + L.attn_offset, out, s));
+}
+
+size_t csa_select_topk_workspace_bytes(const csakv_csa_params* p, int64_t n_compressed) {
+  if (!p || p->mode != CSAKV_MODE_FULL || check_select_params(p) != CSAKV_OK || n_compressed < 0)
+    return 0;
+  const csakv::IndexerPlan plan = csakv::plan_indexer(p->batch, n_compressed, p->top_k);
+  return round_up(csakv::indexer_workspace_bytes(p->batch, plan), kWsAlign);
+}
+
+csakv_status csa_select_topk(const csakv_csa_params* p, const csakv_cache* idx_keys,
+                             const uint16_t* q_idx, const float* w_idx, int32_t* topk,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (!p || p->mode != CSAKV_MODE_FULL) return CSAKV_ERR_INVALID;
+  csakv_status st = check_select_params(p);
+  if (st != CSAKV_OK) return st;
+  if ((st = check_cache(idx_keys, false)) != CSAKV_OK) return st;
+  if (idx_keys->n_rows > INT32_MAX) return CSAKV_ERR_UNSUPPORTED;
+  if (!q_idx || !w_idx || !topk || !aligned(q_idx, 16) || !aligned(w_idx, 4) || !aligned(topk, 4))
+    return CSAKV_ERR_INVALID;
+  const int64_t n_c = idx_keys->n_rows;
+  const csakv::IndexerPlan plan = csakv::plan_indexer(p->batch, n_c, p->top_k);
+  if ((int64_t)plan.n_slices * plan.prefix > csakv::kMergeCap) return CSAKV_ERR_UNSUPPORTED;
+  const size_t need = round_up(csakv::indexer_workspace_bytes(p->batch, plan), kWsAlign);
+  if (workspace_bytes < need) return CSAKV_ERR_WORKSPACE;
+  if (need > 0 && (!workspace || !aligned(workspace, kWsAlign))) return CSAKV_ERR_INVALID;
+  return hip_status(csakv::launch_indexer(
+      idx_keys->fmt, static_cast<const uint8_t*>(idx_keys->codes), idx_keys->scales,
+      idx_keys->seq_stride_rows, n_c, q_idx, w_idx, p->batch, p->n_idx_heads, p->top_k, plan,
+      workspace, topk, static_cast<hipStream_t>(stream)));
+}
+
+size_t hca_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int64_t n_rows) {
+  if (batch < 1 || n_q_heads < 1 || n_rows < 0) return 0;
+  csakv::AttnPlan a = csakv::plan_attention(batch, n_rows, false);
+  return round_up(csakv::attention_workspace_bytes(batch, n_q_heads, a), kWsAlign);
+}
+
+csakv_status hca_decode(int32_t batch, int32_t n_q_heads, float softmax_scale,
+                        const csakv_cache* kv, const uint16_t* q, uint16_t* out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (batch < 1 || n_q_heads < 1 || !std::isfinite(softmax_scale)) return CSAKV_ERR_INVALID;
+  if (n_q_heads % 16 != 0 || n_q_heads > 64) return CSAKV_ERR_UNSUPPORTED;
+  csakv_status st = check_cache(kv, true);
+  if (st != CSAKV_OK) return st;
+  if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return CSAKV_ERR_INVALID;
+  const size_t need = hca_decode_workspace_bytes(batch, n_q_heads, kv->n_rows);
+  if (workspace_bytes < need) return CSAKV_ERR_WORKSPACE;
+  if (need > 0 && (!workspace || !aligned(workspace, kWsAlign))) return CSAKV_ERR_INVALID;
+  csakv::AttnPlan a = csakv::plan_attention(batch, kv->n_rows, false);
+  return hip_status(csakv::launch_attention(
+      kv->fmt, false, static_cast<const uint8_t*>(kv->codes), kv->scales, kv->seq_stride_rows,
+      kv->n_rows, q, batch, n_q_heads, softmax_scale, nullptr, 0, 0, a, workspace, out,
+      static_cast<hipStream_t>(stream)));
+}
+
+csakv_status kv_quantize_fp4(const uint16_t* x, int64_t rows, int32_t dim, uint8_t* codes,
+                             uint8_t* scales, void* stream) {
+  if (rows < 0 || dim <= 0 || dim % 16 != 0) return CSAKV_ERR_INVALID;
+  if (!x || !codes || !scales || !aligned(x, 16) || !aligned(codes, 8)) return CSAKV_ERR_INVALID;
+  return hip_status(csakv::launch_quantize_fp4(x, rows, dim, codes, scales,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+csakv_status kv_quantize_fp8(const uint16_t* x, int64_t rows, int32_t dim, int32_t nope_dim,
+                             uint8_t* out, void* stream) {
+  if (rows < 0 || dim <= 0 || dim % 16 != 0 || nope_dim < 0 || nope_dim > dim ||
+      nope_dim % 16 != 0)
+    return CSAKV_ERR_INVALID;
+  if (!x || !out || !aligned(x, 16) || !aligned(out, 16)) return CSAKV_ERR_INVALID;
+  return hip_status(csakv::launch_quantize_fp8_mixed(x, rows, dim, nope_dim, out,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
+csakv_status kv_dequantize(int32_t fmt, const void* codes, const uint8_t* scales, int64_t rows,
+                           int32_t dim, uint16_t* out, void* stream) {
+  if (rows < 0 || dim <= 0 || dim % 16 != 0) return CSAKV_ERR_INVALID;
+  if (!codes || !out || !aligned(codes, 16) || !aligned(out, 16)) return CSAKV_ERR_INVALID;
+  int nope = 0;
+  if (fmt == CSAKV_KV_BF16) {
+    if (scales) return CSAKV_ERR_INVALID;
+  } else if (fmt == CSAKV_KV_FP8_MIXED) {
+    if (scales) return CSAKV_ERR_INVALID;
+    if (dim != kKvDim) return CSAKV_ERR_UNSUPPORTED;
+    nope = kNopeDim;
+  } else if (fmt == CSAKV_KV_FP4) {
+    if (!scales || !aligned(codes, 8)) return CSAKV_ERR_INVALID;
+  } else {
+    return CSAKV_ERR_INVALID;
+  }
+  return hip_status(csakv::launch_dequantize(fmt, codes, scales, rows, dim, nope, out,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+uint64_t kv_cache_bytes(const kv_cache_spec* sp, int64_t seq_len, kv_cache_breakdown* out) {
+  if (!sp || seq_len < 0 || sp->reserved != 0) return 0;
+  if (sp->n_csa < 0 || sp->n_hca < 0 || sp->n_swa < 0 || sp->csa_ratio < 1 || sp->hca_ratio < 1 ||
+      sp->window < 0 || sp->kv_dim <= 0 || sp->rope_dim < 0 || sp->rope_dim > sp->kv_dim ||
+      sp->idx_dim < 0 || sp->count_window < 0 || sp->count_window > 2 || sp->count_scales < 0 ||
+      sp->count_scales > 1 || sp->swa_layer_bytes < 0)
+    return 0;
+  uint64_t s_kv;
+  switch (sp->kv_fmt) {
+    case CSAKV_KV_BF16: s_kv = 2ull * sp->kv_dim; break;
+    case CSAKV_KV_FP8_MIXED: s_kv = (uint64_t)(sp->kv_dim - sp->rope_dim) + 2ull * sp->rope_dim; break;
+    case CSAKV_KV_FP4:
+      if (sp->kv_dim % 16) return 0;
+      s_kv = sp->kv_dim / 2 + (sp->count_scales ? sp->kv_dim / 16 : 0);
+      break;
+    default: return 0;
+  }
+  uint64_t s_idx = 0;
+  if (sp->idx_dim > 0) {
+    switch (sp->idx_fmt) {
+      case CSAKV_IDX_BF16: s_idx = 2ull * sp->idx_dim; break;
+      case CSAKV_IDX_FP4:
+        if (sp->idx_dim % 16) return 0;
+        s_idx = sp->idx_dim / 2 + (sp->count_scales ? sp->idx_dim / 16 : 0);
+        break;
+      default: return 0;
+    }
+  }
+  const uint64_t n = (uint64_t)seq_len;
+  const uint64_t n_c = sp->n_csa ? n / sp->csa_ratio : 0;
+  const uint64_t n_h = sp->n_hca ? n / sp->hca_ratio : 0;
+  const uint64_t win = (uint64_t)sp->count_window * sp->window * s_kv;
+  kv_cache_breakdown r{};
+  r.csa_per_layer = n_c * s_kv + n_c * s_idx + win;
+  r.hca_per_layer = n_h * s_kv + win;
+  r.csa_shared_kv = sp->n_csa * n_c * s_kv;
+  r.csa_indexer = sp->n_csa * n_c * s_idx;
+  r.hca_shared_kv = sp->n_hca * n_h * s_kv;
+  r.windows = (uint64_t)(sp->n_csa + sp->n_hca) * win;
+  r.swa_layers = (uint64_t)sp->n_swa * (uint64_t)sp->swa_layer_bytes;
+  r.total = sp->n_csa * r.csa_per_layer + sp->n_hca * r.hca_per_layer + r.swa_layers;
+  if (out) *out = r;
+  return r.total;
+}
+
+}  // extern "C"

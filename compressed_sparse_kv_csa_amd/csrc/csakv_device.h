@@ -1,0 +1,117 @@
+// Device-side helpers shared by the csakv HIP kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csakv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16 bits
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bit pattern (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t lsb = (u >> 16) & 1u;
+  return (u + 0x7FFFu + lsb) >> 16;
+}
+
+// Two fp32 values that are exactly representable in bf16 -> packed bf16x2 bits.
+__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+}
+
+// ---------------------------------------------------------------- OCP E4M3FN
+
+// Value of an E4M3FN code (NaN codes are never produced by this library's encoders
+// and are decoded as the pattern the hardware conversion gives).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+  f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8(code & 0xFFu, false);
+  return v[0];
+}
+
+// E4M3FN code of x: round to nearest even on the finite grid, saturating at +-448,
+// sign kept.  Exact integer/power-of-two arithmetic only.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  float a = fabsf(x);
+  if (!(a < 448.0f)) return sign | 0x7Eu;                 // also catches +inf
+  int e = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;  // floor(log2 a) for normal a
+  if (e < -6) e = -6;                                      // subnormal quantum 2^-9
+  float q = __builtin_ldexpf(a, 3 - e);                    // a / 2^(e-3), exact
+  int n = (int)__builtin_rintf(q);                         // round half to even
+  int code = (e + 7) * 8 + n - 8;
+  if (code > 0x7E) code = 0x7E;
+  return sign | (uint32_t)code;
+}
+
+// ---------------------------------------------------------------- OCP E2M1
+
+// E2M1 code of r: nearest of {0,.5,1,1.5,2,3,4,6}, ties to the even code, saturating.
+__device__ __forceinline__ uint32_t f32_to_e2m1(float r) {
+  uint32_t sign = (__float_as_uint(r) >> 28) & 0x8u;
+  float a = fabsf(r);
+  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) +
+               (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+  return sign | c;
+}
+
+// ---------------------------------------------------------------- FP4 block decode
+
+// Eight E2M1 codes (one dword, element 2i in the low nibble of byte i) times the block
+// scale s -> eight bf16 values, packed in pairs.  Exact: an E2M1 value times an E4M3
+// value has at most 6 significant bits.
+__device__ __forceinline__ u32x4 fp4x8_to_bf16(uint32_t codes, float s) {
+  f32x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+  f32x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+  f32x2 e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+  f32x2 e3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+  return u32x4{pack_bf16_exact(e0[0] * s, e0[1] * s), pack_bf16_exact(e1[0] * s, e1[1] * s),
+               pack_bf16_exact(e2[0] * s, e2[1] * s), pack_bf16_exact(e3[0] * s, e3[1] * s)};
+}
+
+// ---------------------------------------------------------------- order keys
+
+// Monotone map fp32 -> uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------- MFMA
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) {
+  return __builtin_bit_cast(f16x8, v);
+}
+
+// fp32 -> IEEE half bit pattern, round to nearest even.
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+}  // namespace csakv

@@ -1,0 +1,55 @@
+// Host-side launchers of the csakv kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csakv {
+
+// ------------------------------------------------------------------ codecs
+hipError_t launch_quantize_fp4(const uint16_t* x, int64_t rows, int dim, uint8_t* codes,
+                               uint8_t* scales, hipStream_t stream);
+hipError_t launch_quantize_fp8_mixed(const uint16_t* x, int64_t rows, int dim, int nope,
+                                     uint8_t* out, hipStream_t stream);
+hipError_t launch_dequantize(int fmt, const void* codes, const uint8_t* scales, int64_t rows,
+                             int dim, int nope, uint16_t* out, hipStream_t stream);
+
+// ------------------------------------------------------------------ indexer + top-k
+// Slice geometry of one indexer pass.
+struct IndexerPlan {
+  int slice_rows;   // rows per slice (multiple of 16)
+  int n_slices;     // slices per query
+  int cand_stride;  // candidate slots per slice = min(top_k, slice_rows)
+  int prefix;       // sorted-prefix length the merge reads first from every slice
+};
+
+constexpr int kMaxSliceRows = 4096;
+constexpr int kMaxTopK = 1024;
+constexpr int kMergeCap = 8192;
+
+IndexerPlan plan_indexer(int batch, int64_t n_c, int top_k);
+size_t indexer_workspace_bytes(int batch, const IndexerPlan& plan);
+
+hipError_t launch_indexer(int key_fmt, const uint8_t* codes, const uint8_t* scales,
+                          int64_t seq_stride, int64_t n_c, const uint16_t* q_idx,
+                          const float* w_idx, int batch, int n_heads, int top_k,
+                          const IndexerPlan& plan, void* workspace, int32_t* topk,
+                          hipStream_t stream);
+
+// ------------------------------------------------------------------ attention
+struct AttnPlan {
+  int64_t n_list;      // row positions per query (CSA: window + top_k; HCA: rows)
+  int rows_per_chunk;  // multiple of 32
+  int n_chunks;        // chunks per query
+};
+
+AttnPlan plan_attention(int batch, int64_t n_list, bool csa);
+size_t attention_workspace_bytes(int batch, int n_heads, const AttnPlan& plan);
+
+hipError_t launch_attention(int kv_fmt, bool csa, const uint8_t* codes, const uint8_t* scales,
+                            int64_t seq_stride, int64_t n_rows, const uint16_t* q, int batch,
+                            int n_heads, float softmax_scale, const int32_t* topk, int top_k,
+                            int window, const AttnPlan& plan, void* workspace, uint16_t* out,
+                            hipStream_t stream);
+
+}  // namespace csakv

@@ -1,0 +1,189 @@
+/*
+ * csakv.h - decode-time attention over compressed sparse KV caches on MI355X (gfx950).
+ *
+ * The operation, as the source pages state it ("DeepSeek-V4 KV Cache 深度分析",
+ * sections 三 "压缩机制详解", 四 "索引器（Indexer）机制" and the 十一 forward-flow
+ * diagram):
+ *   - CSA layers keep one 512-wide shared-KV entry per 4 tokens (448 no-RoPE dims,
+ *     then 64 RoPE dims) plus a 128-wide indexer key per entry.  For each query
+ *     token an indexer score picks the top-k compressed entries, and attention runs
+ *     over those entries together with the most recent 128 uncompressed tokens
+ *     (the sliding window).  Every entry is both key and value.
+ *   - HCA layers keep one entry per 128 tokens and attend densely over all of them
+ *     plus the window, without an indexer.
+ *   - CSA2 "Reuse" layers ("DeepSeek, KV 캐시를 토큰당 890바이트로 줄인 V4.1-Flash 공개",
+ *     section 핵심 내용; "KV cache 890 bajtów na token", section "Trzy mechanizmy
+ *     zamiast jednej sztuczki") attend with the top-512 indices an earlier layer chose.
+ * The pages give no formula for the indexer score; this library computes
+ *     s_j = sum_h w_h * ReLU(q_h . k_j)
+ * and keeps the k largest, ties broken toward the smaller index.
+ *
+ * Conventions shared by every entry point
+ *   - All data pointers are DEVICE pointers into memory the caller owns (for
+ *     example PyTorch tensors).  The library never allocates or frees device
+ *     memory, keeps no pointer after a call returns and has no global state.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     default stream).  No call synchronises.  Device faults surface at the
+ *     caller's next synchronisation.
+ *   - Every argument is checked on the host before anything is launched.  A
+ *     rejected call returns CSAKV_ERR_INVALID, CSAKV_ERR_UNSUPPORTED or
+ *     CSAKV_ERR_WORKSPACE and enqueues nothing.  A failed launch returns
+ *     CSAKV_ERR_HIP.
+ *   - bf16 tensors are passed as uint16_t bit patterns; every row is contiguous
+ *     and little-endian.  Device pointers must be 16-byte aligned.
+ *   - Calls that take a workspace need `workspace_bytes >= *_workspace_bytes(...)`;
+ *     its contents need no initialisation and are scratch after the call.
+ */
+#ifndef CSAKV_H
+#define CSAKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CSAKV_OK = 0,
+  CSAKV_ERR_INVALID = -1,      /* null/misaligned pointer, bad size or shape      */
+  CSAKV_ERR_UNSUPPORTED = -2,  /* valid request outside what the kernels support  */
+  CSAKV_ERR_WORKSPACE = -3,    /* workspace smaller than *_workspace_bytes        */
+  CSAKV_ERR_HIP = -4           /* a HIP launch reported an error                   */
+} csakv_status;
+
+/* Storage formats of 512-wide shared-KV rows ("DeepSeek-V4 KV Cache 深度分析", sections
+ * 二 and 六; the V4.1-Flash pages for FP4).  Row bytes: BF16 1024; FP8_MIXED 576 =
+ * 448 OCP E4M3FN bytes (unscaled) followed by the 64 RoPE dims as bf16; FP4 256 code
+ * bytes (E2M1, element 2i in the low nibble of byte i) plus 32 scale bytes (one
+ * E4M3FN scale per 16 channels) held in a separate scale plane. */
+typedef enum { CSAKV_KV_BF16 = 0, CSAKV_KV_FP8_MIXED = 1, CSAKV_KV_FP4 = 2 } csakv_kv_fmt;
+
+/* Storage formats of 128-wide indexer-key rows: BF16 256 bytes; FP4 64 code bytes
+ * plus 8 scale bytes in a separate scale plane ("DeepSeek-V4 KV Cache 深度分析",
+ * section 四: indexer keys are cached in FP4). */
+typedef enum { CSAKV_IDX_BF16 = 0, CSAKV_IDX_FP4 = 1 } csakv_idx_fmt;
+
+typedef enum { CSAKV_MODE_FULL = 0, CSAKV_MODE_REUSE = 1 } csakv_mode;
+
+/* One cache tensor of B sequences.  Sequence b's row r starts at byte
+ * (b * seq_stride_rows + r) * code_bytes(fmt) of `codes`; for FP4 its scales start
+ * at byte (b * seq_stride_rows + r) * (dim / 16) of `scales` (NULL otherwise).
+ * Shared-KV rows of a sequence are [window rows | compressed rows]: top-k index j
+ * names row window + j.  A cache with n_rows == 0 may pass NULL pointers. */
+typedef struct {
+  int32_t fmt;              /* csakv_kv_fmt for shared-KV, csakv_idx_fmt for keys */
+  int32_t reserved;         /* must be 0                                            */
+  int64_t n_rows;           /* rows per sequence                                    */
+  int64_t seq_stride_rows;  /* rows between consecutive sequences, >= n_rows        */
+  const void* codes;
+  const uint8_t* scales;
+} csakv_cache;
+
+typedef struct {
+  int32_t batch;            /* B >= 1 query tokens, one independent sequence each  */
+  int32_t n_q_heads;        /* H_q: 16, 32, 48 or 64                                 */
+  int32_t n_idx_heads;      /* H_I: 1..64 (FULL mode)                               */
+  int32_t top_k;            /* 1..1024                                              */
+  int32_t window;           /* window rows at the start of each sequence, >= 0      */
+  int32_t mode;             /* csakv_mode                                           */
+  float softmax_scale;      /* logit scale, e.g. 1/sqrt(512)                        */
+  int32_t reserved;         /* must be 0                                            */
+} csakv_csa_params;
+
+/* Bytes of workspace csa_decode needs for these parameters and N_c compressed rows. */
+size_t csa_decode_workspace_bytes(const csakv_csa_params* p, int64_t n_compressed);
+
+/* CSA decode for B query tokens (one layer).
+ *   kv       shared-KV cache, n_rows = window + N_c, any csakv_kv_fmt.
+ *   idx_keys FULL: indexer keys, n_rows = N_c, any csakv_idx_fmt; REUSE: NULL.
+ *   q        [B][H_q][512] bf16 attention queries.
+ *   q_idx    FULL: [B][H_I][128] bf16 indexer queries; REUSE: NULL.
+ *   w_idx    FULL: [B][H_I] fp32 indexer head weights; REUSE: NULL.
+ *   topk     [B][top_k] int32.  FULL writes the selected compressed-row indices
+ *            (order: score descending, index ascending; -1 pads when N_c < top_k).
+ *            REUSE reads it (entries < 0 or >= N_c are skipped).
+ *   out      [B][H_q][512] bf16: softmax(scale * q . e) weighted sum of the rows
+ *            e in (window rows) + (selected rows), one softmax over their union.
+ *            A query with no rows gets zeros.
+ * Returns CSAKV_ERR_UNSUPPORTED for head/row dims other than 512 (KV) and 128
+ * (indexer keys) implied by the formats, or for shapes beyond the limits above. */
+csakv_status csa_decode(const csakv_csa_params* p, const csakv_cache* kv,
+                        const csakv_cache* idx_keys, const uint16_t* q,
+                        const uint16_t* q_idx, const float* w_idx, int32_t* topk,
+                        uint16_t* out, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Bytes of workspace csa_select_topk needs for these parameters and N_c rows. */
+size_t csa_select_topk_workspace_bytes(const csakv_csa_params* p, int64_t n_compressed);
+
+/* The indexer stage of a CSA Full layer alone ("DeepSeek-V4 KV Cache 深度分析", section
+ * 四: the indexer query is scored against every compressed entry's key and the top-k
+ * are kept): writes topk [B][top_k] exactly as csa_decode's FULL mode does, without
+ * the attention.  p->mode must be CSAKV_MODE_FULL; p->n_q_heads and p->window are
+ * not used.  idx_keys, q_idx, w_idx as for csa_decode. */
+csakv_status csa_select_topk(const csakv_csa_params* p, const csakv_cache* idx_keys,
+                             const uint16_t* q_idx, const float* w_idx, int32_t* topk,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace hca_decode needs for B sequences of n_rows rows each. */
+size_t hca_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int64_t n_rows);
+
+/* HCA decode ("DeepSeek-V4 KV Cache 深度分析", section 三 part 1): dense attention of
+ * q [B][H_q][512] over every row of each sequence of `kv` (window and compressed
+ * rows alike), out [B][H_q][512] bf16. */
+csakv_status hca_decode(int32_t batch, int32_t n_q_heads, float softmax_scale,
+                        const csakv_cache* kv, const uint16_t* q, uint16_t* out,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* FP4 block quantisation of bf16 rows x [rows][dim] (dim % 16 == 0):
+ * scale = E4M3FN(amax/6) per 16 channels (round to nearest even, saturating);
+ * code  = E2M1(x / scale), or 0 for every element when the scale decodes to 0.
+ * codes [rows][dim/2], scales [rows][dim/16]. */
+csakv_status kv_quantize_fp4(const uint16_t* x, int64_t rows, int32_t dim,
+                             uint8_t* codes, uint8_t* scales, void* stream);
+
+/* Mixed FP8/BF16 rows: out [rows][nope_dim + 2*(dim - nope_dim)] holds
+ * E4M3FN(x[0..nope_dim)) (round to nearest even, saturating at 448) followed by the
+ * bf16 bytes of x[nope_dim..dim).  nope_dim % 16 == 0, dim % 16 == 0. */
+csakv_status kv_quantize_fp8(const uint16_t* x, int64_t rows, int32_t dim,
+                             int32_t nope_dim, uint8_t* out, void* stream);
+
+/* Decode rows of any KV format back to bf16 (exact for every format):
+ * fmt is csakv_kv_fmt; dim 512 for FP8_MIXED (nope 448), dim % 16 == 0 otherwise. */
+csakv_status kv_dequantize(int32_t fmt, const void* codes, const uint8_t* scales,
+                           int64_t rows, int32_t dim, uint16_t* out, void* stream);
+
+/* KV-cache size in closed form ("DeepSeek-V4 KV Cache 深度分析", section 七):
+ *   PerCSA = (N/csa_ratio + c_w*window) * S_kv + (N/csa_ratio) * S_idx
+ *   PerHCA = (N/hca_ratio + c_w*window) * S_kv
+ *   Total  = n_csa*PerCSA + n_hca*PerHCA + n_swa*swa_layer_bytes
+ * where c_w = count_window (0, 1 or 2) and S_kv / S_idx are the row bytes of
+ * kv_fmt / idx_fmt for kv_dim / idx_dim (FP4 scale bytes included iff count_scales;
+ * FP8_MIXED keeps rope_dim dims in bf16).  idx_dim = 0 means no indexer; an MLA-style
+ * layer is ratio 1, window 0, a BF16 row of kv_dim values.  Pure host arithmetic;
+ * returns the total, fills `out` if non-NULL, and returns 0 for an invalid spec. */
+typedef struct {
+  int32_t n_csa, n_hca, n_swa;
+  int32_t csa_ratio, hca_ratio, window;
+  int32_t kv_dim, rope_dim, idx_dim;
+  int32_t kv_fmt, idx_fmt;
+  int32_t count_window, count_scales;
+  int32_t reserved;
+  int64_t swa_layer_bytes;
+} kv_cache_spec;
+
+typedef struct {
+  uint64_t csa_shared_kv, csa_indexer, hca_shared_kv, windows, swa_layers;
+  uint64_t csa_per_layer, hca_per_layer, total;
+} kv_cache_breakdown;
+
+uint64_t kv_cache_bytes(const kv_cache_spec* spec, int64_t seq_len, kv_cache_breakdown* out);
+
+/* Static, NUL-terminated description of a status code. */
+const char* csakv_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSAKV_H */

@@ -8,3 +8,11 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def pytest_sessionstart(session):
+    """Build the HIP library once if it is missing (tests only ever load a built one)."""
+    import compressed_sparse_kv_csa_amd as ck
+    if not os.path.exists(ck.lib_path()):
+        from compressed_sparse_kv_csa_amd import build
+        build.build()

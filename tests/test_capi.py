@@ -1,0 +1,144 @@
+"""The C ABI on the host: the library loads, exports every entry point the header
+declares, its byte accounting matches the oracle, and invalid calls are rejected
+before anything is launched (no device needed for any of these)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import compressed_sparse_kv_csa_amd as ck
+from oracle import kvbytes
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "csakv.h")
+
+
+def _declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s+\**([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_binding_names():
+    assert _declared_functions() == sorted(ck.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(ck.lib_path())
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def _spec(**kw):
+    base = dict(n_csa=30, n_hca=31, n_swa=0, csa_ratio=4, hca_ratio=128, window=128, kv_dim=512,
+                rope_dim=64, idx_dim=128, kv_fmt=ck.KV_BF16, idx_fmt=ck.IDX_BF16, count_window=1,
+                count_scales=0, reserved=0, swa_layer_bytes=0)
+    base.update(kw)
+    return ck.KvCacheSpec(**base)
+
+
+# (library spec, oracle row bytes) pairs; row bytes follow from the format definitions.
+FORMATS = [
+    (dict(kv_fmt=ck.KV_BF16, idx_fmt=ck.IDX_BF16), dict(s_kv=1024, s_idx=256)),
+    (dict(kv_fmt=ck.KV_FP8_MIXED, idx_fmt=ck.IDX_FP4), dict(s_kv=576, s_idx=64)),
+    (dict(kv_fmt=ck.KV_FP8_MIXED, idx_fmt=ck.IDX_FP4, count_scales=1), dict(s_kv=576, s_idx=72)),
+    (dict(kv_fmt=ck.KV_FP4, idx_fmt=ck.IDX_FP4, count_scales=1), dict(s_kv=288, s_idx=72)),
+    (dict(kv_fmt=ck.KV_FP4, idx_fmt=ck.IDX_FP4), dict(s_kv=256, s_idx=64)),
+]
+
+
+@pytest.mark.parametrize("lib_kw,orc_kw", FORMATS)
+@pytest.mark.parametrize("count_window", [0, 1, 2])
+@pytest.mark.parametrize("seq_len", [0, 1, 4097, 131072, 1 << 20])
+def test_kv_cache_bytes_matches_oracle(lib_kw, orc_kw, count_window, seq_len):
+    total, br = ck.kv_cache_bytes(_spec(count_window=count_window, **lib_kw), seq_len)
+    ref = kvbytes.kv_cache_bytes(seq_len, n_csa=30, n_hca=31, count_window=count_window, **orc_kw)
+    assert total == ref["total"]
+    for f in ("csa_per_layer", "hca_per_layer", "csa_shared_kv", "csa_indexer", "hca_shared_kv",
+              "windows", "swa_layers"):
+        assert getattr(br, f) == ref[f], f
+
+
+def test_kv_cache_bytes_presets_and_invalid():
+    mla = _spec(n_csa=61, n_hca=0, csa_ratio=1, window=0, kv_dim=576, idx_dim=0, count_window=0)
+    assert ck.kv_cache_bytes(mla, 1 << 20)[0] == 1152 * 61 * (1 << 20)
+    flash = _spec(n_csa=21, n_hca=20, n_swa=2, count_window=0,
+                  swa_layer_bytes=kvbytes.swa_layer_bytes(1, 128, 2, 128, pad=256))
+    assert ck.kv_cache_bytes(flash, 1 << 20)[0] == (320 * 21 + 8 * 20) * (1 << 20) + 2 * 196608
+    assert ck.kv_cache_bytes(_spec(count_window=3), 10)[0] == 0
+    assert ck.kv_cache_bytes(_spec(csa_ratio=0), 10)[0] == 0
+    assert ck.kv_cache_bytes(_spec(kv_fmt=7), 10)[0] == 0
+    assert ck.kv_cache_bytes(_spec(), -1)[0] == 0
+
+
+def _params(**kw):
+    base = dict(batch=1, n_q_heads=16, n_idx_heads=4, top_k=512, window=128, mode=ck.MODE_FULL,
+                softmax_scale=0.044, reserved=0)
+    base.update(kw)
+    return ck.CsaParams(**base)
+
+
+FAKE = 1 << 20  # an aligned, never-dereferenced address: every case below is rejected first
+
+
+def _call(p, kv=None, idx=None, q=FAKE, qi=FAKE, w=FAKE, topk=FAKE, out=FAKE, ws=FAKE,
+          ws_bytes=1 << 30):
+    kv = kv or ck.Cache(ck.KV_BF16, 0, 128 + 1024, 128 + 1024, FAKE, None)
+    return ck.csa_decode(p, kv, idx, q, qi, w, topk, out, ws, ws_bytes, stream=0, check=False)
+
+
+IDX = ck.Cache(ck.IDX_BF16, 0, 1024, 1024, FAKE, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), ck.ERR_INVALID),
+    (dict(top_k=0), ck.ERR_INVALID),
+    (dict(top_k=2048), ck.ERR_UNSUPPORTED),
+    (dict(n_q_heads=24), ck.ERR_UNSUPPORTED),
+    (dict(n_q_heads=128), ck.ERR_UNSUPPORTED),
+    (dict(n_idx_heads=65), ck.ERR_UNSUPPORTED),
+    (dict(n_idx_heads=0), ck.ERR_INVALID),
+    (dict(mode=5), ck.ERR_INVALID),
+    (dict(window=-1), ck.ERR_INVALID),
+    (dict(softmax_scale=float("nan")), ck.ERR_INVALID),
+    (dict(reserved=1), ck.ERR_INVALID),
+])
+def test_csa_rejects_bad_params(kw, status):
+    assert _call(_params(**kw), idx=IDX) == status
+
+
+def test_csa_rejects_bad_pointers_and_shapes():
+    p = _params()
+    assert _call(p, idx=IDX, q=FAKE + 2) == ck.ERR_INVALID                 # misaligned
+    assert _call(p, idx=IDX, out=0) == ck.ERR_INVALID                      # null
+    assert _call(p, idx=None) == ck.ERR_INVALID                            # FULL needs keys
+    bad_rows = ck.Cache(ck.IDX_BF16, 0, 1000, 1000, FAKE, None)
+    assert _call(p, idx=bad_rows) == ck.ERR_INVALID                        # keys != N_c rows
+    fp4_no_scales = ck.Cache(ck.IDX_FP4, 0, 1024, 1024, FAKE, None)
+    assert _call(p, idx=fp4_no_scales) == ck.ERR_INVALID
+    bf16_with_scales = ck.Cache(ck.IDX_BF16, 0, 1024, 1024, FAKE, FAKE)
+    assert _call(p, idx=bf16_with_scales) == ck.ERR_INVALID
+    short = ck.Cache(ck.KV_BF16, 0, 100, 100, FAKE, None)                  # fewer rows than window
+    assert _call(p, kv=short, idx=IDX) == ck.ERR_INVALID
+    stride = ck.Cache(ck.KV_BF16, 0, 1152, 1000, FAKE, None)               # stride < rows
+    assert _call(p, kv=stride, idx=IDX) == ck.ERR_INVALID
+    need = ck.csa_decode_workspace_bytes(p, 1024)
+    assert need > 0
+    assert _call(p, idx=IDX, ws_bytes=need - 1) == ck.ERR_WORKSPACE
+    reuse = _params(mode=ck.MODE_REUSE, n_idx_heads=0)
+    assert _call(reuse, idx=IDX) == ck.ERR_INVALID                         # REUSE takes no keys
+
+
+def test_hca_and_codecs_reject_bad_arguments():
+    kv = ck.Cache(ck.KV_BF16, 0, 1000, 1000, FAKE, None)
+    assert ck.hca_decode(0, 64, 0.04, kv, FAKE, FAKE, FAKE, 1 << 30, stream=0, check=False) == ck.ERR_INVALID
+    assert ck.hca_decode(1, 40, 0.04, kv, FAKE, FAKE, FAKE, 1 << 30, stream=0, check=False) == ck.ERR_UNSUPPORTED
+    assert ck.hca_decode(1, 64, 0.04, kv, FAKE, FAKE, FAKE, 0, stream=0, check=False) == ck.ERR_WORKSPACE
+    assert ck.kv_quantize_fp4(FAKE, 10, 100, FAKE, FAKE, stream=0, check=False) == ck.ERR_INVALID
+    assert ck.kv_quantize_fp8(FAKE, 10, 512, 440, FAKE, stream=0, check=False) == ck.ERR_INVALID
+    assert ck.kv_dequantize(1, FAKE, None, 10, 256, FAKE, stream=0, check=False) == ck.ERR_UNSUPPORTED
+    assert ck.kv_dequantize(2, FAKE, None, 10, 512, FAKE, stream=0, check=False) == ck.ERR_INVALID
+    assert ck.kv_dequantize(9, FAKE, None, 10, 512, FAKE, stream=0, check=False) == ck.ERR_INVALID
+    assert ck.csakv_status_string(-2) == "unsupported shape or format"
