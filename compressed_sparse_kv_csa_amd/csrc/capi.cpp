@@ -116,7 +116,7 @@ csakv_status csa_decode(const csakv_csa_params* p, const csakv_cache* kv,
     return CSAKV_ERR_INVALID;
   }
   const CsaLayout L = csa_layout(p, n_c);
-  if (full && (int64_t)L.idx.n_slices * L.idx.prefix > csakv::kMergeCap) return CSAKV_ERR_UNSUPPORTED;
+  if (full && !csakv::indexer_supported(L.idx)) return CSAKV_ERR_UNSUPPORTED;
   if (workspace_bytes < L.total) return CSAKV_ERR_WORKSPACE;
   if (L.total > 0 && (!workspace || !aligned(workspace, kWsAlign))) return CSAKV_ERR_INVALID;
 
@@ -154,7 +154,7 @@ csakv_status csa_select_topk(const csakv_csa_params* p, const csakv_cache* idx_k
     return CSAKV_ERR_INVALID;
   const int64_t n_c = idx_keys->n_rows;
   const csakv::IndexerPlan plan = csakv::plan_indexer(p->batch, n_c, p->top_k);
-  if ((int64_t)plan.n_slices * plan.prefix > csakv::kMergeCap) return CSAKV_ERR_UNSUPPORTED;
+  if (!csakv::indexer_supported(plan)) return CSAKV_ERR_UNSUPPORTED;
   const size_t need = round_up(csakv::indexer_workspace_bytes(p->batch, plan), kWsAlign);
   if (workspace_bytes < need) return CSAKV_ERR_WORKSPACE;
   if (need > 0 && (!workspace || !aligned(workspace, kWsAlign))) return CSAKV_ERR_INVALID;

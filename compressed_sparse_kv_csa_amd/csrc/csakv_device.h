@@ -9,6 +9,7 @@ namespace csakv {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -89,6 +90,69 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16(uint32_t codes, float s) {
 __device__ __forceinline__ uint32_t f32_order_key(float f) {
   uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------- barriers
+
+// Workgroup barrier that orders LDS only: global loads still in flight stay in flight
+// (a full __syncthreads() also waits for every outstanding global access).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// ---------------------------------------------------------------- wave scans (DPP)
+
+// Inclusive prefix sum over the 64 lanes of a wave: row shifts within 16-lane rows,
+// then row broadcasts across rows (no LDS round trips).
+__device__ __forceinline__ uint32_t wave_incl_scan_add(uint32_t x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
+// One step of a 64-bit min/max scan: combine with the lane CTRL selects (lanes without
+// a source keep the identity).
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ void minmax_step(uint64_t& mn, uint64_t& mx) {
+  const uint32_t a_lo = __builtin_amdgcn_update_dpp(0xFFFFFFFFu, (uint32_t)mn, CTRL, ROWMASK, 0xF, false);
+  const uint32_t a_hi = __builtin_amdgcn_update_dpp(0xFFFFFFFFu, (uint32_t)(mn >> 32), CTRL, ROWMASK, 0xF, false);
+  const uint32_t b_lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)mx, CTRL, ROWMASK, 0xF, false);
+  const uint32_t b_hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(mx >> 32), CTRL, ROWMASK, 0xF, false);
+  const uint64_t a = ((uint64_t)a_hi << 32) | a_lo, b = ((uint64_t)b_hi << 32) | b_lo;
+  mn = a < mn ? a : mn;
+  mx = b > mx ? b : mx;
+}
+
+// Wave-wide minimum and maximum of 64-bit values (result uniform across the wave).
+__device__ __forceinline__ void wave_minmax_u64(uint64_t& mn, uint64_t& mx) {
+  minmax_step<0x111, 0xF>(mn, mx);
+  minmax_step<0x112, 0xF>(mn, mx);
+  minmax_step<0x114, 0xF>(mn, mx);
+  minmax_step<0x118, 0xF>(mn, mx);
+  minmax_step<0x142, 0xA>(mn, mx);
+  minmax_step<0x143, 0xC>(mn, mx);
+  // (readlane returns a signed int: widen through uint32_t, never sign-extend)
+  mn = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((uint32_t)(mn >> 32), 63) << 32) |
+       (uint32_t)__builtin_amdgcn_readlane((uint32_t)mn, 63);
+  mx = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((uint32_t)(mx >> 32), 63) << 32) |
+       (uint32_t)__builtin_amdgcn_readlane((uint32_t)mx, 63);
+}
+
+// Sum of a value over the four 16-lane rows of a wave, in every lane (lane l gets
+// x[l%16] + x[l%16+16] + x[l%16+32] + x[l%16+48]).
+__device__ __forceinline__ float wave_sum_rows(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t v = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // ---------------------------------------------------------------- MFMA

@@ -15,19 +15,23 @@ hipError_t launch_dequantize(int fmt, const void* codes, const uint8_t* scales, 
                              int dim, int nope, uint16_t* out, hipStream_t stream);
 
 // ------------------------------------------------------------------ indexer + top-k
-// Slice geometry of one indexer pass.
+// Geometry of one indexer pass.
 struct IndexerPlan {
-  int slice_rows;   // rows per slice (multiple of 16)
-  int n_slices;     // slices per query
-  int cand_stride;  // candidate slots per slice = min(top_k, slice_rows)
-  int prefix;       // sorted-prefix length the merge reads first from every slice
+  int slice_rows;     // rows per slice (multiple of 16 * waves)
+  int n_slices;       // slices per query
+  int slices_per_wg;  // consecutive slices one scan workgroup owns
+  int wg_per_query;   // scan workgroups per query
+  int cand_stride;    // candidate slots per slice = min(top_k, slice_rows)
+  int prefix;         // top-P entries of each slice the merge reads first
 };
 
 constexpr int kMaxSliceRows = 4096;
 constexpr int kMaxTopK = 1024;
 constexpr int kMergeCap = 8192;
+constexpr int kMaxMergeSlices = 512;
 
 IndexerPlan plan_indexer(int batch, int64_t n_c, int top_k);
+bool indexer_supported(const IndexerPlan& plan);
 size_t indexer_workspace_bytes(int batch, const IndexerPlan& plan);
 
 hipError_t launch_indexer(int key_fmt, const uint8_t* codes, const uint8_t* scales,

@@ -100,8 +100,9 @@ size_t csa_decode_workspace_bytes(const csakv_csa_params* p, int64_t n_compresse
  *   q        [B][H_q][512] bf16 attention queries.
  *   q_idx    FULL: [B][H_I][128] bf16 indexer queries; REUSE: NULL.
  *   w_idx    FULL: [B][H_I] fp32 indexer head weights; REUSE: NULL.
- *   topk     [B][top_k] int32.  FULL writes the selected compressed-row indices
- *            (order: score descending, index ascending; -1 pads when N_c < top_k).
+ *   topk     [B][top_k] int32.  FULL writes the set of selected compressed-row
+ *            indices (ties in score go to the lower index) in an unspecified but
+ *            deterministic order; -1 pads when N_c < top_k.
  *            REUSE reads it (entries < 0 or >= N_c are skipped).
  *   out      [B][H_q][512] bf16: softmax(scale * q . e) weighted sum of the rows
  *            e in (window rows) + (selected rows), one softmax over their union.

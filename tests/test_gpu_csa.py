@@ -95,9 +95,18 @@ def test_csa_deterministic():
     _check(case, t1, o1)
 
 
-def test_csa_topk_order_is_score_order():
-    """FULL writes indices by descending oracle score (the inputs are tie-free)."""
-    print("case: csa topk order", flush=True)
-    case = make_csa_case(124, 1, 2048, 128, 16, 8, 256, "bf16", "bf16")
-    topk, _ = run_csa(case)
-    assert np.array_equal(topk, case.expect_topk)
+def test_csa_select_topk_matches_full():
+    """The indexer stage alone writes the same index set, byte for byte, as FULL decode."""
+    print("case: csa_select_topk vs FULL", flush=True)
+    import torch
+    from gpu_helpers import to_dev, upload_idx, workspace
+    case = make_csa_case(124, 3, 70000, 128, 64, 64, 512, "bf16", "fp4")
+    topk_full, out = run_csa(case)
+    _check(case, topk_full, out)
+    p = ck.CsaParams(case.B, case.hq, case.hi, case.top_k, case.window, ck.MODE_FULL, case.scale, 0)
+    idx, keep = upload_idx(case.idx)
+    tk = torch.full((case.B, case.top_k), -7, dtype=torch.int32, device="cuda")
+    ws = workspace(ck.csa_select_topk_workspace_bytes(p, case.n_c))
+    ck.csa_select_topk(p, idx, to_dev(case.q_idx_bits.view(np.int16)), to_dev(case.w), tk, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(tk.cpu().numpy(), topk_full)
