@@ -16,6 +16,7 @@ scan + top-k, csa_select_topk) timed with HIP events on the stream it runs on;
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -39,6 +40,14 @@ WORKLOADS = {
     "csa_fp4_1m": dict(B=8, n_c=262144, window=128, hq=64, hi=64, top_k=512, kv="fp4",
                        idx="fp4", seed=5, context=1 << 20),
 }
+# HBM traffic of the indexer stage, from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs scaled
+# by what the same counters read for a copy kernel of known size.  Valid only while the
+# kernel sources hash to the recorded value.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_stage_csa_mixed_1m_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "compressed_sparse_kv_csa_amd", "csrc", f)
+                  for f in ("indexer.hip", "csakv_device.h", "csakv_launch.h")]
+COPY_PROBE_ELEMS = 1 << 28  # float32 elements: 1 GiB read + 1 GiB written
+
 KV_ROW_BYTES = {"bf16": 1024, "mixed": 576, "fp4": 256 + 32}
 IDX_ROW_BYTES = {"bf16": 256, "fp4": 64 + 8}
 
@@ -156,6 +165,43 @@ def run_gpu(w: dict, steps: int, warmup: int, replicas: int | None):
     return dict(ms=ms, wall=wall, sel_ms=sel_ms, replicas=R, bytes=nbytes)
 
 
+def kernel_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """Bytes per launch from the committed counter summary, or None if stale or absent."""
+    if workload != "csa_mixed_1m" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    with open(TRAFFIC_FILE) as f:
+        for ln in f:
+            if ":" in ln:
+                k, v = ln.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe():
+    """One plain elementwise copy of known size (1 GiB in, 1 GiB out) for counter scaling."""
+    import torch
+    src = torch.ones(COPY_PROBE_ELEMS, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def run_cpu_baseline(w: dict, queries: int):
     """The oracle, untuned, on `queries` query tokens of the same workload (seed, shapes)."""
     import numpy as np
@@ -244,6 +290,8 @@ def main():
     ap.add_argument("--cpu-queries", type=int, default=None,
                     help="query tokens in the oracle sample (default: one step's batch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="first run one 1 GiB elementwise copy (scales HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -255,6 +303,8 @@ def main():
         print("bench.py needs a GPU (HIP device) to run.", file=sys.stderr)
         sys.exit(1)
     w = WORKLOADS[args.workload]
+    if args.copy_probe:
+        copy_probe()
     g = run_gpu(w, args.steps, args.warmup, args.replicas)
     B = w["B"]
     tok_s = B / (g["ms"] * 1e-3)
@@ -283,7 +333,8 @@ def main():
         "hbm_gbps": round(step_gbps, 1),
         "algorithmic_bytes_per_step": g["bytes"]["step"],
         "roofline": {"bound": "hbm", "achieved": round(sel_gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(sel_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(sel_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(args.workload),
                      "kernel": "indexer stage (csa_select_topk)",
                      "avg_launch_us": round(g["sel_ms"] * 1e3, 2),
                      "algorithmic_bytes_per_launch": g["bytes"]["indexer"]},
