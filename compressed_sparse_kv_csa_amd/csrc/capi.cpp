@@ -50,7 +50,7 @@ CsaLayout csa_layout(const csakv_csa_params* p, int64_t n_c) {
     L.idx = csakv::plan_indexer(p->batch, n_c, p->top_k);
     L.idx_bytes = round_up(csakv::indexer_workspace_bytes(p->batch, L.idx), kWsAlign);
   }
-  L.attn = csakv::plan_attention(p->batch, (int64_t)p->window + p->top_k, true);
+  L.attn = csakv::plan_attention(p->batch, (int64_t)p->window + p->top_k, true, p->n_q_heads);
   L.attn_offset = L.idx_bytes;
   L.total = L.idx_bytes + round_up(csakv::attention_workspace_bytes(p->batch, p->n_q_heads, L.attn), kWsAlign);
   return L;
@@ -104,7 +104,7 @@ csakv_status csa_decode(const csakv_csa_params* p, const csakv_cache* kv,
   if ((st = check_cache(kv, true)) != CSAKV_OK) return st;
   if (kv->n_rows < p->window) return CSAKV_ERR_INVALID;
   const int64_t n_c = kv->n_rows - p->window;
-  if (n_c > INT32_MAX) return CSAKV_ERR_UNSUPPORTED;
+  if (kv->n_rows > INT32_MAX) return CSAKV_ERR_UNSUPPORTED;
   if (!q || !out || !topk || !aligned(q, 16) || !aligned(out, 16) || !aligned(topk, 4))
     return CSAKV_ERR_INVALID;
   const bool full = p->mode == CSAKV_MODE_FULL;
@@ -117,6 +117,7 @@ csakv_status csa_decode(const csakv_csa_params* p, const csakv_cache* kv,
   }
   const CsaLayout L = csa_layout(p, n_c);
   if (full && !csakv::indexer_supported(L.idx)) return CSAKV_ERR_UNSUPPORTED;
+  if (!csakv::attention_supported(L.attn)) return CSAKV_ERR_UNSUPPORTED;
   if (workspace_bytes < L.total) return CSAKV_ERR_WORKSPACE;
   if (L.total > 0 && (!workspace || !aligned(workspace, kWsAlign))) return CSAKV_ERR_INVALID;
 
@@ -166,7 +167,7 @@ csakv_status csa_select_topk(const csakv_csa_params* p, const csakv_cache* idx_k
 
 size_t hca_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int64_t n_rows) {
   if (batch < 1 || n_q_heads < 1 || n_rows < 0) return 0;
-  csakv::AttnPlan a = csakv::plan_attention(batch, n_rows, false);
+  csakv::AttnPlan a = csakv::plan_attention(batch, n_rows, false, n_q_heads);
   return round_up(csakv::attention_workspace_bytes(batch, n_q_heads, a), kWsAlign);
 }
 
@@ -178,10 +179,13 @@ csakv_status hca_decode(int32_t batch, int32_t n_q_heads, float softmax_scale,
   csakv_status st = check_cache(kv, true);
   if (st != CSAKV_OK) return st;
   if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return CSAKV_ERR_INVALID;
+  if (kv->n_rows > INT32_MAX) return CSAKV_ERR_UNSUPPORTED;
+  if (!csakv::attention_supported(csakv::plan_attention(batch, kv->n_rows, false, n_q_heads)))
+    return CSAKV_ERR_UNSUPPORTED;
   const size_t need = hca_decode_workspace_bytes(batch, n_q_heads, kv->n_rows);
   if (workspace_bytes < need) return CSAKV_ERR_WORKSPACE;
   if (need > 0 && (!workspace || !aligned(workspace, kWsAlign))) return CSAKV_ERR_INVALID;
-  csakv::AttnPlan a = csakv::plan_attention(batch, kv->n_rows, false);
+  csakv::AttnPlan a = csakv::plan_attention(batch, kv->n_rows, false, n_q_heads);
   return hip_status(csakv::launch_attention(
       kv->fmt, false, static_cast<const uint8_t*>(kv->codes), kv->scales, kv->seq_stride_rows,
       kv->n_rows, q, batch, n_q_heads, softmax_scale, nullptr, 0, 0, a, workspace, out,

@@ -47,7 +47,11 @@ struct AttnPlan {
   int n_chunks;        // chunks per query
 };
 
-AttnPlan plan_attention(int batch, int64_t n_list, bool csa);
+constexpr int kMaxChunkRows = 1024;  // rows one attention workgroup walks
+constexpr int kMaxChunks = 4096;     // chunks per query the combine merges
+
+AttnPlan plan_attention(int batch, int64_t n_list, bool csa, int n_heads);
+bool attention_supported(const AttnPlan& plan);
 size_t attention_workspace_bytes(int batch, int n_heads, const AttnPlan& plan);
 
 hipError_t launch_attention(int kv_fmt, bool csa, const uint8_t* codes, const uint8_t* scales,
