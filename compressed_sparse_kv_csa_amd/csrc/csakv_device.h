@@ -144,6 +144,25 @@ __device__ __forceinline__ void wave_minmax_u64(uint64_t& mn, uint64_t& mx) {
        (uint32_t)__builtin_amdgcn_readlane((uint32_t)mx, 63);
 }
 
+// Wave-wide minimum and maximum of 32-bit values (result uniform across the wave).
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ void minmax_step32(uint32_t& mn, uint32_t& mx) {
+  const uint32_t a = __builtin_amdgcn_update_dpp(0xFFFFFFFFu, mn, CTRL, ROWMASK, 0xF, false);
+  const uint32_t b = __builtin_amdgcn_update_dpp(0u, mx, CTRL, ROWMASK, 0xF, false);
+  mn = a < mn ? a : mn;
+  mx = b > mx ? b : mx;
+}
+__device__ __forceinline__ void wave_minmax_u32(uint32_t& mn, uint32_t& mx) {
+  minmax_step32<0x111, 0xF>(mn, mx);
+  minmax_step32<0x112, 0xF>(mn, mx);
+  minmax_step32<0x114, 0xF>(mn, mx);
+  minmax_step32<0x118, 0xF>(mn, mx);
+  minmax_step32<0x142, 0xA>(mn, mx);
+  minmax_step32<0x143, 0xC>(mn, mx);
+  mn = (uint32_t)__builtin_amdgcn_readlane(mn, 63);
+  mx = (uint32_t)__builtin_amdgcn_readlane(mx, 63);
+}
+
 // Sum of a value over the four 16-lane rows of a wave, in every lane (lane l gets
 // x[l%16] + x[l%16+16] + x[l%16+32] + x[l%16+48]).
 __device__ __forceinline__ float wave_sum_rows(float x) {

@@ -17,15 +17,16 @@ hipError_t launch_dequantize(int fmt, const void* codes, const uint8_t* scales, 
 // ------------------------------------------------------------------ indexer + top-k
 // Geometry of one indexer pass.
 struct IndexerPlan {
-  int slice_rows;     // rows per slice (multiple of 16 * waves)
+  int64_t n_c;        // compressed rows per sequence
+  int slice_rows;     // rows selected together (kSliceRows)
   int n_slices;       // slices per query
   int slices_per_wg;  // consecutive slices one scan workgroup owns
   int wg_per_query;   // scan workgroups per query
-  int cand_stride;    // candidate slots per slice = min(top_k, slice_rows)
-  int prefix;         // top-P entries of each slice the merge reads first
+  int cap;            // candidate slots per slice
+  int prefix;         // P: a slice sends at least its top-P keys
 };
 
-constexpr int kMaxSliceRows = 4096;
+constexpr int kSliceRows = 4096;
 constexpr int kMaxTopK = 1024;
 constexpr int kMergeCap = 8192;
 constexpr int kMaxMergeSlices = 512;

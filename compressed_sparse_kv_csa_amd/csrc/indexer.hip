@@ -6,17 +6,21 @@
 // Score s_j = sum_h w_h * ReLU(q_h . k_j); ties are broken toward the smaller index.
 //
 // Two launches per call:
-//   1. scan kernel, one persistent workgroup per CU.  A workgroup owns a run of
-//      consecutive 2048-row slices of one query.  Its 8 waves stream 16-row key tiles
-//      from HBM straight into registers through a 4-deep prefetch ring that runs on
-//      across slice boundaries, so the next slice's loads are in flight while the
-//      current slice is being selected.  Each tile is one [H_I x 128] x [128 x 16]
-//      contraction on 16x16x32 MFMA with fp32 accumulation; ReLU, the head weights and
-//      the head sum are applied to the accumulators and the scores stay in LDS.  Per
-//      slice a radix select in LDS keeps the top-k, with the slice's top-P placed first.
-//   2. merge kernel, one workgroup per query: selects the k-th largest key among the
-//      top-P prefixes of all slices, and reads further into any slice whose whole
-//      prefix lies above it (exact for any input).
+//   1. scan kernel, about one workgroup per CU.  A workgroup owns a run of consecutive
+//      4096-row slices of one query.  Its 8 waves stream 16-row key tiles from HBM
+//      straight into registers through a 4-deep prefetch ring that runs on across slice
+//      boundaries.  Each tile is one [H_I x 128] x [128 x 16] contraction on 16x16x32
+//      MFMA with fp32 accumulation; ReLU, the head weights and the head sum are applied
+//      to the accumulators and the scores stay in LDS.  When a slice is complete, one
+//      2048-bin histogram of its score keys (between the slice's min and max) gives the
+//      lower edge t of the bin holding the slice's P-th largest score.  Every key >= t
+//      is emitted as a candidate, and t is recorded as the slice's bound: all keys not
+//      emitted lie below it.  The slice's scores are also written out, for the merge's
+//      rare second look.
+//   2. merge kernel, one workgroup per query: the exact k-th largest candidate key, by a
+//      histogram of the candidates and a direct ranking of the one bin that holds it.  A
+//      slice whose bound lies above that key may hide further winners; its stored scores
+//      are re-read and the selection repeated, so the result is exact for any input.
 // Selection keys are 64-bit: (order-preserving score bits << 32) | ~index, so a larger
 // key means a higher score, then a lower index; all keys of a query are distinct.
 //
@@ -29,6 +33,8 @@
 // the fp32 accumulation error of the score.  Products are exact in fp32 either way.
 #include "csakv_device.h"
 #include "csakv_launch.h"
+
+#include <algorithm>
 
 namespace csakv {
 
@@ -43,11 +49,14 @@ constexpr int kMergeThreads = 1024;
 // ------------------------------------------------------------------ block primitives
 
 constexpr int kHistBins = 2048;  // 11-bit digits
-constexpr int kListCap = 256;    // boundary-bin keys resolved by direct ranking
+constexpr int kListCap = 256;    // boundary-bin keys resolved by direct ranking (scan)
+constexpr int kMergeListCap = 1024;  // the same in the merge
 
 struct SelectSmem {
   uint32_t hist[kHistBins];
-  uint64_t red[2 * 16];
+  uint64_t red[2 * 16];    // per-wave 64-bit minima / maxima
+  uint32_t red32[2 * 16];  // per-wave 32-bit minima / maxima
+  uint64_t res64[16];
   uint32_t wsum[16];
   uint32_t bc[8];
   uint64_t list[2][kListCap];
@@ -55,11 +64,15 @@ struct SelectSmem {
   uint64_t res[2];
 };
 
+// Block primitives take the block size NT as a compile-time constant: reading blockDim
+// would load it from the dispatch packet and wait for every outstanding memory load.
+
 // Exclusive prefix sum of one value per thread over the block; *total gets the sum.
+template <int NT>
 __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
-  const int nw = blockDim.x / kWave;
+  constexpr int nw = NT / kWave;
   const uint32_t x = wave_incl_scan_add(v);
   if (lane == kWave - 1) wsum[w] = x;
   lds_barrier();
@@ -75,11 +88,11 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* t
 }
 
 // Minimum and maximum of the nonzero keys of the block (0 = absent).
-template <class KeyAt>
+template <int NT, class KeyAt>
 __device__ void block_minmax(KeyAt key_at, int n, SelectSmem& sm, uint64_t* mn_out,
                              uint64_t* mx_out) {
   uint64_t mn = ~0ull, mx = 0ull;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+  for (int i = threadIdx.x; i < n; i += NT) {
     const uint64_t k = key_at(i);
     if (k != 0ull) {
       mn = k < mn ? k : mn;
@@ -87,7 +100,8 @@ __device__ void block_minmax(KeyAt key_at, int n, SelectSmem& sm, uint64_t* mn_o
     }
   }
   wave_minmax_u64(mn, mx);
-  const int w = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  const int w = threadIdx.x / kWave;
+  constexpr int nw = NT / kWave;
   if ((threadIdx.x & (kWave - 1)) == 0) {
     sm.red[w] = mn;
     sm.red[16 + w] = mx;
@@ -133,7 +147,7 @@ __device__ void radix_pick_digit(const uint32_t* hist, uint32_t remaining, uint3
 // from zeros, which are absent entries; 1 <= k <= number of nonzero keys).  General
 // 8-bit radix passes from the common prefix of min and max, stopping as soon as a
 // whole bin is needed.  Used for bins that hold too many keys to rank directly.
-template <class KeyAt>
+template <int NT, class KeyAt>
 __device__ uint64_t block_kth_largest(KeyAt key_at, int n, int k, SelectSmem& sm, uint64_t mn,
                                       uint64_t mx) {
   if (mn == mx) return mn;
@@ -145,9 +159,9 @@ __device__ uint64_t block_kth_largest(KeyAt key_at, int n, int k, SelectSmem& sm
     const int lo = shift > 8 ? shift - 8 : 0;
     const uint32_t dmask = (1u << (shift - lo)) - 1u;
     const uint64_t hi_mask = shift >= 64 ? 0ull : (~0ull << shift);
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) sm.hist[i] = 0;
+    for (int i = threadIdx.x; i < 256; i += NT) sm.hist[i] = 0;
     lds_barrier();
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    for (int i = threadIdx.x; i < n; i += NT) {
       const uint64_t key = key_at(i);
       if (key != 0ull && (key & hi_mask) == prefix)
         atomicAdd(&sm.hist[(uint32_t)(key >> lo) & dmask], 1u);
@@ -169,11 +183,11 @@ __device__ uint64_t block_kth_largest(KeyAt key_at, int n, int k, SelectSmem& sm
 // number of nonzero keys.  One histogram of the 11 bits below the common prefix of the
 // keys' min and max places both ranks in a bin; a bin only partly needed is resolved by
 // ranking its few keys directly (or by radix passes if it holds many).
-template <class KeyAt>
+template <int NT, class KeyAt>
 __device__ void block_select2(KeyAt key_at, int n, int ra, int rb, SelectSmem& sm, uint64_t* ta,
                               uint64_t* tb) {
   uint64_t mn, mx;
-  block_minmax(key_at, n, sm, &mn, &mx);
+  block_minmax<NT>(key_at, n, sm, &mn, &mx);
   if (mn == mx) {
     *ta = *tb = mn;
     return;
@@ -184,20 +198,20 @@ __device__ void block_select2(KeyAt key_at, int n, int ra, int rb, SelectSmem& s
   const uint64_t prefix = hb >= 63 ? 0ull : (mx & (~0ull << (hb + 1)));
   auto digit = [&](uint64_t key) -> uint32_t { return (uint32_t)(key >> lo) & dmask; };
 
-  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) sm.hist[i] = 0;
+  for (int i = threadIdx.x; i < kHistBins; i += NT) sm.hist[i] = 0;
   if (threadIdx.x < 2) sm.nlist[threadIdx.x] = 0;
   lds_barrier();
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+  for (int i = threadIdx.x; i < n; i += NT) {
     const uint64_t key = key_at(i);
     if (key != 0ull) atomicAdd(&sm.hist[digit(key)], 1u);
   }
   lds_barrier();
-  const int bpt = kHistBins / blockDim.x;  // blockDim divides kHistBins
+  constexpr int bpt = kHistBins / NT;  // NT divides kHistBins
   const int b0 = threadIdx.x * bpt;
   uint32_t own = 0;
   for (int j = 0; j < bpt; ++j) own += sm.hist[b0 + j];
   uint32_t total;
-  const uint32_t below = block_exclusive_scan(own, sm.wsum, &total);
+  const uint32_t below = block_exclusive_scan<NT>(own, sm.wsum, &total);
   const uint32_t above = total - below - own;  // keys in bins >= b0 + bpt
   const uint32_t rr[2] = {(uint32_t)ra, (uint32_t)rb};
 #pragma unroll
@@ -229,7 +243,7 @@ __device__ void block_select2(KeyAt key_at, int n, int ra, int rb, SelectSmem& s
     small[q] = cnt[q] <= (uint32_t)kListCap;
   }
   if (need[0] || need[1]) {
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    for (int i = threadIdx.x; i < n; i += NT) {
       const uint64_t key = key_at(i);
       if (key == 0ull) continue;
       const uint32_t d = digit(key);
@@ -265,13 +279,177 @@ __device__ void block_select2(KeyAt key_at, int n, int ra, int rb, SelectSmem& s
           return (key != 0ull && digit(key) == bq) ? key : 0ull;
         };
         uint64_t bmn, bmx;
-        block_minmax(in_bin, n, sm, &bmn, &bmx);
-        t[q] = block_kth_largest(in_bin, n, (int)rem[q], sm, bmn, bmx);
+        block_minmax<NT>(in_bin, n, sm, &bmn, &bmx);
+        t[q] = block_kth_largest<NT>(in_bin, n, (int)rem[q], sm, bmn, bmx);
       }
     }
   }
   *ta = t[0];
   *tb = t[1];
+}
+
+// Lower edge *t of the histogram bin that holds the P-th largest of the 32-bit values
+// v[0..n) (1 <= P <= n), and *cnt = how many values are >= *t.  The 2048 bins split
+// [min, max] evenly (by a power of two), so one pass places P; no ranking inside the bin.
+template <int NT>
+__device__ void slice_threshold(const uint32_t* v, int n, int P, SelectSmem& sm, uint32_t* t,
+                                uint32_t* cnt) {
+  constexpr int nw = NT / kWave;
+  constexpr int bpt = kHistBins / NT;
+  const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  uint32_t mn = ~0u, mx = 0u;
+  for (int i = threadIdx.x; i < n; i += NT) {
+    const uint32_t x = v[i];
+    mn = x < mn ? x : mn;
+    mx = x > mx ? x : mx;
+  }
+  for (int i = threadIdx.x; i < kHistBins; i += NT) sm.hist[i] = 0;
+  wave_minmax_u32(mn, mx);
+  if (lane == 0) {
+    sm.red32[w] = mn;
+    sm.red32[16 + w] = mx;
+  }
+  lds_barrier();
+  mn = sm.red32[0];
+  mx = sm.red32[16];
+#pragma unroll
+  for (int i = 1; i < nw; ++i) {
+    mn = sm.red32[i] < mn ? sm.red32[i] : mn;
+    mx = sm.red32[16 + i] > mx ? sm.red32[16 + i] : mx;
+  }
+  const uint32_t range = mx - mn;
+  const int sh = range == 0 ? 0 : max(0, 32 - __builtin_clz(range) - 11);
+  for (int i = threadIdx.x; i < n; i += NT) atomicAdd(&sm.hist[(v[i] - mn) >> sh], 1u);
+  lds_barrier();
+  const int b0 = threadIdx.x * bpt;
+  uint32_t own = 0;
+#pragma unroll
+  for (int j = 0; j < bpt; ++j) own += sm.hist[b0 + j];
+  uint32_t total;
+  const uint32_t below = block_exclusive_scan<NT>(own, sm.wsum, &total);
+  const uint32_t above = total - below - own;  // values in bins >= b0 + bpt
+  const uint32_t p = (uint32_t)P;
+  if (above < p && p <= above + own) {
+    uint32_t a = above;
+#pragma unroll
+    for (int j = bpt - 1; j >= 0; --j) {
+      const uint32_t h = sm.hist[b0 + j];
+      if (a < p && p <= a + h) {
+        sm.bc[0] = b0 + j;
+        sm.bc[1] = a + h;
+      }
+      a += h;
+    }
+  }
+  lds_barrier();
+  *t = mn + (sm.bc[0] << sh);
+  *cnt = sm.bc[1];
+}
+
+// The k-th largest of n distinct nonzero 64-bit keys held in LDS (1 <= k <= n).  A
+// histogram of the keys' high words (2048 bins between their min and max) locates the
+// bin holding it; if that whole bin is needed the answer is its smallest key, otherwise
+// the bin's keys are ranked directly (general radix passes if the bin is very full).
+template <int NT>
+__device__ uint64_t block_kth_exact(const uint64_t* keys, int n, int k, SelectSmem& sm,
+                                    uint64_t* list) {
+  constexpr int nw = NT / kWave;
+  constexpr int bpt = kHistBins / NT;
+  const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  uint32_t mn = ~0u, mx = 0u;
+  for (int i = threadIdx.x; i < n; i += NT) {
+    const uint32_t h = (uint32_t)(keys[i] >> 32);
+    mn = h < mn ? h : mn;
+    mx = h > mx ? h : mx;
+  }
+  for (int i = threadIdx.x; i < kHistBins; i += NT) sm.hist[i] = 0;
+  if (threadIdx.x == 0) sm.bc[4] = 0;
+  wave_minmax_u32(mn, mx);
+  if (lane == 0) {
+    sm.red32[w] = mn;
+    sm.red32[16 + w] = mx;
+  }
+  lds_barrier();
+  mn = sm.red32[0];
+  mx = sm.red32[16];
+#pragma unroll
+  for (int i = 1; i < nw; ++i) {
+    mn = sm.red32[i] < mn ? sm.red32[i] : mn;
+    mx = sm.red32[16 + i] > mx ? sm.red32[16 + i] : mx;
+  }
+  auto at = [&](int i) -> uint64_t { return keys[i]; };
+  if (mn == mx) {  // one high word: rank by the low words
+    uint64_t kmn, kmx;
+    block_minmax<NT>(at, n, sm, &kmn, &kmx);
+    return block_kth_largest<NT>(at, n, k, sm, kmn, kmx);
+  }
+  const int sh = max(0, 32 - __builtin_clz(mx - mn) - 11);
+  auto bin_of = [&](uint64_t key) -> uint32_t { return ((uint32_t)(key >> 32) - mn) >> sh; };
+  for (int i = threadIdx.x; i < n; i += NT) atomicAdd(&sm.hist[bin_of(keys[i])], 1u);
+  lds_barrier();
+  const int b0 = threadIdx.x * bpt;
+  uint32_t own = 0;
+#pragma unroll
+  for (int j = 0; j < bpt; ++j) own += sm.hist[b0 + j];
+  uint32_t total;
+  const uint32_t below = block_exclusive_scan<NT>(own, sm.wsum, &total);
+  const uint32_t above = total - below - own;
+  const uint32_t kk = (uint32_t)k;
+  if (above < kk && kk <= above + own) {
+    uint32_t a = above;
+#pragma unroll
+    for (int j = bpt - 1; j >= 0; --j) {
+      const uint32_t h = sm.hist[b0 + j];
+      if (a < kk && kk <= a + h) {
+        sm.bc[0] = b0 + j;
+        sm.bc[1] = a;
+      }
+      a += h;
+    }
+  }
+  lds_barrier();
+  const uint32_t tb = sm.bc[0];
+  const uint32_t need = kk - sm.bc[1];  // rank of the answer inside bin tb
+  const uint32_t cnt = sm.hist[tb];
+  if (cnt == need) {  // every key of the bin is in: the answer is the bin's smallest
+    uint64_t m = ~0ull, unused = 0ull;
+    for (int i = threadIdx.x; i < n; i += NT) {
+      const uint64_t key = keys[i];
+      if (bin_of(key) == tb && key < m) m = key;
+    }
+    wave_minmax_u64(m, unused);
+    if (lane == 0) sm.res64[w] = m;
+    lds_barrier();
+    uint64_t r = sm.res64[0];
+#pragma unroll
+    for (int i = 1; i < nw; ++i) r = sm.res64[i] < r ? sm.res64[i] : r;
+    lds_barrier();
+    return r;
+  }
+  if (cnt <= (uint32_t)kMergeListCap && cnt <= (uint32_t)NT) {
+    for (int i = threadIdx.x; i < n; i += NT) {
+      const uint64_t key = keys[i];
+      if (bin_of(key) == tb) list[atomicAdd(&sm.bc[4], 1u)] = key;
+    }
+    lds_barrier();
+    if (threadIdx.x < cnt) {
+      const uint64_t x = list[threadIdx.x];
+      uint32_t greater = 0;
+      for (uint32_t j = 0; j < cnt; ++j) greater += list[j] > x;
+      if (greater == need - 1) sm.res64[0] = x;
+    }
+    lds_barrier();
+    const uint64_t r = sm.res64[0];
+    lds_barrier();
+    return r;
+  }
+  auto bin_at = [&](int i) -> uint64_t {
+    const uint64_t key = keys[i];
+    return bin_of(key) == tb ? key : 0ull;
+  };
+  uint64_t bmn, bmx;
+  block_minmax<NT>(bin_at, n, sm, &bmn, &bmx);
+  return block_kth_largest<NT>(bin_at, n, (int)need, sm, bmn, bmx);
 }
 
 __device__ __forceinline__ uint64_t compose_key(uint32_t score_key, uint32_t idx) {
@@ -352,14 +530,25 @@ __device__ __forceinline__ f16x8 q_operand(u32x4 v, float scale, f16x8*) {
 
 // ------------------------------------------------------------------ scan kernel
 
-template <class KT, int HT, int PS>
+constexpr int kSubTiles = 16;                          // tiles per wave per unrolled pass
+constexpr int kSubRows = 16 * kScanWaves * kSubTiles;  // 2048 rows per pass
+constexpr int kSliceTiles = 2 * kSubTiles * kScanWaves;
+
+// Per-call buffers of the indexer, carved from the caller's workspace.
+struct IndexerWs {
+  uint64_t* cand;    // [B][n_slices][cap] candidate selection keys of each slice
+  uint64_t* bound;   // [B][n_slices] every key of the slice not in cand is below this
+  uint32_t* count;   // [B][n_slices] candidates of each slice
+  uint32_t* scores;  // [B][n_c] score key of every row
+};
+
+template <class KT, int HT>
 __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t seq_stride,
     int64_t n_c, const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx, int n_heads,
-    int top_k, int slice_rows, int n_slices, int slices_per_wg, int wg_per_query, int prefix,
-    int cand_stride, uint64_t* __restrict__ cand) {
+    int n_slices, int slices_per_wg, int wg_per_query, int prefix, int cap, IndexerWs ws) {
   typedef typename KT::Op Op;
-  __shared__ uint32_t s_score[kMaxSliceRows];
+  __shared__ uint32_t s_score[kSliceRows];
   __shared__ SelectSmem sm;
 
   const int b = blockIdx.x / wg_per_query;
@@ -369,8 +558,9 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int g = lane >> 4;
   const int n = lane & 15;
-  const int64_t row_base = (int64_t)slice0 * slice_rows;              // compressed row index
-  const int64_t rows_total = min((int64_t)n_sl * slice_rows, n_c - row_base);
+  const int64_t row_base = (int64_t)slice0 * kSliceRows;              // compressed row index
+  const int64_t rows_total = min((int64_t)n_sl * kSliceRows, n_c - row_base);
+  const int n_pass = (int)((rows_total + kSubRows - 1) / kSubRows);
   const int64_t seq_row0 = (int64_t)b * seq_stride + row_base;
 
   // Indexer query fragments (A operand, head n of each 16-head tile) and the weights of
@@ -412,17 +602,15 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
     }
   }
 
-  // The wave's tile sequence: slot k -> slice k / per_slice, tile w + 8m of that slice.
-  // Every slot loads (rows clamped into range) and computes, so the loads are straight-
-  // line code and the ring keeps kRing tiles in flight; only valid rows store a score.
-  // PS = tiles per wave per slice (slice_rows / (16 * kScanWaves)), a multiple of kRing;
-  // the slice's tile loop is unrolled whole so the ring's waits are counted exactly.
-  const int tiles_per_slice = PS * kScanWaves;
-  const int per_slice = PS;
-  const int total = n_sl * per_slice;
+  // The wave's tile sequence: slot k -> pass k / kSubTiles, tile wave + 8m of that pass
+  // (m = k % kSubTiles).  Every slot loads (rows clamped into range) and computes, so the
+  // loads are straight-line code and the ring keeps kRing tiles in flight across passes
+  // and slices; only valid rows store a score.  A pass is unrolled whole so that the
+  // ring's waits are counted exactly.
+  const int total = n_pass * kSubTiles;
   auto slot_tile = [&](int k) -> int {
-    const int j = k / per_slice, m = k - j * per_slice;
-    return j * tiles_per_slice + wave + kScanWaves * m;
+    const int ps = k / kSubTiles, m = k - ps * kSubTiles;
+    return ps * (kSubTiles * kScanWaves) + wave + kScanWaves * m;
   };
   const int rows_last = (int)rows_total - 1;
   const uint8_t* kcodes = codes + seq_row0 * KT::kRowBytes;
@@ -435,157 +623,173 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
 #pragma unroll
   for (int d = 0; d < kRing; ++d) load_slot(ring[d], min(d, total - 1));
 
-  for (int j = 0; j < n_sl; ++j) {
+  for (int ps = 0; ps < n_pass; ++ps) {
 #pragma unroll
-    for (int m = 0; m < PS; ++m) {
-      {
-        const int d = m % kRing;
-        const int k = j * per_slice + m;
-        Op kb[4];
-        ring[d].decode(kb);
-        load_slot(ring[d], min(k + kRing, total - 1));
-        f32x4 acc[HT];
+    for (int m = 0; m < kSubTiles; ++m) {
+      const int d = m % kRing;
+      const int k = ps * kSubTiles + m;
+      Op kb[4];
+      ring[d].decode(kb);
+      load_slot(ring[d], min(k + kRing, total - 1));
+      f32x4 acc[HT];
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int ht = 0; ht < HT; ++ht) acc[ht] = KT::mma(qa[ht][t], kb[t], acc[ht]);
-        float sc = 0.0f;
+        for (int ht = 0; ht < HT; ++ht) acc[ht] = KT::mma(qa[ht][t], kb[t], acc[ht]);
+      float sc = 0.0f;
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
+      for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sc += wv[ht][i] * fmaxf(acc[ht][i], 0.0f);
-        sc = wave_sum_rows(sc);
-        const int tile = slot_tile(k);
-        if (g == 0 && (int64_t)tile * 16 + n < rows_total)
-          s_score[(tile - j * tiles_per_slice) * 16 + n] = f32_order_key(sc);
-      }
+        for (int i = 0; i < 4; ++i) sc += wv[ht][i] * fmaxf(acc[ht][i], 0.0f);
+      sc = wave_sum_rows(sc);
+      const int row = slot_tile(k) * 16 + n;  // within the workgroup's rows
+      if (g == 0 && row < rows_total) s_score[row & (kSliceRows - 1)] = f32_order_key(sc);
     }
+    if ((ps & 1) == 0 && ps + 1 < n_pass) continue;  // the slice has a second pass
 
-    // ---- slice j complete: keep its top-k1 with its top-P first
-    const int64_t srow0 = row_base + (int64_t)j * slice_rows;
-    const int rows = (int)min((int64_t)slice_rows, n_c - srow0);
-    const int k1 = min(top_k, rows);
-    const int pk = min(prefix, k1);
+    // ---- slice complete: emit its candidates, its bound and its scores
+    const int j = ps >> 1;
+    const int64_t srow0 = row_base + (int64_t)j * kSliceRows;
+    const int rows = (int)min((int64_t)kSliceRows, n_c - srow0);
+    const int64_t si = (int64_t)b * n_slices + slice0 + j;
     lds_barrier();
-    auto key_at = [&](int i) -> uint64_t { return compose_key(s_score[i], (uint32_t)(srow0 + i)); };
-    uint64_t t_k, t_p;
-    block_select2(key_at, rows, k1, pk, sm, &t_k, &t_p);
-    const int chunk = (rows + kScanThreads - 1) / kScanThreads;
-    const int p0 = threadIdx.x * chunk, p1 = min(p0 + chunk, rows);
-    uint32_t ca = 0, cb = 0;
-    for (int i = p0; i < p1; ++i) {
-      const uint64_t key = key_at(i);
-      ca += key >= t_p;
-      cb += key >= t_k && key < t_p;
+    uint32_t* sc_out = ws.scores + (int64_t)b * n_c + srow0;
+    for (int i = threadIdx.x; i < rows; i += kScanThreads) sc_out[i] = s_score[i];
+    const int pe = min(prefix, rows);
+    uint32_t t32 = 0u, cnt = (uint32_t)rows;
+    if (pe < rows) slice_threshold<kScanThreads>(s_score, rows, pe, sm, &t32, &cnt);
+    uint64_t* dst = ws.cand + si * cap;
+    uint64_t bound;
+    uint32_t emitted;
+    if (cnt <= (uint32_t)cap) {  // every key whose score is >= t32
+      uint32_t c = 0;
+      for (int i = threadIdx.x; i < rows; i += kScanThreads) c += s_score[i] >= t32;
+      uint32_t pos = block_exclusive_scan<kScanThreads>(c, sm.wsum, &emitted);
+      for (int i = threadIdx.x; i < rows; i += kScanThreads) {
+        const uint32_t v = s_score[i];
+        if (v >= t32) dst[pos++] = compose_key(v, (uint32_t)(srow0 + i));
+      }
+      bound = pe < rows ? ((uint64_t)t32 << 32) : 0ull;
+    } else {  // too many keys share the boundary bin: the exact top-cap instead
+      auto key_at = [&](int i) -> uint64_t { return compose_key(s_score[i], (uint32_t)(srow0 + i)); };
+      uint64_t t64, unused;
+      block_select2<kScanThreads>(key_at, rows, cap, cap, sm, &t64, &unused);
+      uint32_t c = 0;
+      for (int i = threadIdx.x; i < rows; i += kScanThreads) c += key_at(i) >= t64;
+      uint32_t pos = block_exclusive_scan<kScanThreads>(c, sm.wsum, &emitted);
+      for (int i = threadIdx.x; i < rows; i += kScanThreads) {
+        const uint64_t key = key_at(i);
+        if (key >= t64) dst[pos++] = key;
+      }
+      bound = t64;
     }
-    uint32_t tot;
-    const uint32_t base = block_exclusive_scan((ca << 16) | cb, sm.wsum, &tot);
-    uint32_t pa = base >> 16, pb = pk + (base & 0xFFFFu);
-    uint64_t* dst = cand + ((int64_t)b * n_slices + slice0 + j) * cand_stride;
-    for (int i = p0; i < p1; ++i) {
-      const uint64_t key = key_at(i);
-      if (key >= t_p) dst[pa++] = key;
-      else if (key >= t_k) dst[pb++] = key;
+    if (threadIdx.x == 0) {
+      ws.count[si] = emitted;
+      ws.bound[si] = bound;
     }
-    lds_barrier();
+    lds_barrier();  // s_score and sm are free for the next slice
   }
 }
 
 // ------------------------------------------------------------------ merge kernel
 
 __global__ __launch_bounds__(kMergeThreads) void indexer_merge_kernel(
-    const uint64_t* __restrict__ cand, int64_t n_c, int top_k, int slice_rows, int n_slices,
-    int cand_stride, int prefix, int32_t* __restrict__ topk) {
+    IndexerWs ws, int64_t n_c, int top_k, int n_slices, int cap, int32_t* __restrict__ topk) {
   __shared__ uint64_t s_buf[kMergeCap];
-  __shared__ uint64_t s_tmp[kMaxTopK];
-  __shared__ SelectSmem sm;
+  __shared__ uint64_t s_list[kMergeListCap];
+  __shared__ uint64_t s_bound[kMaxMergeSlices];
+  __shared__ uint32_t s_off[kMaxMergeSlices + 1];
   __shared__ int s_sat[kMaxMergeSlices];
-  __shared__ int s_nsat;
+  __shared__ SelectSmem sm;
+  constexpr int NT = kMergeThreads;
 
   const int b = blockIdx.x;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int k1 = (int)min((int64_t)top_k, n_c);
-  const uint64_t* cb = cand + (int64_t)b * n_slices * cand_stride;
   int32_t* out = topk + (int64_t)b * top_k;
-  for (int i = k1 + threadIdx.x; i < top_k; i += blockDim.x) out[i] = -1;
+  for (int i = k1 + threadIdx.x; i < top_k; i += NT) out[i] = -1;
   if (k1 == 0) return;
+  const int64_t s0 = (int64_t)b * n_slices;
 
-  auto slice_count = [&](int s) -> int {
-    const int64_t r = min((int64_t)slice_rows, n_c - (int64_t)s * slice_rows);
-    return (int)min((int64_t)top_k, r);
-  };
-
-  if (n_slices == 1) {  // the single slice holds exactly the top-k1
-    for (int i = threadIdx.x; i < k1; i += blockDim.x) out[i] = key_index(cb[i]);
-    return;
+  // Candidate counts -> offsets in the buffer (n_slices <= NT).
+  const uint32_t c = threadIdx.x < n_slices ? ws.count[s0 + threadIdx.x] : 0u;
+  if (threadIdx.x < n_slices) s_bound[threadIdx.x] = ws.bound[s0 + threadIdx.x];
+  uint32_t n_buf;
+  const uint32_t off = block_exclusive_scan<NT>(c, sm.wsum, &n_buf);
+  if (threadIdx.x < n_slices) s_off[threadIdx.x] = off;
+  if (threadIdx.x == 0) s_off[n_slices] = n_buf;
+  lds_barrier();
+  for (int s = wave; s < n_slices; s += NT / kWave) {  // one wave per slice at a time
+    const uint32_t o = s_off[s], m = s_off[s + 1] - o;
+    const uint64_t* src = ws.cand + (s0 + s) * cap;
+    for (uint32_t j = lane; j < m; j += kWave) s_buf[o + j] = src[j];
   }
-
-  // Top-P prefix of every slice at stride `prefix`; missing entries are 0.
-  int n_buf = n_slices * prefix;
-  for (int i = threadIdx.x; i < n_buf; i += blockDim.x) {
-    const int s = i / prefix, j = i - s * prefix;
-    s_buf[i] = j < slice_count(s) ? cb[(int64_t)s * cand_stride + j] : 0ull;
-  }
-  if (threadIdx.x == 0) s_nsat = 0;
   lds_barrier();
 
-  auto buf_at = [&](int i) -> uint64_t { return s_buf[i]; };
-  uint64_t kth, unused;
-  block_select2(buf_at, n_buf, k1, k1, sm, &kth, &unused);
+  // The k1-th largest candidate; 1 (accept all) while there are fewer than k1.
+  uint64_t kth = (int)n_buf >= k1 ? block_kth_exact<NT>(s_buf, (int)n_buf, k1, sm, s_list) : 1ull;
 
-  // A slice whose whole prefix is >= the k1-th key may hold more winners below it.
-  for (int s = threadIdx.x; s < n_slices; s += blockDim.x) {
-    const int cnt = slice_count(s);
-    if (cnt <= prefix) continue;
-    int ge = 0;
-    for (int j = 0; j < prefix; ++j) ge += s_buf[s * prefix + j] >= kth;
-    if (ge == prefix) s_sat[atomicAdd(&s_nsat, 1)] = s;
-  }
-  lds_barrier();
-  const int n_sat = s_nsat;
-
-  // Keep the k1 largest of s_buf[0..n) in s_buf[0..k1).
-  auto compact_topk = [&](int n, uint64_t t) {
-    const int chunk = (n + kMergeThreads - 1) / kMergeThreads;
-    const int p0 = threadIdx.x * chunk, p1 = min(p0 + chunk, n);
-    uint32_t c = 0;
-    for (int p = p0; p < p1; ++p) c += s_buf[p] >= t;
-    uint32_t total;
-    uint32_t pos = block_exclusive_scan(c, sm.wsum, &total);
-    for (int p = p0; p < p1; ++p)
-      if (s_buf[p] >= t) s_tmp[pos++] = s_buf[p];
+  // Slices whose bound lies above kth may hold winners among the keys they did not send.
+  {
+    const uint32_t sat = threadIdx.x < n_slices && s_bound[threadIdx.x] > kth;
+    uint32_t n_sat;
+    const uint32_t pos = block_exclusive_scan<NT>(sat, sm.wsum, &n_sat);
+    if (sat) s_sat[pos] = threadIdx.x;
     lds_barrier();
-    for (int i = threadIdx.x; i < k1; i += blockDim.x) s_buf[i] = s_tmp[i];
-    lds_barrier();
-  };
-
-  if (n_sat > 0) {  // rare: stream the rest of each saturated slice, keeping keys > kth
-    compact_topk(n_buf, kth);
-    n_buf = k1;
-    for (int si = 0; si < n_sat; ++si) {
-      const int s = s_sat[si];
-      const int cnt = slice_count(s);
-      for (int j0 = prefix; j0 < cnt; j0 += kMergeCap - k1) {
-        const int m = min(kMergeCap - k1, cnt - j0);
-        for (int i = threadIdx.x; i < m; i += blockDim.x) {
-          const uint64_t key = cb[(int64_t)s * cand_stride + j0 + i];
-          s_buf[k1 + i] = key > kth ? key : 0ull;
-        }
+    for (uint32_t q = 0; q < n_sat; ++q) {
+      const int s = s_sat[q];
+      if (!(s_bound[s] > kth)) continue;  // kth has risen past this slice's bound
+      // Keep only the current winners (>= kth), in buffer order, to make room.
+      {
+        const int chunk = ((int)n_buf + NT - 1) / NT;
+        const int p0 = threadIdx.x * chunk, p1 = min(p0 + chunk, (int)n_buf);
+        uint32_t cw = 0;
+        for (int p = p0; p < p1; ++p) cw += s_buf[p] >= kth;
+        uint32_t kept;
+        uint32_t w = block_exclusive_scan<NT>(cw, sm.wsum, &kept);
+        for (int p = p0; p < p1; ++p)
+          if (s_buf[p] >= kth) s_list[w++] = s_buf[p];
         lds_barrier();
-        block_select2(buf_at, k1 + m, k1, k1, sm, &kth, &unused);
-        compact_topk(k1 + m, kth);
+        for (uint32_t i = threadIdx.x; i < kept; i += NT) s_buf[i] = s_list[i];
+        n_buf = kept;
+        lds_barrier();
       }
+      // Append the slice's unsent keys >= kth, read back from its stored scores.
+      {
+        const int64_t srow0 = (int64_t)s * kSliceRows;
+        const int rows = (int)min((int64_t)kSliceRows, n_c - srow0);
+        const uint32_t* sc = ws.scores + (int64_t)b * n_c + srow0;
+        const uint64_t bnd = s_bound[s];
+        const int chunk = (rows + NT - 1) / NT;
+        const int p0 = threadIdx.x * chunk, p1 = min(p0 + chunk, rows);
+        uint32_t ca = 0;
+        for (int i = p0; i < p1; ++i) {
+          const uint64_t key = compose_key(sc[i], (uint32_t)(srow0 + i));
+          ca += key >= kth && key < bnd;
+        }
+        uint32_t added;
+        uint32_t w = n_buf + block_exclusive_scan<NT>(ca, sm.wsum, &added);
+        for (int i = p0; i < p1; ++i) {
+          const uint64_t key = compose_key(sc[i], (uint32_t)(srow0 + i));
+          if (key >= kth && key < bnd) s_buf[w++] = key;
+        }
+        n_buf += added;
+        lds_barrier();
+        if (threadIdx.x == 0) s_bound[s] = 0ull;
+      }
+      kth = (int)n_buf >= k1 ? block_kth_exact<NT>(s_buf, (int)n_buf, k1, sm, s_list) : 1ull;
     }
   }
 
   // Write the selected indices in buffer order (deterministic).
-  const int chunk = (n_buf + kMergeThreads - 1) / kMergeThreads;
-  const int p0 = threadIdx.x * chunk, p1 = min(p0 + chunk, n_buf);
-  uint32_t c = 0;
-  for (int p = p0; p < p1; ++p) c += s_buf[p] >= kth;
+  const int chunk = ((int)n_buf + NT - 1) / NT;
+  const int p0 = threadIdx.x * chunk, p1 = min(p0 + chunk, (int)n_buf);
+  uint32_t cw = 0;
+  for (int p = p0; p < p1; ++p) cw += s_buf[p] >= kth;
   uint32_t total;
-  uint32_t pos = block_exclusive_scan(c, sm.wsum, &total);
+  uint32_t pos = block_exclusive_scan<NT>(cw, sm.wsum, &total);
   for (int p = p0; p < p1; ++p)
     if (s_buf[p] >= kth) out[pos++] = key_index(s_buf[p]);
 }
@@ -593,23 +797,19 @@ __global__ __launch_bounds__(kMergeThreads) void indexer_merge_kernel(
 template <class KT, int HT>
 void launch_scan(hipStream_t stream, const uint8_t* codes, const uint8_t* scales,
                  int64_t seq_stride, int64_t n_c, const uint16_t* q_idx, const float* w_idx,
-                 int batch, int n_heads, int top_k, const IndexerPlan& plan, uint64_t* cand) {
-#define CSAKV_SCAN_PS(PS)                                                                         \
-  hipLaunchKernelGGL((indexer_scan_kernel<KT, HT, PS>), dim3(batch * plan.wg_per_query),          \
-                     dim3(kScanThreads), 0, stream, codes, scales, seq_stride, n_c, q_idx, w_idx, \
-                     n_heads, top_k, plan.slice_rows, plan.n_slices, plan.slices_per_wg,          \
-                     plan.wg_per_query, plan.prefix, plan.cand_stride, cand)
-  if (plan.slice_rows == 16 * kScanWaves * 16) CSAKV_SCAN_PS(16);
-  else CSAKV_SCAN_PS(32);
-#undef CSAKV_SCAN_PS
+                 int batch, int n_heads, const IndexerPlan& plan, const IndexerWs& ws) {
+  hipLaunchKernelGGL((indexer_scan_kernel<KT, HT>), dim3(batch * plan.wg_per_query),
+                     dim3(kScanThreads), 0, stream, codes, scales, seq_stride, n_c, q_idx, w_idx,
+                     n_heads, plan.n_slices, plan.slices_per_wg, plan.wg_per_query, plan.prefix,
+                     plan.cap, ws);
 }
 
 template <class KT>
 void launch_scan_ht(int ht, hipStream_t stream, const uint8_t* codes, const uint8_t* scales,
                     int64_t seq_stride, int64_t n_c, const uint16_t* q_idx, const float* w_idx,
-                    int batch, int n_heads, int top_k, const IndexerPlan& plan, uint64_t* cand) {
+                    int batch, int n_heads, const IndexerPlan& plan, const IndexerWs& ws) {
 #define CSAKV_SCAN(H) \
-  launch_scan<KT, H>(stream, codes, scales, seq_stride, n_c, q_idx, w_idx, batch, n_heads, top_k, plan, cand)
+  launch_scan<KT, H>(stream, codes, scales, seq_stride, n_c, q_idx, w_idx, batch, n_heads, plan, ws)
   switch (ht) {
     case 1: CSAKV_SCAN(1); break;
     case 2: CSAKV_SCAN(2); break;
@@ -619,36 +819,57 @@ void launch_scan_ht(int ht, hipStream_t stream, const uint8_t* codes, const uint
 #undef CSAKV_SCAN
 }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+IndexerWs carve_indexer_ws(void* base, int batch, const IndexerPlan& plan) {
+  uint8_t* p = static_cast<uint8_t*>(base);
+  const size_t ns = (size_t)batch * plan.n_slices;
+  IndexerWs ws;
+  ws.cand = reinterpret_cast<uint64_t*>(p);
+  p += align256(ns * plan.cap * sizeof(uint64_t));
+  ws.bound = reinterpret_cast<uint64_t*>(p);
+  p += align256(ns * sizeof(uint64_t));
+  ws.count = reinterpret_cast<uint32_t*>(p);
+  p += align256(ns * sizeof(uint32_t));
+  ws.scores = reinterpret_cast<uint32_t*>(p);
+  return ws;
+}
+
 }  // namespace
 
 IndexerPlan plan_indexer(int batch, int64_t n_c, int top_k) {
   IndexerPlan p{};
-  // 2048-row slices (4096 for very long contexts, so the merge input stays bounded);
-  // about one workgroup per CU (256), each owning a run of slices of one query.
-  int64_t rows = 2048;
-  if ((n_c + rows - 1) / rows > kMaxMergeSlices / 2) rows = kMaxSliceRows;
-  p.slice_rows = (int)rows;
-  p.n_slices = n_c > 0 ? (int)((n_c + rows - 1) / rows) : 0;
-  p.cand_stride = (int)(top_k < rows ? top_k : rows);
+  // 4096-row slices, about one scan workgroup per CU (256), each owning a run of slices
+  // of one query.  A slice sends its top-P or a few more (at least 4x its expected
+  // share k / n_slices of the winners); the merge buffer holds every slice's cap.
+  p.n_c = n_c;
+  p.slice_rows = kSliceRows;
+  p.n_slices = n_c > 0 ? (int)((n_c + kSliceRows - 1) / kSliceRows) : 0;
   if (p.n_slices > 0) {
     int64_t wg = (256 + batch - 1) / batch;
     if (wg > p.n_slices) wg = p.n_slices;
     p.slices_per_wg = (int)((p.n_slices + wg - 1) / wg);
     p.wg_per_query = (p.n_slices + p.slices_per_wg - 1) / p.slices_per_wg;
+    p.cap = (int)std::min<int64_t>(kSliceRows, kMergeCap / p.n_slices);
+    if (p.n_slices == 1) {
+      p.prefix = top_k;
+    } else {
+      int64_t want = (4 * (int64_t)top_k + p.n_slices - 1) / p.n_slices;
+      if (want < 16) want = 16;
+      p.prefix = (int)std::min<int64_t>(want, p.cap / 2);
+    }
   }
-  const int per_slice = p.n_slices > 0 ? (top_k + p.n_slices - 1) / p.n_slices : top_k;
-  int pre = 32;
-  while (pre < 4 * per_slice) pre <<= 1;
-  p.prefix = pre < p.cand_stride ? pre : p.cand_stride;
   return p;
 }
 
 size_t indexer_workspace_bytes(int batch, const IndexerPlan& plan) {
-  return (size_t)batch * plan.n_slices * plan.cand_stride * sizeof(uint64_t);
+  const size_t ns = (size_t)batch * plan.n_slices;
+  return align256(ns * plan.cap * sizeof(uint64_t)) + align256(ns * sizeof(uint64_t)) +
+         align256(ns * sizeof(uint32_t)) + align256((size_t)batch * plan.n_c * sizeof(uint32_t));
 }
 
 bool indexer_supported(const IndexerPlan& plan) {
-  return plan.n_slices <= kMaxMergeSlices && (int64_t)plan.n_slices * plan.prefix <= kMergeCap;
+  return plan.n_slices <= kMaxMergeSlices && (plan.n_slices == 0 || plan.prefix >= 1);
 }
 
 hipError_t launch_indexer(int key_fmt, const uint8_t* codes, const uint8_t* scales,
@@ -656,20 +877,20 @@ hipError_t launch_indexer(int key_fmt, const uint8_t* codes, const uint8_t* scal
                           const float* w_idx, int batch, int n_heads, int top_k,
                           const IndexerPlan& plan, void* workspace, int32_t* topk,
                           hipStream_t stream) {
-  uint64_t* cand = static_cast<uint64_t*>(workspace);
+  const IndexerWs ws = carve_indexer_ws(workspace, batch, plan);
   if (plan.n_slices > 0) {
     const int ht = (n_heads + 15) / 16;
     if (key_fmt == 0)
       launch_scan_ht<KeyTileBf16>(ht, stream, codes, scales, seq_stride, n_c, q_idx, w_idx, batch,
-                                  n_heads, top_k, plan, cand);
+                                  n_heads, plan, ws);
     else
       launch_scan_ht<KeyTileFp4>(ht, stream, codes, scales, seq_stride, n_c, q_idx, w_idx, batch,
-                                 n_heads, top_k, plan, cand);
+                                 n_heads, plan, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(indexer_merge_kernel, dim3(batch), dim3(kMergeThreads), 0, stream, cand, n_c,
-                     top_k, plan.slice_rows, plan.n_slices, plan.cand_stride, plan.prefix, topk);
+  hipLaunchKernelGGL(indexer_merge_kernel, dim3(batch), dim3(kMergeThreads), 0, stream, ws, n_c,
+                     top_k, plan.n_slices, plan.cap, topk);
   return hipGetLastError();
 }
 
