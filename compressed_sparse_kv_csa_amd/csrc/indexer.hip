@@ -459,17 +459,30 @@ __device__ __forceinline__ int32_t key_index(uint64_t key) { return (int32_t)(~(
 
 // ------------------------------------------------------------------ key tiles
 
-// Lane (g, n) owns row n of a 16-row tile and 32 of its 128 channels.
+// Lane (g, n) owns row n of a 16-row tile and 32 of its 128 channels.  Tiles are read
+// through buffer resources whose base is the tile's first row and whose size ends at the
+// workgroup's last row: a row past the end reads as zeros (no clamping, no fault), and
+// every lane's offset inside a tile is a constant.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
+__device__ __forceinline__ Rsrc make_rsrc(const uint8_t* base, int64_t bytes) {
+  const int n = bytes > 0 ? (int)bytes : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, n, kRsrcWord3);
+}
 
 // bf16 rows: in K-step t the lane supplies channels 32t + 8g .. 32t + 8g + 7.
 struct KeyTileBf16 {
   typedef bf16x8 Op;
   u32x4 c[4];
   static constexpr int kRowBytes = kIdxDim * 2;
-  __device__ __forceinline__ void load(const uint8_t* codes, const uint8_t*, int row, int g) {
-    const uint8_t* p = codes + row * kRowBytes + 16 * g;
+  static constexpr bool kScales = false;
+  static __device__ __forceinline__ int code_offset(int n, int g) { return n * kRowBytes + 16 * g; }
+  static __device__ __forceinline__ int scale_offset(int, int) { return 0; }
+  __device__ __forceinline__ void set_lane(int) {}
+  __device__ __forceinline__ void load(Rsrc rc, Rsrc, int co, int) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) c[t] = *reinterpret_cast<const u32x4*>(p + 64 * t);
+    for (int t = 0; t < 4; ++t) c[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, co + 64 * t, 0, 0));
   }
   __device__ __forceinline__ void decode(Op* op) const {
 #pragma unroll
@@ -486,12 +499,14 @@ struct KeyTileFp4 {
   u32x4 c;
   uint32_t s;  // the dword of scale bytes holding blocks 2g and 2g + 1
   int hi;      // 1 when those two bytes are the dword's upper half (odd g)
+  __device__ __forceinline__ void set_lane(int g) { hi = g & 1; }
   static constexpr int kRowBytes = kIdxDim / 2;
-  __device__ __forceinline__ void load(const uint8_t* codes, const uint8_t* scales, int row,
-                                       int g) {
-    c = *reinterpret_cast<const u32x4*>(codes + row * kRowBytes + 16 * g);
-    s = *reinterpret_cast<const uint32_t*>(scales + row * (kIdxDim / 16) + 4 * (g >> 1));
-    hi = g & 1;
+  static constexpr bool kScales = true;
+  static __device__ __forceinline__ int code_offset(int n, int g) { return n * kRowBytes + 16 * g; }
+  static __device__ __forceinline__ int scale_offset(int n, int g) { return n * (kIdxDim / 16) + 4 * (g >> 1); }
+  __device__ __forceinline__ void load(Rsrc rc, Rsrc rs, int co, int so) {
+    c = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, co, 0, 0));
+    s = __builtin_amdgcn_raw_buffer_load_b32(rs, so, 0, 0);
   }
   __device__ __forceinline__ void decode(Op* op) const {
     // Both E4M3 scales as an fp16 pair (exact), then each broadcast to a pair.
@@ -532,7 +547,7 @@ __device__ __forceinline__ f16x8 q_operand(u32x4 v, float scale, f16x8*) {
 
 constexpr int kSubTiles = 16;                          // tiles per wave per unrolled pass
 constexpr int kSubRows = 16 * kScanWaves * kSubTiles;  // 2048 rows per pass
-constexpr int kSliceTiles = 2 * kSubTiles * kScanWaves;
+constexpr int kPassesPerSlice = kSliceRows / kSubRows;
 
 // Per-call buffers of the indexer, carved from the caller's workspace.
 struct IndexerWs {
@@ -548,7 +563,7 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
     int64_t n_c, const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx, int n_heads,
     int n_slices, int slices_per_wg, int wg_per_query, int prefix, int cap, IndexerWs ws) {
   typedef typename KT::Op Op;
-  __shared__ uint32_t s_score[kSliceRows];
+  __shared__ uint32_t s_score[kSliceRows + kWave];  // + one dummy slot per lane
   __shared__ SelectSmem sm;
 
   const int b = blockIdx.x / wg_per_query;
@@ -563,9 +578,46 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
   const int n_pass = (int)((rows_total + kSubRows - 1) / kSubRows);
   const int64_t seq_row0 = (int64_t)b * seq_stride + row_base;
 
+  // The wave's tile sequence: slot k -> pass k / kSubTiles, tile wave + 8m of that pass
+  // (m = k % kSubTiles).  Every slot loads (rows clamped into range) and computes, so the
+  // loads are straight-line code and the ring keeps kRing tiles in flight across passes
+  // and slices; only valid rows store a score.  A pass is unrolled whole so that the
+  // ring's waits are counted exactly.
+  const int total = n_pass * kSubTiles;
+  auto slot_tile = [&](int k) -> int {
+    const int ps = k / kSubTiles, m = k - ps * kSubTiles;
+    return ps * (kSubTiles * kScanWaves) + wave + kScanWaves * m;
+  };
+  const uint8_t* kcodes = codes + seq_row0 * KT::kRowBytes;
+  const uint8_t* kscales = KT::kScales ? scales + seq_row0 * (kIdxDim / 16) : nullptr;
+  const int lane_co = KT::code_offset(n, g), lane_so = KT::scale_offset(n, g);
+  auto load_slot = [&](KT& kt, int k) {
+    const int64_t r0 = (int64_t)__builtin_amdgcn_readfirstlane(slot_tile(k)) * 16;  // wave-uniform
+    const Rsrc rc = make_rsrc(kcodes + r0 * KT::kRowBytes, (rows_total - r0) * KT::kRowBytes);
+    const Rsrc rs = KT::kScales ? make_rsrc(kscales + r0 * (kIdxDim / 16), (rows_total - r0) * (kIdxDim / 16))
+                                : rc;
+    kt.load(rc, rs, lane_co, lane_so);
+  };
+
+  // The ring's first loads go out before the query setup, which they overlap.
+  KT ring[kRing];
+#pragma unroll
+  for (int d = 0; d < kRing; ++d) {
+    ring[d].set_lane(g);
+    load_slot(ring[d], d);
+  }
+
   // Indexer query fragments (A operand, head n of each 16-head tile) and the weights of
   // the accumulator rows this lane holds (heads 16*ht + 4g + i).
   u32x4 qraw[HT][4];
+  float wv[HT][4];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 16 * ht + 4 * g + i;
+      wv[ht][i] = h < n_heads ? w_idx[(int64_t)b * n_heads + h] : 0.0f;
+    }
   float qmax = 0.0f;
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
@@ -590,38 +642,10 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
   p = max(-100, min(p, 100));
   const float qscale = __builtin_ldexpf(1.0f, p);
   Op qa[HT][4];
-  float wv[HT][4];
 #pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
+  for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
     for (int t = 0; t < 4; ++t) qa[ht][t] = q_operand(qraw[ht][t], qscale, (Op*)nullptr);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 16 * ht + 4 * g + i;
-      wv[ht][i] = h < n_heads ? w_idx[(int64_t)b * n_heads + h] : 0.0f;
-    }
-  }
-
-  // The wave's tile sequence: slot k -> pass k / kSubTiles, tile wave + 8m of that pass
-  // (m = k % kSubTiles).  Every slot loads (rows clamped into range) and computes, so the
-  // loads are straight-line code and the ring keeps kRing tiles in flight across passes
-  // and slices; only valid rows store a score.  A pass is unrolled whole so that the
-  // ring's waits are counted exactly.
-  const int total = n_pass * kSubTiles;
-  auto slot_tile = [&](int k) -> int {
-    const int ps = k / kSubTiles, m = k - ps * kSubTiles;
-    return ps * (kSubTiles * kScanWaves) + wave + kScanWaves * m;
-  };
-  const int rows_last = (int)rows_total - 1;
-  const uint8_t* kcodes = codes + seq_row0 * KT::kRowBytes;
-  const uint8_t* kscales = scales ? scales + seq_row0 * (kIdxDim / 16) : nullptr;
-  auto load_slot = [&](KT& kt, int k) {
-    kt.load(kcodes, kscales, min(slot_tile(k) * 16 + n, rows_last), g);
-  };
-
-  KT ring[kRing];
-#pragma unroll
-  for (int d = 0; d < kRing; ++d) load_slot(ring[d], min(d, total - 1));
 
   for (int ps = 0; ps < n_pass; ++ps) {
 #pragma unroll
@@ -630,7 +654,7 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
       const int k = ps * kSubTiles + m;
       Op kb[4];
       ring[d].decode(kb);
-      load_slot(ring[d], min(k + kRing, total - 1));
+      load_slot(ring[d], k + kRing);  // past the end: reads zeros
       f32x4 acc[HT];
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -638,19 +662,24 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) acc[ht] = KT::mma(qa[ht][t], kb[t], acc[ht]);
+      // ReLU as a signed-integer max: negative floats (and -0) have the sign bit set.
       float sc = 0.0f;
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc += wv[ht][i] * fmaxf(acc[ht][i], 0.0f);
+        for (int i = 0; i < 4; ++i)
+          sc += wv[ht][i] * __int_as_float(max(__float_as_int(acc[ht][i]), 0));
       sc = wave_sum_rows(sc);
+      // Every lane stores (no branch, so a pass stays one basic block): the lanes of
+      // group 0 holding a valid row store its score, the others a dummy slot.
       const int row = slot_tile(k) * 16 + n;  // within the workgroup's rows
-      if (g == 0 && row < rows_total) s_score[row & (kSliceRows - 1)] = f32_order_key(sc);
+      const bool keep = g == 0 && row < rows_total;
+      s_score[keep ? (row & (kSliceRows - 1)) : kSliceRows + lane] = f32_order_key(sc);
     }
-    if ((ps & 1) == 0 && ps + 1 < n_pass) continue;  // the slice has a second pass
+    if ((ps + 1) % kPassesPerSlice != 0 && ps + 1 < n_pass) continue;  // more passes in this slice
 
     // ---- slice complete: emit its candidates, its bound and its scores
-    const int j = ps >> 1;
+    const int j = ps / kPassesPerSlice;
     const int64_t srow0 = row_base + (int64_t)j * kSliceRows;
     const int rows = (int)min((int64_t)kSliceRows, n_c - srow0);
     const int64_t si = (int64_t)b * n_slices + slice0 + j;
