@@ -8,6 +8,7 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "fullsize: a workload-sized GPU parity test")
 
 
 def pytest_sessionstart(session):

@@ -1,0 +1,96 @@
+"""Parity at the workloads' full sizes, in the launch configuration the bench times.
+
+Each test runs the whole batch on the GPU and compares the queries the oracle checks
+(all of them where the oracle finishes in seconds, a sample otherwise): top-k index
+sets bit-exact (those queries' keys made tie-free), attention outputs within 1e-2."""
+import numpy as np
+import pytest
+import torch
+
+import compressed_sparse_kv_csa_amd as ck
+from cases import attention_error, topk_sets_equal
+from fullsize import (make_indexer, make_kv_cache, oracle_topk, query_bits, run_decode,
+                      bf16_out, scale_of, DEV)
+from oracle import decode as OD
+
+pytestmark = [pytest.mark.gpu, pytest.mark.fullsize]
+
+
+def _check_query(name, b, topk_gpu, out_gpu, sel, ref):
+    assert topk_sets_equal(topk_gpu[b:b + 1], sel[None]), f"{name}: top-k set differs for query {b}"
+    err, ok = attention_error(out_gpu[b], ref)
+    print(f"{name} query {b}: max |out - oracle| = {err:.3e}", flush=True)
+    assert ok, (name, b, err)
+
+
+def _csa_full_layer(seed, B, n_c, W, hq, hi, k, kvf, idf, check, name):
+    print(f"case: {name} seed={seed} B={B} Nc={n_c} W={W} Hq={hq} HI={hi} k={k} kv={kvf} idx={idf} "
+          f"checked={check}", flush=True)
+    ix = make_indexer(seed, 0, B, n_c, hi, k, idf, check)
+    kv = make_kv_cache(seed, 0, B, W + n_c, kvf)
+    q, qv = query_bits(seed, 0, B, hq)
+    expect = {}
+    for b in check:
+        sel = oracle_topk(ix, b, k)
+        rows = np.concatenate([np.arange(W), W + sel[sel >= 0]])
+        expect[b] = (sel, OD.attention(qv[b], kv.put_oracle_rows(b, rows), scale_of()))
+    p = ck.CsaParams(B, hq, hi, k, W, ck.MODE_FULL, scale_of(), 0)
+    topk = torch.empty((B, k), dtype=torch.int32, device=DEV)
+    out = bf16_out(run_decode(p, kv, ix, q, topk, n_c))
+    tk = topk.cpu().numpy()
+    for b in check:
+        _check_query(name, b, tk, out, *expect[b])
+    return topk, expect
+
+
+def test_csa_pro_bf16_131k():
+    # 131072-token context: 32768 entries, bf16 keys and rows, 32 query tokens
+    _csa_full_layer(2, 32, 32768, 128, 64, 64, 512, "bf16", "bf16", list(range(32)), "csa_bf16_131k")
+
+
+def test_csa_mixed_1m():
+    # 1M-token context: 262144 entries, mixed FP8/BF16 rows, FP4 indexer keys, 4 tokens
+    _csa_full_layer(4, 4, 262144, 128, 64, 64, 512, "mixed", "fp4", [0, 1, 2, 3], "csa_mixed_1m")
+
+
+def test_csa2_stack_fp4_1m():
+    # CSA2 stack: one Full layer (indexer + top-512) and five Reuse layers that attend with
+    # its indices over their own FP4 caches; 8 tokens, queries 0 and 5 checked.
+    seed, B, n_c, W, hq, hi, k = 5, 8, 262144, 128, 64, 64, 512
+    check = [0, 5]
+    topk, expect = _csa_full_layer(seed, B, n_c, W, hq, hi, k, "fp4", "fp4", check, "csa2 full layer")
+    for layer in range(1, 6):
+        print(f"case: csa2 reuse layer {layer}", flush=True)
+        kv = make_kv_cache(seed, layer, B, W + n_c, "fp4")
+        q, qv = query_bits(seed, layer, B, hq)
+        ref = {}
+        for b in check:
+            sel = expect[b][0]
+            rows = np.concatenate([np.arange(W), W + sel[sel >= 0]])
+            ref[b] = OD.attention(qv[b], kv.put_oracle_rows(b, rows), scale_of())
+        p = ck.CsaParams(B, hq, 0, k, W, ck.MODE_REUSE, scale_of(), 0)
+        out = bf16_out(run_decode(p, kv, None, q, topk, n_c))
+        for b in check:
+            err, ok = attention_error(out[b], ref[b])
+            print(f"reuse layer {layer} query {b}: max |out - oracle| = {err:.3e}", flush=True)
+            assert ok, (layer, b, err)
+        del kv
+
+
+def test_hca_1m():
+    # HCA: 1M tokens at ratio 128 -> 8192 entries + 128 window rows, bf16, 16 tokens
+    seed, B, rows, hq = 3, 16, 8192 + 128, 64
+    print(f"case: hca seed={seed} B={B} rows={rows} Hq={hq}", flush=True)
+    kv = make_kv_cache(seed, 0, B, rows, "bf16")
+    q, qv = query_bits(seed, 0, B, hq)
+    out = torch.empty((B, hq, 512), dtype=torch.int16, device=DEV)
+    ws = torch.empty(max(ck.hca_decode_workspace_bytes(B, hq, rows), 256), dtype=torch.uint8, device=DEV)
+    ck.hca_decode(B, hq, scale_of(), kv.descriptor(), q, out, ws)
+    torch.cuda.synchronize()
+    got = bf16_out(out)
+    for b in range(B):
+        vals = kv.put_oracle_rows(b, np.arange(rows))
+        ref = OD.hca_decode_one(qv[b], vals, scale_of())
+        err, ok = attention_error(got[b], ref)
+        print(f"hca query {b}: max |out - oracle| = {err:.3e}", flush=True)
+        assert ok, (b, err)
