@@ -275,17 +275,18 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
   float m_run = -INFINITY, l_run = 0.0f;
 
   // This thread's work item inside a step: row r, segment seg (one item per thread).
+  // Two steps are fetched ahead (raw0 / raw1 alternate), so both steps of a 64-row chunk
+  // are in flight as soon as the row indices are known.
   int item_r, item_seg;
   SegRaw<KVFMT>::item_rs(threadIdx.x, &item_r, &item_seg);
-  SegRaw<KVFMT> raw;
-  auto fetch = [&](int step) {
+  SegRaw<KVFMT> raw0, raw1;
+  auto fetch = [&](SegRaw<KVFMT>& raw, int step) {
     const int row = s_rows[step * kStepRows + item_r];
     if (row >= 0) raw.load(codes, scales, (int64_t)b * seq_stride + row, item_seg);
     else raw.zero();
   };
 
-  if (n_steps > 0) fetch(0);
-  for (int step = 0; step < n_steps; ++step) {
+  auto run_step = [&](SegRaw<KVFMT>& raw, int step) {
     uint16_t* tile = s_kv0 + (NB == 2 ? (step & 1) * kTileElems : 0);
     if (NB == 1 && step > 0) lds_barrier();  // the previous step's tile is consumed
     // ---- decode the fetched rows into the tile (fp16, row-major)
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
       for (int i = 0; i < 8; ++i) dst[i] = d[i];
     }
     lds_barrier();
-    if (step + 1 < n_steps) fetch(step + 1);
+    if (step + 2 < n_steps) fetch(raw, step + 2);
 
     // ---- logits S^T: lane (g, n) gets rows 16*rt + 4g + i of head n
     f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -355,6 +356,13 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
 #pragma unroll
     for (int i = 0; i < kDimsPerWave / 16; ++i)
       o[i] = mfma16x16x32_f16(v_fragment(tile, g, n, (kDimsPerWave / 16) * wave + i), pb, o[i]);
+  };
+
+  if (n_steps > 0) fetch(raw0, 0);
+  if (n_steps > 1) fetch(raw1, 1);
+  for (int step = 0; step < n_steps; step += 2) {
+    run_step(raw0, step);
+    if (step + 1 < n_steps) run_step(raw1, step + 1);
   }
 
   // ---- partial records: the 16 x 512 output block is staged through LDS so that each
