@@ -1,17 +1,20 @@
 #!/usr/bin/env python3
 """CSA decode benchmark on one MI355X: query-tokens/s and achieved HBM GB/s.
 
-A step is one pass of the decode hot path over one batch: the indexer scores every
-compressed entry of each query's sequence, keeps the top-512, and attends over those
-entries plus the 128-row sliding window (csa_decode, FULL mode).  The default workload
-is the 1M-token context with mixed FP8/BF16 shared-KV rows and FP4 indexer keys,
-B = 4 query tokens.  Inputs are synthetic and seed-generated, and resident in HBM
-before timing starts; R replicas of every cache (>= 1 GiB in all) rotate across steps
-so that the 256 MB Infinity Cache cannot serve a step from the previous one.
+A step is one pass of the decode hot path over one batch.  For the CSA workloads the
+indexer scores every compressed entry of each query's sequence, keeps the top-512, and
+attends over those entries plus the 128-row sliding window (csa_decode, FULL mode);
+the CSA2 stack adds five Reuse layers that attend with the same indices over their own
+caches.  The HCA workload attends densely over every row (hca_decode).  The default
+workload is the 1M-token context with mixed FP8/BF16 shared-KV rows and FP4 indexer
+keys, B = 4 query tokens.  Inputs are synthetic and seed-generated, and resident in HBM
+before timing starts; R replicas of every cache (>= 1 GiB in all) rotate across steps so
+that the 256 MB Infinity Cache cannot serve a step from the previous one.
 
-Output: one JSON line (rank 0).  `roofline` reports the dominant stage (the indexer
-scan + top-k, csa_select_topk) timed with HIP events on the stream it runs on;
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+Output: one JSON line (rank 0).  `roofline` reports the dominant stage (the indexer scan
++ top-k, csa_select_topk; for HCA the whole hca_decode) timed with HIP events on the
+stream it runs on; `cpu_baseline` times the CPU oracle on a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -32,13 +35,16 @@ HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 1 << 30
 
 WORKLOADS = {
-    # name: B, N_c, window, H_q, H_I, top_k, kv format, indexer format, seed
-    "csa_mixed_1m": dict(B=4, n_c=262144, window=128, hq=64, hi=64, top_k=512, kv="mixed",
-                         idx="fp4", seed=4, context=1 << 20),
-    "csa_bf16_131k": dict(B=32, n_c=32768, window=128, hq=64, hi=64, top_k=512, kv="bf16",
-                          idx="bf16", seed=2, context=131072),
-    "csa_fp4_1m": dict(B=8, n_c=262144, window=128, hq=64, hi=64, top_k=512, kv="fp4",
-                       idx="fp4", seed=5, context=1 << 20),
+    # kind, B, N_c, window, H_q, H_I, top_k, kv format, indexer format, seed, layers
+    # (csa: layer 0 runs the indexer, layers 1.. reuse its top-k over their own caches)
+    "csa_mixed_1m": dict(kind="csa", B=4, n_c=262144, window=128, hq=64, hi=64, top_k=512,
+                         kv="mixed", idx="fp4", seed=4, context=1 << 20, layers=1),
+    "csa_bf16_131k": dict(kind="csa", B=32, n_c=32768, window=128, hq=64, hi=64, top_k=512,
+                          kv="bf16", idx="bf16", seed=2, context=131072, layers=1),
+    "csa2_stack_fp4_1m": dict(kind="csa", B=8, n_c=262144, window=128, hq=64, hi=64, top_k=512,
+                              kv="fp4", idx="fp4", seed=5, context=1 << 20, layers=6),
+    "hca_bf16_1m": dict(kind="hca", B=16, n_c=8192, window=128, hq=64, hi=0, top_k=0, kv="bf16",
+                        idx=None, seed=3, context=1 << 20, layers=1),
 }
 # HBM traffic of the indexer stage, from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs scaled
 # by what the same counters read for a copy kernel of known size.  Valid only while the
@@ -55,10 +61,14 @@ IDX_ROW_BYTES = {"bf16": 256, "fp4": 64 + 8}
 def algorithmic_bytes(w: dict) -> dict:
     """Bytes the method itself moves per step (no workspace, re-reads or padding)."""
     B, n_c, k = w["B"], w["n_c"], w["top_k"]
+    if w["kind"] == "hca":
+        attn = B * ((n_c + w["window"]) * KV_ROW_BYTES[w["kv"]] + 2 * w["hq"] * 512 * 2)
+        return {"indexer": 0, "attention": attn, "step": attn}
     rows = min(k, n_c) + w["window"]
     idx = B * (n_c * IDX_ROW_BYTES[w["idx"]] + w["hi"] * 128 * 2 + w["hi"] * 4 + k * 4)
     attn = B * (rows * KV_ROW_BYTES[w["kv"]] + 2 * w["hq"] * 512 * 2)
-    return {"indexer": idx, "attention": attn, "step": idx + attn}
+    reuse = (w["layers"] - 1) * (attn + B * k * 4)
+    return {"indexer": idx, "attention": attn, "step": idx + attn + reuse}
 
 
 def build_inputs(w: dict, replicas: int):
@@ -70,44 +80,53 @@ def build_inputs(w: dict, replicas: int):
     T = seedgen.TID
     B, n_c, W = w["B"], w["n_c"], w["window"]
     rows = W + n_c
-    # One set of caches, generated and quantised on the GPU, then copied per replica.
-    keys16 = seedgen.bf16_normal(w["seed"], seedgen.tid(T.IDX_KEYS), (B, n_c, 128), dev)
-    if w["idx"] == "fp4":
-        k_codes = torch.empty((B, n_c, 64), dtype=torch.uint8, device=dev)
-        k_scales = torch.empty((B, n_c, 8), dtype=torch.uint8, device=dev)
-        ck.kv_quantize_fp4(keys16, B * n_c, 128, k_codes, k_scales)
-    else:
-        k_codes, k_scales = keys16, None
-    kv16 = seedgen.kv_rows_bf16(w["seed"], seedgen.tid(T.KV), (B, rows, 512), dev)
-    if w["kv"] == "mixed":
-        kv_codes, kv_scales = torch.empty((B, rows, 576), dtype=torch.uint8, device=dev), None
-        ck.kv_quantize_fp8(kv16, B * rows, 512, 448, kv_codes)
-    elif w["kv"] == "fp4":
-        kv_codes = torch.empty((B, rows, 256), dtype=torch.uint8, device=dev)
-        kv_scales = torch.empty((B, rows, 32), dtype=torch.uint8, device=dev)
-        ck.kv_quantize_fp4(kv16, B * rows, 512, kv_codes, kv_scales)
-    else:
-        kv_codes, kv_scales = kv16, None
-    torch.cuda.synchronize()
-    del kv16
-    if w["idx"] == "fp4":
-        del keys16
     kv_fmt = {"bf16": ck.KV_BF16, "mixed": ck.KV_FP8_MIXED, "fp4": ck.KV_FP4}[w["kv"]]
-    idx_fmt = {"bf16": ck.IDX_BF16, "fp4": ck.IDX_FP4}[w["idx"]]
+
+    def kv_cache(layer):
+        kv16 = seedgen.kv_rows_bf16(w["seed"], seedgen.tid(T.KV, layer), (B, rows, 512), dev)
+        if w["kv"] == "mixed":
+            codes = torch.empty((B, rows, 576), dtype=torch.uint8, device=dev)
+            ck.kv_quantize_fp8(kv16, B * rows, 512, 448, codes)
+            return codes, None
+        if w["kv"] == "fp4":
+            codes = torch.empty((B, rows, 256), dtype=torch.uint8, device=dev)
+            scales = torch.empty((B, rows, 32), dtype=torch.uint8, device=dev)
+            ck.kv_quantize_fp4(kv16, B * rows, 512, codes, scales)
+            return codes, scales
+        return kv16, None
+
+    # One set of caches, generated and quantised on the GPU, then copied per replica.
+    kvs = [kv_cache(layer) for layer in range(w["layers"])]
+    k_codes = k_scales = None
+    if w["kind"] == "csa":
+        keys16 = seedgen.bf16_normal(w["seed"], seedgen.tid(T.IDX_KEYS), (B, n_c, 128), dev)
+        if w["idx"] == "fp4":
+            k_codes = torch.empty((B, n_c, 64), dtype=torch.uint8, device=dev)
+            k_scales = torch.empty((B, n_c, 8), dtype=torch.uint8, device=dev)
+            ck.kv_quantize_fp4(keys16, B * n_c, 128, k_codes, k_scales)
+            del keys16
+        else:
+            k_codes = keys16
+    torch.cuda.synchronize()
     reps = []
     for r in range(replicas):
         def cp(t):
             return None if t is None else (t if r == 0 else t.clone())
-        rep = dict(kc=cp(k_codes), ks=cp(k_scales), vc=cp(kv_codes), vs=cp(kv_scales))
-        # Distinct queries per replica (their own top-k rows).
-        s = w["seed"] * 1000 + r
-        rep["q"] = seedgen.bf16_normal(s, seedgen.tid(T.Q), (B, w["hq"], 512), dev)
-        rep["qi"] = seedgen.bf16_normal(s, seedgen.tid(T.Q_IDX), (B, w["hi"], 128), dev)
-        rep["w"] = seedgen.uniform01(s, seedgen.tid(T.W_IDX), (B, w["hi"]), dev)
-        rep["kv"] = ck.cache(kv_fmt, rep["vc"], rows, rows, rep["vs"])
-        rep["idx"] = ck.cache(idx_fmt, rep["kc"], n_c, n_c, rep["ks"])
-        rep["topk"] = torch.empty((B, w["top_k"]), dtype=torch.int32, device=dev)
-        rep["out"] = torch.empty((B, w["hq"], 512), dtype=torch.bfloat16, device=dev)
+        rep = {"kv": [], "q": [], "out": []}
+        s = w["seed"] * 1000 + r  # distinct queries per replica (their own top-k rows)
+        for layer, (codes, scales) in enumerate(kvs):
+            c, sc = cp(codes), cp(scales)
+            rep["kv"].append(ck.cache(kv_fmt, c, rows, rows, sc))
+            rep.setdefault("keep", []).append((c, sc))
+            rep["q"].append(seedgen.bf16_normal(s, seedgen.tid(T.Q, layer), (B, w["hq"], 512), dev))
+            rep["out"].append(torch.empty((B, w["hq"], 512), dtype=torch.bfloat16, device=dev))
+        if w["kind"] == "csa":
+            idx_fmt = {"bf16": ck.IDX_BF16, "fp4": ck.IDX_FP4}[w["idx"]]
+            rep["kc"], rep["ks"] = cp(k_codes), cp(k_scales)
+            rep["idx"] = ck.cache(idx_fmt, rep["kc"], n_c, n_c, rep["ks"])
+            rep["qi"] = seedgen.bf16_normal(s, seedgen.tid(T.Q_IDX), (B, w["hi"], 128), dev)
+            rep["w"] = seedgen.uniform01(s, seedgen.tid(T.W_IDX), (B, w["hi"]), dev)
+            rep["topk"] = torch.empty((B, w["top_k"]), dtype=torch.int32, device=dev)
         reps.append(rep)
     torch.cuda.synchronize()
     return reps
@@ -120,21 +139,38 @@ def run_gpu(w: dict, steps: int, warmup: int, replicas: int | None):
     nbytes = algorithmic_bytes(w)
     R = replicas or max(2, math.ceil(MALL_BYTES / nbytes["step"]))
     reps = build_inputs(w, R)
-    p = ck.CsaParams(w["B"], w["hq"], w["hi"], w["top_k"], w["window"], ck.MODE_FULL,
-                     1.0 / math.sqrt(512), 0)
-    ws_bytes = ck.csa_decode_workspace_bytes(p, w["n_c"])
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    B, scale = w["B"], 1.0 / math.sqrt(512)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
+    if w["kind"] == "hca":
+        rows = w["n_c"] + w["window"]
+        ws_bytes = ck.hca_decode_workspace_bytes(B, w["hq"], rows)
+        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
 
-    def step(i):
-        r = reps[i % R]
-        ck.csa_decode(p, r["kv"], r["idx"], r["q"], r["qi"], r["w"], r["topk"], r["out"], ws,
-                      ws_bytes, stream=sh)
+        def step(i):
+            r = reps[i % R]
+            ck.hca_decode(B, w["hq"], scale, r["kv"][0], r["q"][0], r["out"][0], ws, ws_bytes, stream=sh)
 
-    def select(i):
-        r = reps[i % R]
-        ck.csa_select_topk(p, r["idx"], r["qi"], r["w"], r["topk"], ws, ws_bytes, stream=sh)
+        stage, stage_bytes, stage_name = step, nbytes["attention"], "hca_decode (attention + combine)"
+    else:
+        p = ck.CsaParams(B, w["hq"], w["hi"], w["top_k"], w["window"], ck.MODE_FULL, scale, 0)
+        p_reuse = ck.CsaParams(B, w["hq"], 0, w["top_k"], w["window"], ck.MODE_REUSE, scale, 0)
+        ws_bytes = ck.csa_decode_workspace_bytes(p, w["n_c"])
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+
+        def step(i):
+            r = reps[i % R]
+            ck.csa_decode(p, r["kv"][0], r["idx"], r["q"][0], r["qi"], r["w"], r["topk"], r["out"][0],
+                          ws, ws_bytes, stream=sh)
+            for layer in range(1, w["layers"]):
+                ck.csa_decode(p_reuse, r["kv"][layer], None, r["q"][layer], None, None, r["topk"],
+                              r["out"][layer], ws, ws_bytes, stream=sh)
+
+        def stage(i):
+            r = reps[i % R]
+            ck.csa_select_topk(p, r["idx"], r["qi"], r["w"], r["topk"], ws, ws_bytes, stream=sh)
+
+        stage_bytes, stage_name = nbytes["indexer"], "indexer stage (csa_select_topk)"
 
     for i in range(warmup):
         step(i)
@@ -150,19 +186,20 @@ def run_gpu(w: dict, steps: int, warmup: int, replicas: int | None):
     wall = time.perf_counter() - wall0
     ms = t0.elapsed_time(t1) / steps
 
-    # Dominant stage: indexer scan + top-k, one event pair per launch on its stream.
+    # Dominant stage, one event pair per launch on its stream.
     for i in range(warmup):
-        select(i)
+        stage(i)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     for i in range(steps):
         ev[i][0].record(stream)
-        select(i)
+        stage(i)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    sel_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
-    return dict(ms=ms, wall=wall, sel_ms=sel_ms, replicas=R, bytes=nbytes)
+    stage_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    return dict(ms=ms, wall=wall, stage_ms=stage_ms, stage_bytes=stage_bytes, stage_name=stage_name,
+                replicas=R, bytes=nbytes)
 
 
 def kernel_sources_sha256() -> str:
@@ -214,69 +251,78 @@ def run_cpu_baseline(w: dict, queries: int):
     except Exception:
         cores = os.cpu_count() or 1
     T = seedgen.TID
-    n_c, W, k = w["n_c"], w["window"], w["top_k"]
+    n_c, W, k, B = w["n_c"], w["window"], w["top_k"], w["B"]
     dev = "cuda" if torch.cuda.is_available() else "cpu"
     s = w["seed"] * 1000           # replica 0's queries
-    q = seedgen.bf16_normal(s, seedgen.tid(T.Q), (w["B"], w["hq"], 512), dev)[:queries]
-    qi = seedgen.bf16_normal(s, seedgen.tid(T.Q_IDX), (w["B"], w["hi"], 128), dev)[:queries]
-    wv = seedgen.uniform01(s, seedgen.tid(T.W_IDX), (w["B"], w["hi"]), dev)[:queries]
-    q = q.float().cpu().double().numpy()
-    qi = qi.float().cpu().double().numpy()
-    wv = wv.cpu().double().numpy()
+    scale = 1.0 / math.sqrt(512)
 
     def bits(t):
         return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
+    def encode(row_bits):
+        if w["kv"] == "mixed":
+            return OF.mixed_quantize(row_bits)
+        if w["kv"] == "fp4":
+            return OF.fp4_quantize(OF.bf16_bits_to_f64(row_bits))
+        return row_bits
+
+    def decode(enc):
+        if w["kv"] == "mixed":
+            return OF.mixed_dequantize(enc)
+        if w["kv"] == "fp4":
+            return OF.fp4_dequantize(*enc)
+        return OF.bf16_bits_to_f64(enc)
+
+    qs = [seedgen.bf16_normal(s, seedgen.tid(T.Q, layer), (B, w["hq"], 512), dev)[:queries]
+          .float().cpu().double().numpy() for layer in range(w["layers"])]
+
     # Untimed preparation by the oracle's own encoders: every indexer key, and the KV rows
-    # the decode reads (window + the oracle's own top-k); unread rows stay zero.
-    keys = bits(seedgen.bf16_normal(w["seed"], seedgen.tid(T.IDX_KEYS), (w["B"], n_c, 128), dev)[:queries])
-    caches = []
-    kv_all = seedgen.kv_rows_bf16(w["seed"], seedgen.tid(T.KV), (w["B"], W + n_c, 512), dev)
+    # the decode reads (window + the oracle's own top-k, in every layer).
+    if w["kind"] == "hca":
+        kv_all = seedgen.kv_rows_bf16(w["seed"], seedgen.tid(T.KV), (B, W + n_c, 512), dev)
+        encs = [encode(bits(kv_all[b])) for b in range(queries)]
+        del kv_all
+        t0 = time.perf_counter()
+        for b in range(queries):
+            OD.hca_decode_one(qs[0][b], decode(encs[b]), scale)
+        dt = time.perf_counter() - t0
+        sample = (f"{queries} of the {B} query tokens of one step (same seeds and shapes): dense "
+                  f"attention over {W + n_c} {w['kv']} rows each; numpy fp64, {dt:.1f} s")
+        return {"value": round(queries / dt, 4), "unit": "query-tokens/s", "cores": int(cores),
+                "kind": "oracle", "sample": sample}
+
+    qi = seedgen.bf16_normal(s, seedgen.tid(T.Q_IDX), (B, w["hi"], 128), dev)[:queries]
+    wv = seedgen.uniform01(s, seedgen.tid(T.W_IDX), (B, w["hi"]), dev)[:queries]
+    qi = qi.float().cpu().double().numpy()
+    wv = wv.cpu().double().numpy()
+    keys = bits(seedgen.bf16_normal(w["seed"], seedgen.tid(T.IDX_KEYS), (B, n_c, 128), dev)[:queries])
+    key_enc, sels = [], []
     for b in range(queries):
         vals = OF.bf16_bits_to_f64(keys[b])
-        if w["idx"] == "fp4":
-            kc = OF.fp4_quantize(vals)
-            kd = OF.fp4_dequantize(*kc)
-        else:
-            kc, kd = keys[b], vals
-        sel = OD.topk_indices(OD.indexer_scores(qi[b], wv[b], kd), k)
-        need = np.concatenate([np.arange(W), W + sel[sel >= 0]])
-        row_bits = bits(kv_all[b, torch.from_numpy(need).to(kv_all.device)])
-        if w["kv"] == "mixed":
-            enc = OF.mixed_quantize(row_bits)
-            full = np.zeros((W + n_c, 576), dtype=np.uint8)
-        elif w["kv"] == "fp4":
-            c, sc = OF.fp4_quantize(OF.bf16_bits_to_f64(row_bits))
-            enc = (c, sc)
-            full = (np.zeros((W + n_c, 256), np.uint8), np.zeros((W + n_c, 32), np.uint8))
-        else:
-            enc, full = row_bits, np.zeros((W + n_c, 512), dtype=np.uint16)
-        if isinstance(full, tuple):
-            full[0][need], full[1][need] = enc
-        else:
-            full[need] = enc
-        caches.append((kc, full))
-    del kv_all
-
-    def decode_rows(full, idx):
-        if w["kv"] == "mixed":
-            return OF.mixed_dequantize(full[idx])
-        if w["kv"] == "fp4":
-            return OF.fp4_dequantize(full[0][idx], full[1][idx])
-        return OF.bf16_bits_to_f64(full[idx])
+        kc = OF.fp4_quantize(vals) if w["idx"] == "fp4" else keys[b]
+        kd = OF.fp4_dequantize(*kc) if w["idx"] == "fp4" else vals
+        key_enc.append(kc)
+        sels.append(OD.topk_indices(OD.indexer_scores(qi[b], wv[b], kd), k))
+    rows_enc = [[None] * queries for _ in range(w["layers"])]
+    for layer in range(w["layers"]):
+        kv_all = seedgen.kv_rows_bf16(w["seed"], seedgen.tid(T.KV, layer), (B, W + n_c, 512), dev)
+        for b in range(queries):
+            need = np.concatenate([np.arange(W), W + sels[b][sels[b] >= 0]])
+            rows_enc[layer][b] = encode(bits(kv_all[b, torch.from_numpy(need).to(kv_all.device)]))
+        del kv_all
 
     t0 = time.perf_counter()
     for b in range(queries):
-        kc, full = caches[b]
-        kd = OF.fp4_dequantize(*kc) if w["idx"] == "fp4" else OF.bf16_bits_to_f64(kc)
-        sel = OD.topk_indices(OD.indexer_scores(qi[b], wv[b], kd), k)
-        rows = decode_rows(full, np.concatenate([np.arange(W), W + sel[sel >= 0]]))
-        OD.attention(q[b], rows, 1.0 / math.sqrt(512))
+        kd = OF.fp4_dequantize(*key_enc[b]) if w["idx"] == "fp4" else OF.bf16_bits_to_f64(key_enc[b])
+        OD.topk_indices(OD.indexer_scores(qi[b], wv[b], kd), k)
+        for layer in range(w["layers"]):
+            OD.attention(qs[layer][b], decode(rows_enc[layer][b]), scale)
     dt = time.perf_counter() - t0
+    layers = f" in each of {w['layers']} layers" if w["layers"] > 1 else ""
     return {"value": round(queries / dt, 4), "unit": "query-tokens/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": f"{queries} of the {w['B']} query tokens of one step (same seeds and shapes): "
-                      f"{n_c} {w['idx']} indexer keys each, then {W}+{k} {w['kv']} rows; "
+            "sample": f"{queries} of the {B} query tokens of one step (same seeds and shapes): "
+                      f"{n_c} {w['idx']} indexer keys each, then {W}+{k} {w['kv']} rows{layers}; "
                       f"numpy fp64, {dt:.1f} s"}
 
 
@@ -309,7 +355,7 @@ def main():
     B = w["B"]
     tok_s = B / (g["ms"] * 1e-3)
     step_gbps = g["bytes"]["step"] / (g["ms"] * 1e-3) / 1e9
-    sel_gbps = g["bytes"]["indexer"] / (g["sel_ms"] * 1e-3) / 1e9
+    stage_gbps = g["stage_bytes"] / (g["stage_ms"] * 1e-3) / 1e9
     cpu = None
     if not args.no_cpu_baseline:
         cpu = run_cpu_baseline(w, args.cpu_queries or B)
@@ -329,15 +375,15 @@ def main():
         "config": {"workload": args.workload, "batch": B, "context_tokens": w["context"],
                    "n_compressed": w["n_c"], "top_k": w["top_k"], "window": w["window"],
                    "q_heads": w["hq"], "idx_heads": w["hi"], "kv_format": w["kv"],
-                   "idx_format": w["idx"], "replicas": g["replicas"]},
+                   "idx_format": w["idx"], "layers": w["layers"], "replicas": g["replicas"]},
         "hbm_gbps": round(step_gbps, 1),
         "algorithmic_bytes_per_step": g["bytes"]["step"],
-        "roofline": {"bound": "hbm", "achieved": round(sel_gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(sel_gbps / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(stage_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(stage_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(args.workload),
-                     "kernel": "indexer stage (csa_select_topk)",
-                     "avg_launch_us": round(g["sel_ms"] * 1e3, 2),
-                     "algorithmic_bytes_per_launch": g["bytes"]["indexer"]},
+                     "kernel": g["stage_name"],
+                     "avg_launch_us": round(g["stage_ms"] * 1e3, 2),
+                     "algorithmic_bytes_per_launch": g["stage_bytes"]},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -36,6 +36,9 @@ constexpr int kStepRows = 32;
 constexpr int kPitch = kDim + 16;     // fp16 elements per LDS row (32-byte pad)
 constexpr int kOutPitch = kDim + 4;   // floats per LDS row when staging the output
 constexpr float kLog2e = 1.4426950408889634f;
+// Buffer offset given to an absent row: at or past the end of every sequence the
+// launcher accepts (sequence bytes are checked against it on the host).
+constexpr uint32_t kAbsentOffset = kAttnMaxSeqBytes;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef v4i16 __attribute__((address_space(3))) lds_v4i16;
@@ -49,127 +52,135 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
   return pack_f16(__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u));
 }
 
-// Raw bytes of one (row, 64-dim segment) work item, and their decode to 32 dwords of
-// fp16 pairs (dims seg*64 .. seg*64+63).  Raw data is kept in scalar arrays so that it
-// stays in registers.
-__device__ __forceinline__ void load16(uint32_t* w, const uint8_t* p) {
-  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+// One step's gathered rows: every thread loads a fixed set of 16-byte pieces and
+// later stores them, decoded to fp16, into the row-major tile.  Pieces are assigned so
+// that the 64 lanes of one load instruction read consecutive bytes of the cached rows
+// (whole cache lines, not one 16-byte piece of 64 different lines), and so that the
+// assignment depends only on the thread, not on the step.  Raw data is kept in scalar
+// arrays so that it stays in registers.  `rows` points at the step's 32 sequence rows
+// (-1: absent); an absent row is read at an offset past the sequence, which returns
+// zeros without touching memory.
+__device__ __forceinline__ void load16(uint32_t* w, Rsrc rc, uint32_t off) {
+  const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0));
   w[0] = v[0];
   w[1] = v[1];
   w[2] = v[2];
   w[3] = v[3];
 }
+__device__ __forceinline__ void store16(uint16_t* dst, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  *reinterpret_cast<u32x4*>(dst) = u32x4{a, b, c, d};
+}
+__device__ __forceinline__ uint32_t row_offset(int row, uint32_t row_bytes, uint32_t in_row) {
+  return row >= 0 ? (uint32_t)row * row_bytes + in_row : kAbsentOffset;
+}
 
 template <int KVFMT>
-struct SegRaw;
+struct StepRaw;
 
+// bf16 rows (1 KB): load k of wave w reads step row 8w + k whole, lane l its bytes
+// 16l .. 16l + 15 (dims 8l .. 8l + 7).  The row is wave-uniform.
 template <>
-struct SegRaw<0> {  // bf16: 128 bytes per item; rows split into 8 equal segments
-  static constexpr int kRowItems = 8;
+struct StepRaw<0> {
+  static constexpr uint32_t kRowBytes = kDim * 2;
+  static constexpr uint32_t kScaleRowBytes = 0;
   uint32_t w[32];
-  static __device__ __forceinline__ void item_rs(int item, int* r, int* seg) {
-    *r = item >> 3;
-    *seg = item & 7;
+  __device__ __forceinline__ void load(Rsrc rc, Rsrc, const int* rows, int tid) {
+    const int wave = tid / kWave, lane = tid & (kWave - 1);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int row = __builtin_amdgcn_readfirstlane(rows[8 * wave + k]);
+      load16(w + 4 * k, rc, row_offset(row, kRowBytes, 16 * lane));
+    }
   }
-  __device__ __forceinline__ void load(const uint8_t* codes, const uint8_t*, int64_t row, int seg) {
-    const uint8_t* p = codes + row * (kDim * 2) + seg * 128;
+  __device__ __forceinline__ void store(uint16_t* tile, int tid) const {
+    const int wave = tid / kWave, lane = tid & (kWave - 1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) load16(w + 4 * i, p + 16 * i);
-  }
-  __device__ __forceinline__ void zero() {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) w[i] = 0u;
-  }
-  __device__ __forceinline__ void decode(int, u32x4* out) const {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) out[i][j] = bf16x2_to_f16x2(w[4 * i + j]);
+    for (int k = 0; k < 8; ++k)
+      store16(tile + (8 * wave + k) * kPitch + 8 * lane, bf16x2_to_f16x2(w[4 * k]),
+              bf16x2_to_f16x2(w[4 * k + 1]), bf16x2_to_f16x2(w[4 * k + 2]),
+              bf16x2_to_f16x2(w[4 * k + 3]));
   }
 };
 
-// Mixed rows: items 0 .. 7*32-1 are the E4M3 segments (row = item / 7, 64 bytes each),
-// items 7*32 .. 8*32-1 the bf16 RoPE segments (128 bytes), so that only the one wave
-// holding both kinds diverges.
+// Mixed rows (576 B: 448 E4M3 codes, then 64 bf16).  The step's 32 x 28 E4M3 pieces
+// are numbered row-major, piece p = 256k + tid (k < 4; the last round covers 128 of
+// them), each 16 dims; the 32 x 8 bf16 pieces go one per thread (8 dims each).  The
+// threads of the last E4M3 round that have no piece read nothing and write their 32
+// bytes into the tile's row padding (dims 512 .. 527, which no product reads).
 template <>
-struct SegRaw<1> {
-  static constexpr int kRowItems = 8;
-  uint32_t w[32];
-  static __device__ __forceinline__ void item_rs(int item, int* r, int* seg) {
-    if (item < 7 * kStepRows) {
-      *r = item / 7;
-      *seg = item - 7 * (item / 7);
-    } else {
-      *r = item - 7 * kStepRows;
-      *seg = 7;
+struct StepRaw<1> {
+  static constexpr uint32_t kRowBytes = kNope + 2 * (kDim - kNope);
+  static constexpr uint32_t kScaleRowBytes = 0;
+  static constexpr int kFp8Pieces = kStepRows * (kNope / 16);  // 896
+  uint32_t e[16];  // four E4M3 pieces
+  uint32_t r[4];   // one bf16 piece
+  __device__ __forceinline__ void load(Rsrc rc, Rsrc, const int* rows, int tid) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int p = 256 * k + tid;
+      const int rl = p / (kNope / 16), c = p - rl * (kNope / 16);
+      const int row = p < kFp8Pieces ? rows[rl < kStepRows ? rl : kStepRows - 1] : -1;
+      load16(e + 4 * k, rc, row_offset(row, kRowBytes, 16 * c));
     }
+    load16(r, rc, row_offset(rows[tid >> 3], kRowBytes, kNope + 16 * (tid & 7)));
   }
-  // Every item loads 128 contiguous bytes of its row (an E4M3 item also reads the next
-  // 64 bytes, which stay unused), so the load shape does not depend on the segment.
-  __device__ __forceinline__ void load(const uint8_t* codes, const uint8_t*, int64_t row, int seg) {
-    const uint8_t* p = codes + row * (kNope + 2 * (kDim - kNope)) + (seg < 7 ? seg * 64 : kNope);
+  __device__ __forceinline__ void store(uint16_t* tile, int tid) const {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) load16(w + 4 * i, p + 16 * i);
-  }
-  __device__ __forceinline__ void zero() {
+    for (int k = 0; k < 4; ++k) {
+      const int p = 256 * k + tid;
+      const int rl = p / (kNope / 16), c = p - rl * (kNope / 16);
+      uint16_t* dst = p < kFp8Pieces ? tile + rl * kPitch + 16 * c : tile + (p & 31) * kPitch + kDim;
+      uint32_t h[8];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) w[i] = 0u;
-  }
-  __device__ __forceinline__ void decode(int seg, u32x4* out) const {
-    if (seg < 7) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {  // 4 E4M3 codes -> 4 fp16 (exact)
-        out[i >> 1][2 * (i & 1)] = __builtin_bit_cast(
-            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, false));
-        out[i >> 1][2 * (i & 1) + 1] = __builtin_bit_cast(
-            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, true));
+      for (int i = 0; i < 4; ++i) {  // 4 E4M3 codes -> 4 fp16 (exact)
+        h[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e[4 * k + i], 1.0f, false));
+        h[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e[4 * k + i], 1.0f, true));
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) out[i][j] = bf16x2_to_f16x2(w[4 * i + j]);
+      store16(dst, h[0], h[1], h[2], h[3]);
+      store16(dst + 8, h[4], h[5], h[6], h[7]);
     }
+    store16(tile + (tid >> 3) * kPitch + kNope + 8 * (tid & 7), bf16x2_to_f16x2(r[0]),
+            bf16x2_to_f16x2(r[1]), bf16x2_to_f16x2(r[2]), bf16x2_to_f16x2(r[3]));
   }
 };
 
+// FP4 rows (256 code bytes, 32 E4M3 scale bytes, one per 16 dims): piece p = 256k + tid
+// (k < 2) is row p / 16, code bytes 16c .. 16c + 15 with c = p % 16 (dims 32c .. 32c + 31),
+// and the two scale bytes of those dims.
 template <>
-struct SegRaw<2> {  // FP4: 32 code bytes + 4 E4M3 scale bytes (one per 16 dims)
-  static constexpr int kRowItems = 8;
+struct StepRaw<2> {
+  static constexpr uint32_t kRowBytes = kDim / 2;
+  static constexpr uint32_t kScaleRowBytes = kDim / 16;
   uint32_t c[8];
-  uint32_t s;
-  static __device__ __forceinline__ void item_rs(int item, int* r, int* seg) {
-    *r = item >> 3;
-    *seg = item & 7;
-  }
-  __device__ __forceinline__ void load(const uint8_t* codes, const uint8_t* scales, int64_t row,
-                                       int seg) {
-    const uint8_t* p = codes + row * (kDim / 2) + seg * 32;
-    load16(c, p);
-    load16(c + 4, p + 16);
-    s = *reinterpret_cast<const uint32_t*>(scales + row * (kDim / 16) + seg * 4);
-  }
-  __device__ __forceinline__ void zero() {
+  uint32_t s[2];
+  __device__ __forceinline__ void load(Rsrc rc, Rsrc rs, const int* rows, int tid) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = 0u;
-    s = 0u;
+    for (int k = 0; k < 2; ++k) {
+      const int p = 256 * k + tid;
+      const int row = rows[p >> 4];
+      load16(c + 4 * k, rc, row_offset(row, kRowBytes, 16 * (p & 15)));
+      s[k] = __builtin_amdgcn_raw_buffer_load_b16(rs, row_offset(row, kScaleRowBytes, 2 * (p & 15)), 0, 0);
+    }
   }
-  __device__ __forceinline__ void decode(int, u32x4* out) const {
-    // The four scales as fp16 (exact), each broadcast to both halves of a pair.
-    const uint32_t s01 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 1.0f, false));
-    const uint32_t s23 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 1.0f, true));
-    const uint32_t sc[4] = {__builtin_amdgcn_perm(s01, s01, 0x01000100u),
-                            __builtin_amdgcn_perm(s01, s01, 0x03020302u),
-                            __builtin_amdgcn_perm(s23, s23, 0x01000100u),
-                            __builtin_amdgcn_perm(s23, s23, 0x03020302u)};
+  __device__ __forceinline__ void store(uint16_t* tile, int tid) const {
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {  // code dword w holds dims 8w .. 8w+7 (block w / 2)
-      const uint32_t cw = c[w];
-      const f16x2 scv = __builtin_bit_cast(f16x2, sc[w >> 1]);
-      out[w][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 0) * scv);
-      out[w][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1) * scv);
-      out[w][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2) * scv);
-      out[w][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 3) * scv);
+    for (int k = 0; k < 2; ++k) {
+      const int p = 256 * k + tid;
+      uint16_t* dst = tile + (p >> 4) * kPitch + 32 * (p & 15);
+      // Both scales as an fp16 pair (exact), each broadcast to both halves of a pair.
+      const uint32_t sp = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s[k], 1.0f, false));
+      const f16x2 s0 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(sp, sp, 0x01000100u));
+      const f16x2 s1 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(sp, sp, 0x03020302u));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {  // code dword j holds dims 8j .. 8j + 7 (scale j / 2)
+        const uint32_t cw = c[4 * k + j];
+        const f16x2 sc = j < 2 ? s0 : s1;
+        store16(dst + 8 * j,
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 0) * sc),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1) * sc),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2) * sc),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 3) * sc));
+      }
     }
   }
 };
@@ -219,7 +230,8 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
   constexpr int kOutBytes = 16 * kOutPitch * 4;
   constexpr int kSmem = kTileBytes + kQBytes > kOutBytes ? kTileBytes + kQBytes : kOutBytes;
   __shared__ __attribute__((aligned(16))) uint8_t s_mem[kSmem];
-  __shared__ int s_rows[kMaxChunkRows];
+  __shared__ __attribute__((aligned(16))) int s_rows[kMaxChunkRows + 2 * kStepRows];
+  __shared__ __attribute__((aligned(16))) float s_logit[2][kStepRows][16];  // per K half
   uint16_t* const s_kv0 = reinterpret_cast<uint16_t*>(s_mem);
   uint16_t* const s_q = reinterpret_cast<uint16_t*>(s_mem + kTileBytes);
   float* const s_out = reinterpret_cast<float*>(s_mem);
@@ -236,8 +248,9 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
   const int n_steps = (int)((p_end - p_begin + kStepRows - 1) / kStepRows);
   const int64_t n_c = n_rows - window;
 
-  // Sequence row of every list position of the chunk (-1: absent or out of range).
-  for (int i = threadIdx.x; i < n_steps * kStepRows; i += kAttnThreads) {
+  // Sequence row of every list position of the chunk (-1: absent or out of range), and
+  // two steps of -1 past the end for the fetches that run ahead of the last step.
+  for (int i = threadIdx.x; i < (n_steps + 2) * kStepRows; i += kAttnThreads) {
     const int64_t p = p_begin + i;
     int row = -1;
     if (p < p_end) {
@@ -274,45 +287,52 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
   for (int i = 0; i < kDimsPerWave / 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  // This thread's work item inside a step: row r, segment seg (one item per thread).
   // Two steps are fetched ahead (raw0 / raw1 alternate), so both steps of a 64-row chunk
-  // are in flight as soon as the row indices are known.
-  int item_r, item_seg;
-  SegRaw<KVFMT>::item_rs(threadIdx.x, &item_r, &item_seg);
-  SegRaw<KVFMT> raw0, raw1;
-  auto fetch = [&](SegRaw<KVFMT>& raw, int step) {
-    const int row = s_rows[step * kStepRows + item_r];
-    if (row >= 0) raw.load(codes, scales, (int64_t)b * seq_stride + row, item_seg);
-    else raw.zero();
-  };
+  // are in flight as soon as the row indices are known.  Rows are read through buffer
+  // resources over this query's sequence.  Every fetch is issued unconditionally (the
+  // steps past the end have only absent rows, which read nothing); an absent row's logit
+  // is masked to -inf, so its probability is exactly 0.  With no branch around the
+  // loads, both fetched steps stay in flight across the step being computed.
+  typedef StepRaw<KVFMT> Raw;
+  Raw raw0, raw1;
+  const Rsrc rc = make_rsrc(codes + (int64_t)b * seq_stride * Raw::kRowBytes,
+                            (uint32_t)(n_rows * Raw::kRowBytes));
+  const Rsrc rs = Raw::kScaleRowBytes == 0
+                      ? rc
+                      : make_rsrc(scales + (int64_t)b * seq_stride * Raw::kScaleRowBytes,
+                                  (uint32_t)(n_rows * Raw::kScaleRowBytes));
+  auto fetch = [&](Raw& raw, int step) { raw.load(rc, rs, s_rows + step * kStepRows, threadIdx.x); };
 
-  auto run_step = [&](SegRaw<KVFMT>& raw, int step) {
+  auto run_step = [&](Raw& raw, int step) {
     uint16_t* tile = s_kv0 + (NB == 2 ? (step & 1) * kTileElems : 0);
     if (NB == 1 && step > 0) lds_barrier();  // the previous step's tile is consumed
     // ---- decode the fetched rows into the tile (fp16, row-major)
+    raw.store(tile, threadIdx.x);
+    lds_barrier();
+    fetch(raw, step + 2);
+
+    // ---- logits S^T, split over the waves: wave w computes row tile w & 1 over dims
+    // 256 * (w >> 1) .. +255 (lane (g, n): rows 16*rt + 4g + i, head n); the two halves
+    // meet in LDS and every wave reads the full 32 x 16 block.
     {
-      u32x4 d[8];
-      raw.decode(item_seg, d);
-      u32x4* dst = reinterpret_cast<u32x4*>(tile + item_r * kPitch + item_seg * 64);
+      const int rt = wave & 1, kh = wave >> 1;
+      const uint16_t* qr = s_q + n * kPitch + 256 * kh + 8 * g;
+      const uint16_t* kr = tile + (16 * rt + n) * kPitch + 256 * kh + 8 * g;
+      f32x4 part = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dst[i] = d[i];
+      for (int t = 0; t < 8; ++t)
+        part = mfma16x16x32_f16(as_f16x8(*reinterpret_cast<const u32x4*>(kr + 32 * t)),
+                                as_f16x8(*reinterpret_cast<const u32x4*>(qr + 32 * t)), part);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_logit[kh][16 * rt + 4 * g + i][n] = part[i];
     }
     lds_barrier();
-    if (step + 2 < n_steps) fetch(raw, step + 2);
-
-    // ---- logits S^T: lane (g, n) gets rows 16*rt + 4g + i of head n
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    {
-      const uint16_t* qr = s_q + n * kPitch + 8 * g;
-      const uint16_t* k0 = tile + n * kPitch + 8 * g;
-      const uint16_t* k1 = tile + (16 + n) * kPitch + 8 * g;
+    f32x4 sacc[2];
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const f16x8 qb = as_f16x8(*reinterpret_cast<const u32x4*>(qr + 32 * t));
-        sacc[0] = mfma16x16x32_f16(as_f16x8(*reinterpret_cast<const u32x4*>(k0 + 32 * t)), qb, sacc[0]);
-        sacc[1] = mfma16x16x32_f16(as_f16x8(*reinterpret_cast<const u32x4*>(k1 + 32 * t)), qb, sacc[1]);
-      }
-    }
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sacc[rt][i] = s_logit[0][16 * rt + 4 * g + i][n] + s_logit[1][16 * rt + 4 * g + i][n];
     // ---- online softmax (log2 domain)
     float x[8];
     float mloc = -INFINITY;
@@ -358,12 +378,14 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
       o[i] = mfma16x16x32_f16(v_fragment(tile, g, n, (kDimsPerWave / 16) * wave + i), pb, o[i]);
   };
 
-  if (n_steps > 0) fetch(raw0, 0);
-  if (n_steps > 1) fetch(raw1, 1);
-  for (int step = 0; step < n_steps; step += 2) {
+  fetch(raw0, 0);
+  fetch(raw1, 1);
+  int step = 0;
+  for (; step + 1 < n_steps; step += 2) {
     run_step(raw0, step);
-    if (step + 1 < n_steps) run_step(raw1, step + 1);
+    run_step(raw1, step + 1);
   }
+  if (step < n_steps) run_step(raw0, step);
 
   // ---- partial records: the 16 x 512 output block is staged through LDS so that each
   // head's 2 KB record is written by consecutive lanes in whole cache lines; the
@@ -462,8 +484,9 @@ void launch_chunks(hipStream_t stream, const uint8_t* codes, const uint8_t* scal
                      stream, codes, scales, seq_stride, n_rows, q, n_heads, scale_log2, topk,    \
                      top_k, window, plan.n_list, plan.rows_per_chunk, plan.n_chunks, n_pairs,   \
                      part_o, part_ml)
-  if (plan.rows_per_chunk <= kStepRows) CSAKV_CHUNK(1);
-  else CSAKV_CHUNK(2);
+  // One decode tile (55 KB of LDS: two workgroups per CU); the second tile's one barrier
+  // per step saved less than the halved occupancy cost.
+  CSAKV_CHUNK(1);
 #undef CSAKV_CHUNK
 }
 
@@ -487,8 +510,12 @@ AttnPlan plan_attention(int batch, int64_t n_list, bool csa, int n_heads) {
   return p;
 }
 
-bool attention_supported(const AttnPlan& plan) {
-  return plan.n_chunks <= kMaxChunks && plan.rows_per_chunk <= kMaxChunkRows;
+bool attention_supported(const AttnPlan& plan, int kv_fmt, int64_t n_rows) {
+  const int64_t row_bytes = kv_fmt == 0 ? StepRaw<0>::kRowBytes
+                            : kv_fmt == 1 ? StepRaw<1>::kRowBytes
+                                          : StepRaw<2>::kRowBytes;
+  return plan.n_chunks <= kMaxChunks && plan.rows_per_chunk <= kMaxChunkRows && n_rows >= 0 &&
+         n_rows * row_bytes <= (int64_t)kAttnMaxSeqBytes;
 }
 
 // Workspace: O records [B][chunks][H][512] fp32, then (max, sum) pairs [B][chunks][H][2].

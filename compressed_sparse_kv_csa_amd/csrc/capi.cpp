@@ -117,7 +117,7 @@ csakv_status csa_decode(const csakv_csa_params* p, const csakv_cache* kv,
   }
   const CsaLayout L = csa_layout(p, n_c);
   if (full && !csakv::indexer_supported(L.idx)) return CSAKV_ERR_UNSUPPORTED;
-  if (!csakv::attention_supported(L.attn)) return CSAKV_ERR_UNSUPPORTED;
+  if (!csakv::attention_supported(L.attn, kv->fmt, kv->n_rows)) return CSAKV_ERR_UNSUPPORTED;
   if (workspace_bytes < L.total) return CSAKV_ERR_WORKSPACE;
   if (L.total > 0 && (!workspace || !aligned(workspace, kWsAlign))) return CSAKV_ERR_INVALID;
 
@@ -180,7 +180,8 @@ csakv_status hca_decode(int32_t batch, int32_t n_q_heads, float softmax_scale,
   if (st != CSAKV_OK) return st;
   if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return CSAKV_ERR_INVALID;
   if (kv->n_rows > INT32_MAX) return CSAKV_ERR_UNSUPPORTED;
-  if (!csakv::attention_supported(csakv::plan_attention(batch, kv->n_rows, false, n_q_heads)))
+  if (!csakv::attention_supported(csakv::plan_attention(batch, kv->n_rows, false, n_q_heads),
+                                 kv->fmt, kv->n_rows))
     return CSAKV_ERR_UNSUPPORTED;
   const size_t need = hca_decode_workspace_bytes(batch, n_q_heads, kv->n_rows);
   if (workspace_bytes < need) return CSAKV_ERR_WORKSPACE;

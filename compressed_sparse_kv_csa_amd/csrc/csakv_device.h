@@ -17,6 +17,17 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
+// ---------------------------------------------------------------- buffer resources
+
+// A raw buffer resource over [base, base + bytes): a load at an offset at or past the
+// end returns zeros and touches no memory.  base must be wave-uniform.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
 // ---------------------------------------------------------------- bf16 bits
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {

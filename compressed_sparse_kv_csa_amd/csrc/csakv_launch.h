@@ -50,9 +50,12 @@ struct AttnPlan {
 
 constexpr int kMaxChunkRows = 1024;  // rows one attention workgroup walks
 constexpr int kMaxChunks = 4096;     // chunks per query the combine merges
+// Largest shared-KV byte count of one sequence (codes, and FP4 scales separately): rows
+// are addressed by 32-bit offsets inside a per-sequence buffer resource.
+constexpr uint32_t kAttnMaxSeqBytes = 0xFFFFFF00u;
 
 AttnPlan plan_attention(int batch, int64_t n_list, bool csa, int n_heads);
-bool attention_supported(const AttnPlan& plan);
+bool attention_supported(const AttnPlan& plan, int kv_fmt, int64_t n_rows);
 size_t attention_workspace_bytes(int batch, int n_heads, const AttnPlan& plan);
 
 hipError_t launch_attention(int kv_fmt, bool csa, const uint8_t* codes, const uint8_t* scales,

@@ -463,12 +463,9 @@ __device__ __forceinline__ int32_t key_index(uint64_t key) { return (int32_t)(~(
 // through buffer resources whose base is the tile's first row and whose size ends at the
 // workgroup's last row: a row past the end reads as zeros (no clamping, no fault), and
 // every lane's offset inside a tile is a constant.
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
-
-__device__ __forceinline__ Rsrc make_rsrc(const uint8_t* base, int64_t bytes) {
-  const int n = bytes > 0 ? (int)bytes : 0;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, n, kRsrcWord3);
+// Offsets inside a tile are small, so a remainder past 4 GiB is clamped, not wrapped.
+__device__ __forceinline__ Rsrc tile_rsrc(const uint8_t* base, int64_t bytes) {
+  return make_rsrc(base, bytes <= 0 ? 0u : bytes >= 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)bytes);
 }
 
 // bf16 rows: in K-step t the lane supplies channels 32t + 8g .. 32t + 8g + 7.
@@ -593,8 +590,8 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
   const int lane_co = KT::code_offset(n, g), lane_so = KT::scale_offset(n, g);
   auto load_slot = [&](KT& kt, int k) {
     const int64_t r0 = (int64_t)__builtin_amdgcn_readfirstlane(slot_tile(k)) * 16;  // wave-uniform
-    const Rsrc rc = make_rsrc(kcodes + r0 * KT::kRowBytes, (rows_total - r0) * KT::kRowBytes);
-    const Rsrc rs = KT::kScales ? make_rsrc(kscales + r0 * (kIdxDim / 16), (rows_total - r0) * (kIdxDim / 16))
+    const Rsrc rc = tile_rsrc(kcodes + r0 * KT::kRowBytes, (rows_total - r0) * KT::kRowBytes);
+    const Rsrc rs = KT::kScales ? tile_rsrc(kscales + r0 * (kIdxDim / 16), (rows_total - r0) * (kIdxDim / 16))
                                 : rc;
     kt.load(rc, rs, lane_co, lane_so);
   };
