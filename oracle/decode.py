@@ -12,6 +12,10 @@ What one query token computes, per the pages:
   compressed entry plus the window.
 * CSA2 Reuse layers ("DeepSeek, KV 캐시를 토큰당 890바이트로 줄인 V4.1-Flash 공개",
   section 핵심 내용): attend with the top-512 indices an earlier layer chose.
+* CSA2 Reindex layers (same section, and "KV cache 890 bajtów na token", section
+  "Trzy mechanizmy zamiast jednej sztuczki"): a fresh indexer query re-ranks the
+  candidate pool that the group's Full layer built over the shared indexer keys
+  (the hierarchical sparse indexer), and the top-k of the pool is kept.
 
 Readings where the pages are silent
 * Indexer score: s_j = sum_h w_h * ReLU(q_h . k_j)  (the pages give no formula;
@@ -24,10 +28,16 @@ Readings where the pages are silent
 Row layout of a sequence's shared-KV cache: ``[window rows | compressed rows]``;
 top-k index j refers to compressed row j, i.e. cache row ``window + j``.
 
+* Reindex pool: the Full layer's candidate rows (its own top-P, P >= k); entries that
+  are negative or past N_c are empty, and a row listed twice counts once.  The pool
+  size is a parameter (the pages give none).
+
 Parity pins (tests/test_oracle_decode.py): brute-force per-element loops on tiny
 shapes, permutation and scaling invariances, the H_I = 1 / w = 1 reduction to a
 plain top-k of dot products, k >= N_c reducing CSA to dense attention, single-
-row and identical-row attention.
+row and identical-row attention; for Reindex, the whole-sequence pool reducing to
+the Full selection, a pool holding the global top-k returning it, pool-order and
+empty-entry invariance, and brute force over all subsets of a tiny pool.
 """
 from __future__ import annotations
 
@@ -54,6 +64,24 @@ def topk_indices(scores, k: int) -> np.ndarray:
     out = np.full(k, -1, dtype=np.int64)
     m = min(k, n)
     out[:m] = order[:m]
+    return out
+
+
+def reindex_topk(q_idx, w_idx, keys, pool, k: int) -> np.ndarray:
+    """CSA2 Reindex: the k rows of the candidate pool with the largest scores under this
+    layer's own indexer query, by (score desc, row index asc); -1 pads a short pool.
+
+    keys: [N_c, d_I] decoded shared indexer keys; pool: compressed-row indices (empty
+    when negative or >= N_c; repeats count once) -> [k] row indices.
+    """
+    keys = np.asarray(keys, dtype=np.float64)
+    p = np.asarray(pool, dtype=np.int64).reshape(-1)
+    rows = np.unique(p[(p >= 0) & (p < keys.shape[0])])
+    s = indexer_scores(q_idx, w_idx, keys[rows])
+    order = np.lexsort((rows, -s))
+    out = np.full(k, -1, dtype=np.int64)
+    m = min(k, rows.shape[0])
+    out[:m] = rows[order[:m]]
     return out
 
 

@@ -78,6 +78,56 @@ def test_topk_brute_force_subsets():
     assert set(D.topk_indices(s, 3).tolist()) == set(best)
 
 
+# ------------------------------------------------------------------ CSA2 reindex
+
+def test_reindex_whole_sequence_pool_is_the_full_selection():
+    """A pool of every row reduces Reindex to the Full layer's own selection."""
+    r = _rng(21)
+    q = r.standard_normal((6, 16)); w = r.uniform(0, 1, 6); k = r.standard_normal((500, 16))
+    s = D.indexer_scores(q, w, k)
+    for kk in (1, 37, 500, 520):
+        got = D.reindex_topk(q, w, k, r.permutation(500), kk)
+        assert got.tolist() == D.topk_indices(s, kk).tolist()
+
+
+def test_reindex_pool_holding_the_global_topk_returns_it():
+    """Whatever else the pool holds, the global top-k rows win inside it (row indices, not pool slots)."""
+    r = _rng(22)
+    q = r.standard_normal((4, 8)); w = r.uniform(0, 1, 4); k = r.standard_normal((1000, 8))
+    top = D.topk_indices(D.indexer_scores(q, w, k), 24)
+    others = r.choice(np.setdiff1d(np.arange(1000), top), 200, replace=False)
+    pool = r.permutation(np.concatenate([top, others]))
+    got = D.reindex_topk(q, w, k, pool, 24)
+    assert set(got.tolist()) == set(top.tolist())
+
+
+def test_reindex_pool_order_empty_entries_and_repeats():
+    r = _rng(23)
+    q = r.standard_normal((3, 8)); w = r.uniform(0, 1, 3); k = r.standard_normal((64, 8))
+    pool = r.choice(64, 20, replace=False)
+    ref = D.reindex_topk(q, w, k, pool, 8)
+    noisy = np.concatenate([pool[::-1], [-1, 64, 1000, -7], pool[:5]])
+    assert D.reindex_topk(q, w, k, noisy, 8).tolist() == ref.tolist()
+    short = D.reindex_topk(q, w, k, pool, 25)   # k beyond the pool: all 20, then -1
+    assert short[20:].tolist() == [-1] * 5
+    assert set(short[:20].tolist()) == set(pool.tolist())
+    assert D.reindex_topk(q, w, k, np.array([-1, -1]), 3).tolist() == [-1, -1, -1]
+
+
+def test_reindex_brute_force_over_pool_subsets():
+    """Tiny pools: the result maximises the summed score over every k-subset of the pool;
+    with integer dots and equal scores, the lower row index wins."""
+    r = _rng(24)
+    q = r.standard_normal((2, 4)); w = r.uniform(0, 1, 2); k = r.standard_normal((40, 4))
+    pool = r.choice(40, 9, replace=False)
+    s = D.indexer_scores(q, w, k)
+    best = max(itertools.combinations(pool.tolist(), 4), key=lambda t: sum(s[i] for i in t))
+    assert set(D.reindex_topk(q, w, k, pool, 4).tolist()) == set(best)
+    # H_I = 1, w = 1, integer keys: rows 3, 9 and 12 tie at the top score.
+    qi = np.ones((1, 2)); ki = np.zeros((16, 2)); ki[[3, 9, 12]] = [2.0, 3.0]; ki[5] = [1.0, 1.0]
+    assert D.reindex_topk(qi, np.ones(1), ki, [12, 5, 9, 3, 0], 2).tolist() == [3, 9]
+
+
 # ------------------------------------------------------------------ attention
 
 def test_attention_two_rows_closed_form():
