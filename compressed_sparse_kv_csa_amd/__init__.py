@@ -13,22 +13,22 @@ import os
 
 __all__ = [
     "CsakvError", "KV_BF16", "KV_FP8_MIXED", "KV_FP4", "IDX_BF16", "IDX_FP4", "MODE_FULL",
-    "MODE_REUSE", "CsaParams", "Cache", "KvCacheSpec", "KvCacheBreakdown", "lib", "lib_path",
+    "MODE_REUSE", "MODE_REINDEX", "CsaParams", "Cache", "KvCacheSpec", "KvCacheBreakdown", "lib", "lib_path",
     "cache", "csa_decode_workspace_bytes", "csa_decode", "csa_select_topk_workspace_bytes",
-    "csa_select_topk", "hca_decode_workspace_bytes",
+    "csa_select_topk", "csa_reindex_topk", "hca_decode_workspace_bytes",
     "hca_decode", "kv_quantize_fp4", "kv_quantize_fp8", "kv_dequantize", "kv_cache_bytes",
     "csakv_status_string", "EXPORTED_SYMBOLS",
 ]
 
 KV_BF16, KV_FP8_MIXED, KV_FP4 = 0, 1, 2
 IDX_BF16, IDX_FP4 = 0, 1
-MODE_FULL, MODE_REUSE = 0, 1
+MODE_FULL, MODE_REUSE, MODE_REINDEX = 0, 1, 2
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 
 EXPORTED_SYMBOLS = (
     "csa_decode_workspace_bytes", "csa_decode", "csa_select_topk_workspace_bytes",
-    "csa_select_topk", "hca_decode_workspace_bytes", "hca_decode",
+    "csa_select_topk", "csa_reindex_topk", "hca_decode_workspace_bytes", "hca_decode",
     "kv_quantize_fp4", "kv_quantize_fp8", "kv_dequantize", "kv_cache_bytes",
     "csakv_status_string",
 )
@@ -94,6 +94,8 @@ def lib() -> ctypes.CDLL:
         L.csa_select_topk_workspace_bytes.restype = SZ
         L.csa_select_topk.argtypes = [P(CsaParams), P(Cache), VP, VP, VP, VP, SZ, VP]
         L.csa_select_topk.restype = I32
+        L.csa_reindex_topk.argtypes = [P(CsaParams), P(Cache), VP, VP, VP, I32, VP, VP]
+        L.csa_reindex_topk.restype = I32
         L.hca_decode_workspace_bytes.argtypes = [I32, I32, I64]
         L.hca_decode_workspace_bytes.restype = SZ
         L.hca_decode.argtypes = [I32, I32, F, P(Cache), VP, VP, VP, SZ, VP]
@@ -177,6 +179,16 @@ def csa_select_topk(params: CsaParams, idx_keys: Cache, q_idx, w_idx, topk, work
                                _stream(stream))
     if check:
         _check(st, "csa_select_topk")
+    return st
+
+
+def csa_reindex_topk(params: CsaParams, idx_keys: Cache, q_idx, w_idx, pool, n_pool: int, topk,
+                     stream=None, check: bool = True) -> int:
+    keys = ctypes.byref(idx_keys) if idx_keys is not None else None
+    st = lib().csa_reindex_topk(ctypes.byref(params), keys, _ptr(q_idx),
+                                _ptr(w_idx), _ptr(pool), int(n_pool), _ptr(topk), _stream(stream))
+    if check:
+        _check(st, "csa_reindex_topk")
     return st
 
 

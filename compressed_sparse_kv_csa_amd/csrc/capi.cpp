@@ -165,6 +165,31 @@ csakv_status csa_select_topk(const csakv_csa_params* p, const csakv_cache* idx_k
       workspace, topk, static_cast<hipStream_t>(stream)));
 }
 
+csakv_status csa_reindex_topk(const csakv_csa_params* p, const csakv_cache* idx_keys,
+                              const uint16_t* q_idx, const float* w_idx, const int32_t* pool,
+                              int32_t n_pool, int32_t* topk, void* stream) {
+  if (!p || p->mode != CSAKV_MODE_REINDEX) return CSAKV_ERR_INVALID;
+  csakv_status st = check_select_params(p);
+  if (st != CSAKV_OK) return st;
+  if ((st = check_cache(idx_keys, false)) != CSAKV_OK) return st;
+  if (n_pool < 1) return CSAKV_ERR_INVALID;
+  if (n_pool > csakv::kMaxPool) return CSAKV_ERR_UNSUPPORTED;
+  if (!q_idx || !w_idx || !pool || !topk || !aligned(q_idx, 16) || !aligned(w_idx, 4) ||
+      !aligned(pool, 4) || !aligned(topk, 4))
+    return CSAKV_ERR_INVALID;
+  const int64_t n_c = idx_keys->n_rows;
+  if (n_c > INT32_MAX || !csakv::reindex_supported(idx_keys->fmt, n_c))
+    return CSAKV_ERR_UNSUPPORTED;
+  // The output must not overlap the pool it is computed from.
+  const uintptr_t pb = reinterpret_cast<uintptr_t>(pool), tb = reinterpret_cast<uintptr_t>(topk);
+  const uintptr_t pe = pb + (uintptr_t)p->batch * n_pool * 4, te = tb + (uintptr_t)p->batch * p->top_k * 4;
+  if (pb < te && tb < pe) return CSAKV_ERR_INVALID;
+  return hip_status(csakv::launch_reindex(
+      idx_keys->fmt, static_cast<const uint8_t*>(idx_keys->codes), idx_keys->scales,
+      idx_keys->seq_stride_rows, n_c, q_idx, w_idx, p->batch, p->n_idx_heads, pool, n_pool,
+      p->top_k, topk, static_cast<hipStream_t>(stream)));
+}
+
 size_t hca_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int64_t n_rows) {
   if (batch < 1 || n_q_heads < 1 || n_rows < 0) return 0;
   csakv::AttnPlan a = csakv::plan_attention(batch, n_rows, false, n_q_heads);

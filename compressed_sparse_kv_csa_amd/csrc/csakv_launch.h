@@ -31,6 +31,17 @@ constexpr int kMaxTopK = 1024;
 constexpr int kMergeCap = 8192;
 constexpr int kMaxMergeSlices = 512;
 
+// CSA2 reindex: pool slots per query, and the largest indexer-key byte count of one
+// sequence (rows are addressed by 32-bit offsets inside a per-sequence buffer resource).
+constexpr int kMaxPool = 4096;
+constexpr uint32_t kReindexMaxSeqBytes = 0xFFFFFF00u;
+
+bool reindex_supported(int key_fmt, int64_t n_c);
+hipError_t launch_reindex(int key_fmt, const uint8_t* codes, const uint8_t* scales,
+                          int64_t seq_stride, int64_t n_c, const uint16_t* q_idx,
+                          const float* w_idx, int batch, int n_heads, const int32_t* pool,
+                          int n_pool, int top_k, int32_t* topk, hipStream_t stream);
+
 IndexerPlan plan_indexer(int batch, int64_t n_c, int top_k);
 bool indexer_supported(const IndexerPlan& plan);
 size_t indexer_workspace_bytes(int batch, const IndexerPlan& plan);

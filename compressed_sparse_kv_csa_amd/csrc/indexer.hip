@@ -540,6 +540,53 @@ __device__ __forceinline__ f16x8 q_operand(u32x4 v, float scale, f16x8*) {
   return r;
 }
 
+// Query b's indexer query fragments (A operand: head n of each 16-head tile, the lane's
+// K-channels) and the weights of the accumulator rows lane (g, n) holds (heads
+// 16*ht + 4g + i); heads past n_heads get zeros.
+template <class KT, int HT>
+__device__ __forceinline__ void query_frags(const uint16_t* __restrict__ q_idx,
+                                            const float* __restrict__ w_idx, int b, int n_heads,
+                                            int g, int n, typename KT::Op (&qa)[HT][4],
+                                            float (&wv)[HT][4]) {
+  typedef typename KT::Op Op;
+  u32x4 qraw[HT][4];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 16 * ht + 4 * g + i;
+      wv[ht][i] = h < n_heads ? w_idx[(int64_t)b * n_heads + h] : 0.0f;
+    }
+  float qmax = 0.0f;
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const int head = 16 * ht + n;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (head < n_heads)
+        v = *reinterpret_cast<const u32x4*>(q_idx + ((int64_t)b * n_heads + head) * kIdxDim +
+                                            KT::q_channel(g, t));
+      qraw[ht][t] = v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        qmax = fmaxf(qmax, fmaxf(fabsf(bf16_to_f32(v[i] & 0xFFFFu)), fabsf(bf16_to_f32(v[i] >> 16))));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, off));
+  // Power of two putting max|q| in [2^14, 2^15) (used by the fp16 path only).
+  int p = 0;
+  if (qmax > 0.0f) p = 14 - ((int)((__float_as_uint(qmax) >> 23) & 0xFF) - 127);
+  p = max(-100, min(p, 100));
+  const float qscale = __builtin_ldexpf(1.0f, p);
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) qa[ht][t] = q_operand(qraw[ht][t], qscale, (Op*)nullptr);
+
+}
+
 // ------------------------------------------------------------------ scan kernel
 
 constexpr int kSubTiles = 16;                          // tiles per wave per unrolled pass
@@ -604,45 +651,10 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
     load_slot(ring[d], d);
   }
 
-  // Indexer query fragments (A operand, head n of each 16-head tile) and the weights of
-  // the accumulator rows this lane holds (heads 16*ht + 4g + i).
-  u32x4 qraw[HT][4];
-  float wv[HT][4];
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 16 * ht + 4 * g + i;
-      wv[ht][i] = h < n_heads ? w_idx[(int64_t)b * n_heads + h] : 0.0f;
-    }
-  float qmax = 0.0f;
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    const int head = 16 * ht + n;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (head < n_heads)
-        v = *reinterpret_cast<const u32x4*>(q_idx + ((int64_t)b * n_heads + head) * kIdxDim +
-                                            KT::q_channel(g, t));
-      qraw[ht][t] = v;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        qmax = fmaxf(qmax, fmaxf(fabsf(bf16_to_f32(v[i] & 0xFFFFu)), fabsf(bf16_to_f32(v[i] >> 16))));
-    }
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, off));
-  // Power of two putting max|q| in [2^14, 2^15) (used by the fp16 path only).
-  int p = 0;
-  if (qmax > 0.0f) p = 14 - ((int)((__float_as_uint(qmax) >> 23) & 0xFF) - 127);
-  p = max(-100, min(p, 100));
-  const float qscale = __builtin_ldexpf(1.0f, p);
+  // Indexer query fragments and head weights.
   Op qa[HT][4];
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) qa[ht][t] = q_operand(qraw[ht][t], qscale, (Op*)nullptr);
+  float wv[HT][4];
+  query_frags<KT, HT>(q_idx, w_idx, b, n_heads, g, n, qa, wv);
 
   for (int ps = 0; ps < n_pass; ++ps) {
 #pragma unroll
@@ -820,6 +832,145 @@ __global__ __launch_bounds__(kMergeThreads) void indexer_merge_kernel(
     if (s_buf[p] >= kth) out[pos++] = key_index(s_buf[p]);
 }
 
+// ------------------------------------------------------------------ CSA2 reindex
+
+// One workgroup per query re-ranks the query's candidate pool with its own indexer
+// query: lane (g, n) of a 16-row tile reads pool row pool[16t + n], the tile is scored
+// exactly as in the scan, and the top-k of the pool is selected in LDS.  Rows are
+// addressed by 32-bit offsets inside a buffer resource over the query's sequence; an
+// empty slot (and every tile past the end) is read past that range, which returns
+// zeros without touching memory.
+constexpr int kReindexThreads = 512;
+constexpr int kReindexWaves = kReindexThreads / kWave;
+constexpr uint32_t kAbsentKeyOffset = kReindexMaxSeqBytes;
+
+template <class KT, int HT>
+__global__ __launch_bounds__(kReindexThreads) void reindex_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t seq_stride,
+    int64_t n_c, const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
+    int n_heads, const int32_t* __restrict__ pool, int n_pool, int top_k,
+    int32_t* __restrict__ topk) {
+  typedef typename KT::Op Op;
+  constexpr int NT = kReindexThreads;
+  __shared__ int s_row[kMaxPool];        // pool rows, -1 for an empty slot
+  __shared__ uint64_t s_key[kMaxPool];   // selection key of every slot, 0 when empty
+  __shared__ uint64_t s_val[kMaxPool];   // the non-empty keys, in pool order
+  __shared__ uint64_t s_list[kMergeListCap];
+  __shared__ SelectSmem sm;
+  const int b = blockIdx.x;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int g = lane >> 4, n = lane & 15;
+
+  for (int i = threadIdx.x; i < n_pool; i += NT) {
+    const int32_t r = pool[(int64_t)b * n_pool + i];
+    s_row[i] = (r >= 0 && r < n_c) ? r : -1;
+  }
+  Op qa[HT][4];
+  float wv[HT][4];
+  query_frags<KT, HT>(q_idx, w_idx, b, n_heads, g, n, qa, wv);
+  lds_barrier();
+
+  const Rsrc rc = make_rsrc(codes + (int64_t)b * seq_stride * KT::kRowBytes,
+                            (uint32_t)(n_c * KT::kRowBytes));
+  const Rsrc rs = KT::kScales ? make_rsrc(scales + (int64_t)b * seq_stride * (kIdxDim / 16),
+                                          (uint32_t)(n_c * (kIdxDim / 16)))
+                              : rc;
+  const int n_tiles = (n_pool + 15) / 16;
+  auto slot_row = [&](int t) -> int {  // pool row of lane n in tile t (-1: none)
+    const int pos = 16 * t + n;
+    return pos < n_pool ? s_row[pos < kMaxPool ? pos : kMaxPool - 1] : -1;
+  };
+  auto load_tile = [&](KT& kt, int t) {
+    const int row = slot_row(t);
+    kt.load(rc, rs,
+            row >= 0 ? (uint32_t)row * KT::kRowBytes + KT::code_offset(0, g) : kAbsentKeyOffset,
+            row >= 0 ? (uint32_t)row * (kIdxDim / 16) + KT::scale_offset(0, g) : kAbsentKeyOffset);
+  };
+
+  // The wave's tiles are wave + 8m; kRing of them are in flight.
+  const int my_tiles = n_tiles > wave ? (n_tiles - wave + kReindexWaves - 1) / kReindexWaves : 0;
+  KT ring[kRing];
+#pragma unroll
+  for (int d = 0; d < kRing; ++d) {
+    ring[d].set_lane(g);
+    load_tile(ring[d], wave + kReindexWaves * d);
+  }
+  for (int m0 = 0; m0 < my_tiles; m0 += kRing) {
+#pragma unroll
+    for (int d = 0; d < kRing; ++d) {
+      const int t = wave + kReindexWaves * (m0 + d);
+      Op kb[4];
+      ring[d].decode(kb);
+      load_tile(ring[d], t + kReindexWaves * kRing);
+      f32x4 acc[HT];
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) acc[ht] = KT::mma(qa[ht][k], kb[k], acc[ht]);
+      float sc = 0.0f;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sc += wv[ht][i] * __int_as_float(max(__float_as_int(acc[ht][i]), 0));
+      sc = wave_sum_rows(sc);
+      const int pos = 16 * t + n;
+      if (g == 0 && pos < n_pool) {
+        const int row = s_row[pos];
+        s_key[pos] = row >= 0 ? compose_key(f32_order_key(sc), (uint32_t)row) : 0ull;
+      }
+    }
+  }
+  lds_barrier();
+
+  // The non-empty keys, compacted in pool order.
+  constexpr int kPer = kMaxPool / NT;
+  const int q0 = threadIdx.x * kPer;
+  uint32_t c = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) c += (q0 + j < n_pool && s_key[q0 + j] != 0ull);
+  uint32_t n_valid;
+  uint32_t wpos = block_exclusive_scan<NT>(c, sm.wsum, &n_valid);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (q0 + j < n_pool && s_key[q0 + j] != 0ull) s_val[wpos++] = s_key[q0 + j];
+  lds_barrier();
+
+  int32_t* out = topk + (int64_t)b * top_k;
+  const int k1 = min(top_k, (int)n_valid);
+  for (int i = k1 + threadIdx.x; i < top_k; i += NT) out[i] = -1;
+  if (k1 == 0) return;
+  const uint64_t kth = (int)n_valid > k1 ? block_kth_exact<NT>(s_val, (int)n_valid, k1, sm, s_list) : 1ull;
+  const int chunk = ((int)n_valid + NT - 1) / NT;
+  const int p0 = threadIdx.x * chunk, p1 = min(p0 + chunk, (int)n_valid);
+  uint32_t cw = 0;
+  for (int p = p0; p < p1; ++p) cw += s_val[p] >= kth;
+  uint32_t total;
+  uint32_t opos = block_exclusive_scan<NT>(cw, sm.wsum, &total);
+  for (int p = p0; p < p1; ++p)  // (the bound only matters for a pool that repeats a row)
+    if (s_val[p] >= kth && opos < (uint32_t)k1) out[opos++] = key_index(s_val[p]);
+}
+
+template <class KT>
+void launch_reindex_ht(int ht, hipStream_t stream, const uint8_t* codes, const uint8_t* scales,
+                       int64_t seq_stride, int64_t n_c, const uint16_t* q_idx, const float* w_idx,
+                       int batch, int n_heads, const int32_t* pool, int n_pool, int top_k,
+                       int32_t* topk) {
+#define CSAKV_REINDEX(H)                                                                        \
+  hipLaunchKernelGGL((reindex_kernel<KT, H>), dim3(batch), dim3(kReindexThreads), 0, stream,   \
+                     codes, scales, seq_stride, n_c, q_idx, w_idx, n_heads, pool, n_pool, top_k, \
+                     topk)
+  switch (ht) {
+    case 1: CSAKV_REINDEX(1); break;
+    case 2: CSAKV_REINDEX(2); break;
+    case 3: CSAKV_REINDEX(3); break;
+    default: CSAKV_REINDEX(4); break;
+  }
+#undef CSAKV_REINDEX
+}
+
 template <class KT, int HT>
 void launch_scan(hipStream_t stream, const uint8_t* codes, const uint8_t* scales,
                  int64_t seq_stride, int64_t n_c, const uint16_t* q_idx, const float* w_idx,
@@ -917,6 +1068,25 @@ hipError_t launch_indexer(int key_fmt, const uint8_t* codes, const uint8_t* scal
   }
   hipLaunchKernelGGL(indexer_merge_kernel, dim3(batch), dim3(kMergeThreads), 0, stream, ws, n_c,
                      top_k, plan.n_slices, plan.cap, topk);
+  return hipGetLastError();
+}
+
+bool reindex_supported(int key_fmt, int64_t n_c) {
+  const int64_t row_bytes = key_fmt == 0 ? KeyTileBf16::kRowBytes : KeyTileFp4::kRowBytes;
+  return n_c >= 0 && n_c * row_bytes <= (int64_t)kReindexMaxSeqBytes;
+}
+
+hipError_t launch_reindex(int key_fmt, const uint8_t* codes, const uint8_t* scales,
+                          int64_t seq_stride, int64_t n_c, const uint16_t* q_idx,
+                          const float* w_idx, int batch, int n_heads, const int32_t* pool,
+                          int n_pool, int top_k, int32_t* topk, hipStream_t stream) {
+  const int ht = (n_heads + 15) / 16;
+  if (key_fmt == 0)
+    launch_reindex_ht<KeyTileBf16>(ht, stream, codes, scales, seq_stride, n_c, q_idx, w_idx,
+                                   batch, n_heads, pool, n_pool, top_k, topk);
+  else
+    launch_reindex_ht<KeyTileFp4>(ht, stream, codes, scales, seq_stride, n_c, q_idx, w_idx,
+                                  batch, n_heads, pool, n_pool, top_k, topk);
   return hipGetLastError();
 }
 

@@ -64,7 +64,13 @@ typedef enum { CSAKV_KV_BF16 = 0, CSAKV_KV_FP8_MIXED = 1, CSAKV_KV_FP4 = 2 } csa
  * section 四: indexer keys are cached in FP4). */
 typedef enum { CSAKV_IDX_BF16 = 0, CSAKV_IDX_FP4 = 1 } csakv_idx_fmt;
 
-typedef enum { CSAKV_MODE_FULL = 0, CSAKV_MODE_REUSE = 1 } csakv_mode;
+/* Layer modes of CSA2 ("DeepSeek, KV 캐시를 토큰당 890바이트로 줄인 V4.1-Flash 공개",
+ * section 핵심 내용; "KV cache 890 bajtów na token", section "Trzy mechanizmy zamiast
+ * jednej sztuczki"): FULL scores every compressed entry; REINDEX re-ranks the Full
+ * layer's candidate pool with its own indexer query (csa_reindex_topk); REUSE attends
+ * with indices chosen by an earlier layer.  csa_decode runs FULL or REUSE; a Reindex
+ * layer is csa_reindex_topk followed by csa_decode in REUSE mode. */
+typedef enum { CSAKV_MODE_FULL = 0, CSAKV_MODE_REUSE = 1, CSAKV_MODE_REINDEX = 2 } csakv_mode;
 
 /* One cache tensor of B sequences.  Sequence b's row r starts at byte
  * (b * seq_stride_rows + r) * code_bytes(fmt) of `codes`; for FP4 its scales start
@@ -126,6 +132,30 @@ size_t csa_select_topk_workspace_bytes(const csakv_csa_params* p, int64_t n_comp
 csakv_status csa_select_topk(const csakv_csa_params* p, const csakv_cache* idx_keys,
                              const uint16_t* q_idx, const float* w_idx, int32_t* topk,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* CSA2 Reindex, the hierarchical sparse indexer ("DeepSeek, KV 캐시를 토큰당 890바이트로
+ * 줄인 V4.1-Flash 공개", section 핵심 내용: a Reindex layer computes only a new query and
+ * re-ranks; "KV cache 890 bajtów na token", section "Trzy mechanizmy zamiast jednej
+ * sztuczki": deeper layers index only the candidate pool the group's Full layer built,
+ * so their indexing cost no longer grows with the context).  For each query b, the rows
+ * of pool[b] are scored with this layer's indexer query as s_j = sum_h w_h *
+ * ReLU(q_h . k_j) over the shared indexer keys, and the top_k of the pool are kept.
+ *   p         mode CSAKV_MODE_REINDEX; batch, n_idx_heads (1..64) and top_k
+ *             (1..1024) are used, n_q_heads, window and softmax_scale are not.
+ *   idx_keys  the shared indexer keys, n_rows = N_c, any csakv_idx_fmt; one sequence's
+ *             keys (codes, and FP4 scales) must span at most 4 GiB - 256 bytes.
+ *   q_idx     [B][H_I][128] bf16, this layer's indexer queries.
+ *   w_idx     [B][H_I] fp32, this layer's head weights.
+ *   pool      [B][n_pool] int32 compressed-row indices, 1 <= n_pool <= 4096, for
+ *             example csa_select_topk's output with top_k = n_pool.  Entries < 0 or
+ *             >= N_c are empty; the other entries of one query must be distinct.
+ *   topk      [B][top_k] int32: the set of the top_k pool rows (ties in score go to
+ *             the lower row index) in pool order; -1 pads when the pool holds fewer
+ *             rows.  Must not overlap pool.
+ * No workspace: one workgroup per query keeps the pool in LDS. */
+csakv_status csa_reindex_topk(const csakv_csa_params* p, const csakv_cache* idx_keys,
+                              const uint16_t* q_idx, const float* w_idx, const int32_t* pool,
+                              int32_t n_pool, int32_t* topk, void* stream);
 
 /* Bytes of workspace hca_decode needs for B sequences of n_rows rows each. */
 size_t hca_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int64_t n_rows);

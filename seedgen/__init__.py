@@ -132,6 +132,14 @@ def kv_rows_bf16(seed: int, tensor_id: int, shape, device="cpu") -> torch.Tensor
     return (z * gain).to(torch.bfloat16)
 
 
+def distinct_indices(seed: int, tensor_id: int, n: int, m: int) -> "np.ndarray":
+    """m distinct indices in [0, n), in a seeded random order: the first m of the stable
+    argsort of draws 0 .. n-1 (a seeded permutation of range(n))."""
+    import numpy as np
+    d = draws(seed, tensor_id, 0, n).numpy()
+    return np.argsort(d, kind="stable")[:m].astype(np.int64)
+
+
 class TID:
     """Tensor-id roles; the id of a tensor is ``role * 256 + layer``."""
 
@@ -140,6 +148,7 @@ class TID:
     W_IDX = 3      # indexer head weights [B][H_I]
     IDX_KEYS = 4   # indexer keys [B][N_c][128]
     KV = 5         # shared-KV rows [B][W + N_c][512]
+    POOL = 6       # candidate pools [B][n_pool] (one stream per query: layer = query)
 
 
 def tid(role: int, layer: int = 0) -> int:

@@ -142,3 +142,24 @@ def test_hca_and_codecs_reject_bad_arguments():
     assert ck.kv_dequantize(2, FAKE, None, 10, 512, FAKE, stream=0, check=False) == ck.ERR_INVALID
     assert ck.kv_dequantize(9, FAKE, None, 10, 512, FAKE, stream=0, check=False) == ck.ERR_INVALID
     assert ck.csakv_status_string(-2) == "unsupported shape or format"
+
+
+def test_reindex_rejects_bad_arguments():
+    p = _params(mode=ck.MODE_REINDEX)
+
+    def call(p=p, idx=IDX, qi=FAKE, w=FAKE, pool=FAKE, n_pool=1024, topk=FAKE + 65536):
+        return ck.csa_reindex_topk(p, idx, qi, w, pool, n_pool, topk, stream=0, check=False)
+
+    assert call(p=_params(mode=ck.MODE_FULL)) == ck.ERR_INVALID            # wrong mode
+    assert ck.csa_decode_workspace_bytes(p, 1024) == 0                    # csa_decode has no REINDEX
+    assert _call(p, idx=IDX) == ck.ERR_INVALID
+    assert call(n_pool=0) == ck.ERR_INVALID
+    assert call(n_pool=4097) == ck.ERR_UNSUPPORTED
+    assert call(p=_params(mode=ck.MODE_REINDEX, top_k=2048)) == ck.ERR_UNSUPPORTED
+    assert call(p=_params(mode=ck.MODE_REINDEX, n_idx_heads=0)) == ck.ERR_INVALID
+    assert call(pool=0) == ck.ERR_INVALID                                 # null
+    assert call(qi=FAKE + 2) == ck.ERR_INVALID                            # misaligned
+    assert call(idx=None) == ck.ERR_INVALID
+    assert call(topk=FAKE + 1024) == ck.ERR_INVALID                       # output overlaps the pool
+    huge = ck.Cache(ck.IDX_BF16, 0, 1 << 24, 1 << 24, FAKE, None)         # 4 GiB of keys
+    assert call(idx=huge) == ck.ERR_UNSUPPORTED
