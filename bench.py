@@ -5,7 +5,10 @@ A step is one pass of the decode hot path over one batch.  For the CSA workloads
 indexer scores every compressed entry of each query's sequence, keeps the top-512, and
 attends over those entries plus the 128-row sliding window (csa_decode, FULL mode);
 the CSA2 stack adds five Reuse layers that attend with the same indices over their own
-caches.  The HCA workload attends densely over every row (hca_decode).  The default
+caches.  The CSA2 Reindex stack is the hierarchical indexer: the Full layer selects a
+1024-row pool, and each of six layers re-ranks the pool with its own indexer query to
+512 rows (csa_reindex_topk; the Full layer with its own query) and attends over them in
+its own cache.  The HCA workload attends densely over every row (hca_decode).  The default
 workload is the 1M-token context with mixed FP8/BF16 shared-KV rows and FP4 indexer
 keys, B = 4 query tokens.  Inputs are synthetic and seed-generated, and resident in HBM
 before timing starts; R replicas of every cache (>= 1 GiB in all) rotate across steps so
@@ -43,6 +46,9 @@ WORKLOADS = {
                           kv="bf16", idx="bf16", seed=2, context=131072, layers=1),
     "csa2_stack_fp4_1m": dict(kind="csa", B=8, n_c=262144, window=128, hq=64, hi=64, top_k=512,
                               kv="fp4", idx="fp4", seed=5, context=1 << 20, layers=6),
+    "csa2_reindex_fp4_1m": dict(kind="csa2r", B=8, n_c=262144, window=128, hq=64, hi=64,
+                                top_k=512, pool=1024, kv="fp4", idx="fp4", seed=5,
+                                context=1 << 20, layers=6),
     "hca_bf16_1m": dict(kind="hca", B=16, n_c=8192, window=128, hq=64, hi=0, top_k=0, kv="bf16",
                         idx=None, seed=3, context=1 << 20, layers=1),
 }
@@ -65,8 +71,15 @@ def algorithmic_bytes(w: dict) -> dict:
         attn = B * ((n_c + w["window"]) * KV_ROW_BYTES[w["kv"]] + 2 * w["hq"] * 512 * 2)
         return {"indexer": 0, "attention": attn, "step": attn}
     rows = min(k, n_c) + w["window"]
-    idx = B * (n_c * IDX_ROW_BYTES[w["idx"]] + w["hi"] * 128 * 2 + w["hi"] * 4 + k * 4)
+    q_i = w["hi"] * 128 * 2 + w["hi"] * 4
     attn = B * (rows * KV_ROW_BYTES[w["kv"]] + 2 * w["hq"] * 512 * 2)
+    if w["kind"] == "csa2r":  # pool select, then per layer: re-rank the pool and attend
+        P = w["pool"]
+        idx = B * (n_c * IDX_ROW_BYTES[w["idx"]] + q_i + P * 4)
+        reindex = B * (P * IDX_ROW_BYTES[w["idx"]] + q_i + P * 4 + k * 4)
+        return {"indexer": idx, "attention": attn,
+                "step": idx + w["layers"] * (reindex + attn + B * k * 4)}
+    idx = B * (n_c * IDX_ROW_BYTES[w["idx"]] + q_i + k * 4)
     reuse = (w["layers"] - 1) * (attn + B * k * 4)
     return {"indexer": idx, "attention": attn, "step": idx + attn + reuse}
 
@@ -98,7 +111,7 @@ def build_inputs(w: dict, replicas: int):
     # One set of caches, generated and quantised on the GPU, then copied per replica.
     kvs = [kv_cache(layer) for layer in range(w["layers"])]
     k_codes = k_scales = None
-    if w["kind"] == "csa":
+    if w["kind"] in ("csa", "csa2r"):
         keys16 = seedgen.bf16_normal(w["seed"], seedgen.tid(T.IDX_KEYS), (B, n_c, 128), dev)
         if w["idx"] == "fp4":
             k_codes = torch.empty((B, n_c, 64), dtype=torch.uint8, device=dev)
@@ -127,6 +140,16 @@ def build_inputs(w: dict, replicas: int):
             rep["qi"] = seedgen.bf16_normal(s, seedgen.tid(T.Q_IDX), (B, w["hi"], 128), dev)
             rep["w"] = seedgen.uniform01(s, seedgen.tid(T.W_IDX), (B, w["hi"]), dev)
             rep["topk"] = torch.empty((B, w["top_k"]), dtype=torch.int32, device=dev)
+        if w["kind"] == "csa2r":
+            idx_fmt = {"bf16": ck.IDX_BF16, "fp4": ck.IDX_FP4}[w["idx"]]
+            rep["kc"], rep["ks"] = cp(k_codes), cp(k_scales)
+            rep["idx"] = ck.cache(idx_fmt, rep["kc"], n_c, n_c, rep["ks"])
+            rep["qi"] = [seedgen.bf16_normal(s, seedgen.tid(T.Q_IDX, layer), (B, w["hi"], 128), dev)
+                         for layer in range(w["layers"])]
+            rep["w"] = [seedgen.uniform01(s, seedgen.tid(T.W_IDX, layer), (B, w["hi"]), dev)
+                        for layer in range(w["layers"])]
+            rep["pool"] = torch.empty((B, w["pool"]), dtype=torch.int32, device=dev)
+            rep["topk"] = torch.empty((B, w["top_k"]), dtype=torch.int32, device=dev)
         reps.append(rep)
     torch.cuda.synchronize()
     return reps
@@ -152,6 +175,31 @@ def run_gpu(w: dict, steps: int, warmup: int, replicas: int | None):
             ck.hca_decode(B, w["hq"], scale, r["kv"][0], r["q"][0], r["out"][0], ws, ws_bytes, stream=sh)
 
         stage, stage_bytes, stage_name = step, nbytes["attention"], "hca_decode (attention + combine)"
+    elif w["kind"] == "csa2r":
+        P = w["pool"]
+        p_pool = ck.CsaParams(B, w["hq"], w["hi"], P, w["window"], ck.MODE_FULL, scale, 0)
+        p_rx = ck.CsaParams(B, 0, w["hi"], w["top_k"], 0, ck.MODE_REINDEX, 1.0, 0)
+        p_reuse = ck.CsaParams(B, w["hq"], 0, w["top_k"], w["window"], ck.MODE_REUSE, scale, 0)
+        ws_bytes = max(ck.csa_select_topk_workspace_bytes(p_pool, w["n_c"]),
+                       ck.csa_decode_workspace_bytes(p_reuse, w["n_c"]))
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+
+        def step(i):
+            r = reps[i % R]
+            ck.csa_select_topk(p_pool, r["idx"], r["qi"][0], r["w"][0], r["pool"], ws, ws_bytes,
+                               stream=sh)
+            for layer in range(w["layers"]):
+                ck.csa_reindex_topk(p_rx, r["idx"], r["qi"][layer], r["w"][layer], r["pool"], P,
+                                    r["topk"], stream=sh)
+                ck.csa_decode(p_reuse, r["kv"][layer], None, r["q"][layer], None, None, r["topk"],
+                              r["out"][layer], ws, ws_bytes, stream=sh)
+
+        def stage(i):
+            r = reps[i % R]
+            ck.csa_select_topk(p_pool, r["idx"], r["qi"][0], r["w"][0], r["pool"], ws, ws_bytes,
+                               stream=sh)
+
+        stage_bytes, stage_name = nbytes["indexer"], "indexer stage (csa_select_topk, 1024-row pool)"
     else:
         p = ck.CsaParams(B, w["hq"], w["hi"], w["top_k"], w["window"], ck.MODE_FULL, scale, 0)
         p_reuse = ck.CsaParams(B, w["hq"], 0, w["top_k"], w["window"], ck.MODE_REUSE, scale, 0)
@@ -291,6 +339,9 @@ def run_cpu_baseline(w: dict, queries: int):
         return {"value": round(queries / dt, 4), "unit": "query-tokens/s", "cores": int(cores),
                 "kind": "oracle", "sample": sample}
 
+    if w["kind"] == "csa2r":
+        return cpu_baseline_reindex(w, queries, qs, bits, encode, decode, cores)
+
     qi = seedgen.bf16_normal(s, seedgen.tid(T.Q_IDX), (B, w["hi"], 128), dev)[:queries]
     wv = seedgen.uniform01(s, seedgen.tid(T.W_IDX), (B, w["hi"]), dev)[:queries]
     qi = qi.float().cpu().double().numpy()
@@ -323,6 +374,49 @@ def run_cpu_baseline(w: dict, queries: int):
             "kind": "oracle",
             "sample": f"{queries} of the {B} query tokens of one step (same seeds and shapes): "
                       f"{n_c} {w['idx']} indexer keys each, then {W}+{k} {w['kv']} rows{layers}; "
+                      f"numpy fp64, {dt:.1f} s"}
+
+
+def cpu_baseline_reindex(w, queries, qs, bits, encode, decode, cores):
+    """The oracle on the CSA2 Reindex stack: the Full layer's pool, then per layer the
+    re-ranked top-k and the attention over it (same seeds and shapes as the GPU run)."""
+    import numpy as np
+    import torch
+    import seedgen
+    from oracle import decode as OD, formats as OF
+    T = seedgen.TID
+    n_c, W, k, B, P = w["n_c"], w["window"], w["top_k"], w["B"], w["pool"]
+    dev = "cuda" if torch.cuda.is_available() else "cpu"
+    s = w["seed"] * 1000
+    scale = 1.0 / math.sqrt(512)
+    qi = [seedgen.bf16_normal(s, seedgen.tid(T.Q_IDX, layer), (B, w["hi"], 128), dev)[:queries]
+          .float().cpu().double().numpy() for layer in range(w["layers"])]
+    wv = [seedgen.uniform01(s, seedgen.tid(T.W_IDX, layer), (B, w["hi"]), dev)[:queries]
+          .cpu().double().numpy() for layer in range(w["layers"])]
+    keys = bits(seedgen.bf16_normal(w["seed"], seedgen.tid(T.IDX_KEYS), (B, n_c, 128), dev)[:queries])
+    kds = [OF.fp4_dequantize(*OF.fp4_quantize(OF.bf16_bits_to_f64(keys[b]))) for b in range(queries)]
+    # Untimed: the rows each layer reads, encoded by the oracle's own encoders.
+    rows_enc = [[None] * queries for _ in range(w["layers"])]
+    for b in range(queries):
+        pool = OD.topk_indices(OD.indexer_scores(qi[0][b], wv[0][b], kds[b]), P)
+        for layer in range(w["layers"]):
+            sel = OD.reindex_topk(qi[layer][b], wv[layer][b], kds[b], pool, k)
+            kv_all = seedgen.kv_rows_bf16(w["seed"], seedgen.tid(T.KV, layer), (B, W + n_c, 512), dev)
+            need = np.concatenate([np.arange(W), W + sel[sel >= 0]])
+            rows_enc[layer][b] = encode(bits(kv_all[b, torch.from_numpy(need).to(kv_all.device)]))
+            del kv_all
+    t0 = time.perf_counter()
+    for b in range(queries):
+        pool = OD.topk_indices(OD.indexer_scores(qi[0][b], wv[0][b], kds[b]), P)
+        for layer in range(w["layers"]):
+            OD.reindex_topk(qi[layer][b], wv[layer][b], kds[b], pool, k)
+            OD.attention(qs[layer][b], decode(rows_enc[layer][b]), scale)
+    dt = time.perf_counter() - t0
+    return {"value": round(queries / dt, 4), "unit": "query-tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{queries} of the {B} query tokens of one step (same seeds and shapes): "
+                      f"{n_c} {w['idx']} indexer keys -> a {P}-row pool, then in each of "
+                      f"{w['layers']} layers the pool re-ranked to {k} and {W}+{k} {w['kv']} rows; "
                       f"numpy fp64, {dt:.1f} s"}
 
 
@@ -375,7 +469,8 @@ def main():
         "config": {"workload": args.workload, "batch": B, "context_tokens": w["context"],
                    "n_compressed": w["n_c"], "top_k": w["top_k"], "window": w["window"],
                    "q_heads": w["hq"], "idx_heads": w["hi"], "kv_format": w["kv"],
-                   "idx_format": w["idx"], "layers": w["layers"], "replicas": g["replicas"]},
+                   "idx_format": w["idx"], "layers": w["layers"], "replicas": g["replicas"],
+                   **({"pool": w["pool"]} if "pool" in w else {})},
         "hbm_gbps": round(step_gbps, 1),
         "algorithmic_bytes_per_step": g["bytes"]["step"],
         "roofline": {"bound": "hbm", "achieved": round(stage_gbps, 1), "peak": HBM_PEAK_GBPS,

@@ -90,6 +90,7 @@ class IndexerInputs:
     q_idx_values: np.ndarray  # [B][H_I][128] fp64
     w_values: np.ndarray      # [B][H_I] fp64
     certs: list
+    key_bits: dict            # checked query -> [N_c][128] bf16 source bits of the stored keys
 
 
 def make_indexer(seed: int, layer: int, B: int, n_c: int, hi: int, top_k: int, fmt: str,
@@ -123,7 +124,33 @@ def make_indexer(seed: int, layer: int, B: int, n_c: int, hi: int, top_k: int, f
         keep = (codes, scales)
     del keys
     return IndexerInputs(cache, keep, _dev(bf16_bits(qi).view(np.int16)), w.to(DEV), key_values,
-                         qv, wv, certs)
+                         qv, wv, certs, {b: adj[i] for i, b in enumerate(check)})
+
+
+def reindex_query(seed: int, layer: int, B: int, hi: int):
+    """A Reindex layer's indexer query and head weights: device tensors and fp64 values."""
+    qi = seedgen.bf16_normal(seed, seedgen.tid(T.Q_IDX, layer), (B, hi, DI))
+    w = seedgen.uniform01(seed, seedgen.tid(T.W_IDX, layer), (B, hi))
+    return (_dev(bf16_bits(qi).view(np.int16)), w.to(DEV), qi.double().numpy(),
+            w.double().numpy())
+
+
+def make_pool_tie_free(ix: IndexerInputs, b: int, pool_rows: np.ndarray, qv: np.ndarray,
+                       wv: np.ndarray, top_k: int, fmt: str):
+    """Make query b's keys tie-free inside its pool for a Reindex query (halving pool rows
+    as needed), and store the re-encoded rows in the device cache and the oracle's view."""
+    rows = np.sort(pool_rows[pool_rows >= 0])
+    adj, _ = tiefree.make_tie_free(ix.key_bits[b][rows][None], qv[None], wv[None], top_k, fmt)
+    ix.key_bits[b][rows] = adj[0]
+    idx = torch.from_numpy(rows).to(DEV)
+    if fmt == "bf16":
+        ix.keep[0][b, idx] = _dev(np.ascontiguousarray(adj[0]).view(np.uint8).reshape(len(rows), 256))
+        ix.key_values[b][rows] = OF.bf16_bits_to_f64(adj[0])
+    else:
+        c, s = OF.fp4_quantize(OF.bf16_bits_to_f64(adj[0]))
+        ix.keep[0][b, idx] = _dev(c)
+        ix.keep[1][b, idx] = _dev(s)
+        ix.key_values[b][rows] = OF.fp4_dequantize(c, s)
 
 
 def oracle_topk(ix: IndexerInputs, b: int, top_k: int) -> np.ndarray:

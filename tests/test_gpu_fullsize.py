@@ -9,8 +9,8 @@ import torch
 
 import compressed_sparse_kv_csa_amd as ck
 from cases import attention_error, topk_sets_equal
-from fullsize import (make_indexer, make_kv_cache, oracle_topk, query_bits, run_decode,
-                      bf16_out, scale_of, DEV)
+from fullsize import (make_indexer, make_kv_cache, make_pool_tie_free, oracle_topk, query_bits,
+                      reindex_query, run_decode, bf16_out, scale_of, DEV)
 from oracle import decode as OD
 
 pytestmark = [pytest.mark.gpu, pytest.mark.fullsize]
@@ -75,6 +75,50 @@ def test_csa2_stack_fp4_1m():
             print(f"reuse layer {layer} query {b}: max |out - oracle| = {err:.3e}", flush=True)
             assert ok, (layer, b, err)
         del kv
+
+
+def test_csa2_reindex_fp4_1m():
+    # Hierarchical indexer at the CSA2 workload: the Full layer selects a 1024-row pool over
+    # 262,144 FP4 keys; a Reindex layer re-ranks the pool with its own indexer query to 512
+    # rows and attends (REUSE) over its own FP4 cache.  8 tokens, queries 0 and 5 checked.
+    seed, B, n_c, W, hq, hi, P, k = 5, 8, 262144, 128, 64, 64, 1024, 512
+    check = [0, 5]
+    print(f"case: csa2 reindex seed={seed} B={B} Nc={n_c} pool={P} k={k} checked={check}", flush=True)
+    ix = make_indexer(seed, 0, B, n_c, hi, P, "fp4", check)
+    p = ck.CsaParams(B, 0, hi, P, 0, ck.MODE_FULL, 1.0, 0)
+    pool = torch.empty((B, P), dtype=torch.int32, device=DEV)
+    ws = torch.empty(max(ck.csa_select_topk_workspace_bytes(p, n_c), 256), dtype=torch.uint8, device=DEV)
+    ck.csa_select_topk(p, ix.cache, ix.q_idx, ix.w, pool, ws)
+    torch.cuda.synchronize()
+    pl = pool.cpu().numpy()
+    for b in check:
+        assert topk_sets_equal(pl[b:b + 1], oracle_topk(ix, b, P)[None]), f"pool of query {b}"
+    qi1, w1, qv1, wv1 = reindex_query(seed, 1, B, hi)
+    for b in check:
+        make_pool_tie_free(ix, b, pl[b], qv1[b], wv1[b], k, "fp4")
+    print("case: csa2 reindex layer 1 select", flush=True)
+    pr = ck.CsaParams(B, 0, hi, k, 0, ck.MODE_REINDEX, 1.0, 0)
+    tk = torch.empty((B, k), dtype=torch.int32, device=DEV)
+    ck.csa_reindex_topk(pr, ix.cache, qi1, w1, pool, P, tk)
+    torch.cuda.synchronize()
+    tkn = tk.cpu().numpy()
+    sel = {}
+    for b in check:
+        sel[b] = OD.reindex_topk(qv1[b], wv1[b], ix.key_values[b], pl[b], k)
+        assert topk_sets_equal(tkn[b:b + 1], sel[b][None]), f"reindexed top-k of query {b}"
+    print("case: csa2 reindex layer 1 attention", flush=True)
+    kv = make_kv_cache(seed, 1, B, W + n_c, "fp4")
+    q, qv = query_bits(seed, 1, B, hq)
+    ref = {}
+    for b in check:
+        rows = np.concatenate([np.arange(W), W + sel[b][sel[b] >= 0]])
+        ref[b] = OD.attention(qv[b], kv.put_oracle_rows(b, rows), scale_of())
+    out = bf16_out(run_decode(ck.CsaParams(B, hq, 0, k, W, ck.MODE_REUSE, scale_of(), 0), kv, None,
+                              q, tk, n_c))
+    for b in check:
+        err, ok = attention_error(out[b], ref[b])
+        print(f"reindex layer query {b}: max |out - oracle| = {err:.3e}", flush=True)
+        assert ok, (b, err)
 
 
 def test_hca_1m():
