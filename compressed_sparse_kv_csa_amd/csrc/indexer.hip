@@ -460,13 +460,9 @@ __device__ __forceinline__ int32_t key_index(uint64_t key) { return (int32_t)(~(
 // ------------------------------------------------------------------ key tiles
 
 // Lane (g, n) owns row n of a 16-row tile and 32 of its 128 channels.  Tiles are read
-// through buffer resources whose base is the tile's first row and whose size ends at the
-// workgroup's last row: a row past the end reads as zeros (no clamping, no fault), and
+// through buffer resources whose base is the tile's first row and whose size covers the
+// tile's rows that exist: a row past the end reads as zeros (no clamping, no fault), and
 // every lane's offset inside a tile is a constant.
-// Offsets inside a tile are small, so a remainder past 4 GiB is clamped, not wrapped.
-__device__ __forceinline__ Rsrc tile_rsrc(const uint8_t* base, int64_t bytes) {
-  return make_rsrc(base, bytes <= 0 ? 0u : bytes >= 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)bytes);
-}
 
 // bf16 rows: in K-step t the lane supplies channels 32t + 8g .. 32t + 8g + 7.
 struct KeyTileBf16 {
@@ -635,10 +631,13 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
   const uint8_t* kcodes = codes + seq_row0 * KT::kRowBytes;
   const uint8_t* kscales = KT::kScales ? scales + seq_row0 * (kIdxDim / 16) : nullptr;
   const int lane_co = KT::code_offset(n, g), lane_so = KT::scale_offset(n, g);
+  const int rows_wg = (int)rows_total;  // at most 512 slices of 4096 rows: 32-bit math
   auto load_slot = [&](KT& kt, int k) {
-    const int64_t r0 = (int64_t)__builtin_amdgcn_readfirstlane(slot_tile(k)) * 16;  // wave-uniform
-    const Rsrc rc = tile_rsrc(kcodes + r0 * KT::kRowBytes, (rows_total - r0) * KT::kRowBytes);
-    const Rsrc rs = KT::kScales ? tile_rsrc(kscales + r0 * (kIdxDim / 16), (rows_total - r0) * (kIdxDim / 16))
+    const int r0 = __builtin_amdgcn_readfirstlane(slot_tile(k)) * 16;  // wave-uniform
+    const int live = __builtin_amdgcn_readfirstlane(min(max(rows_wg - r0, 0), 16));  // rows that exist
+    const Rsrc rc = make_rsrc(kcodes + (int64_t)r0 * KT::kRowBytes, (uint32_t)(live * KT::kRowBytes));
+    const Rsrc rs = KT::kScales ? make_rsrc(kscales + (int64_t)r0 * (kIdxDim / 16),
+                                            (uint32_t)(live * (kIdxDim / 16)))
                                 : rc;
     kt.load(rc, rs, lane_co, lane_so);
   };
@@ -682,7 +681,7 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
       // Every lane stores (no branch, so a pass stays one basic block): the lanes of
       // group 0 holding a valid row store its score, the others a dummy slot.
       const int row = slot_tile(k) * 16 + n;  // within the workgroup's rows
-      const bool keep = g == 0 && row < rows_total;
+      const bool keep = g == 0 && row < rows_wg;
       s_score[keep ? (row & (kSliceRows - 1)) : kSliceRows + lane] = f32_order_key(sc);
     }
     if ((ps + 1) % kPassesPerSlice != 0 && ps + 1 < n_pass) continue;  // more passes in this slice
