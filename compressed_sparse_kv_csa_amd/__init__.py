@@ -16,8 +16,8 @@ __all__ = [
     "MODE_REUSE", "MODE_REINDEX", "CsaParams", "Cache", "KvCacheSpec", "KvCacheBreakdown", "lib", "lib_path",
     "cache", "csa_decode_workspace_bytes", "csa_decode", "csa_select_topk_workspace_bytes",
     "csa_select_topk", "csa_reindex_topk", "hca_decode_workspace_bytes",
-    "hca_decode", "kv_quantize_fp4", "kv_quantize_fp8", "kv_dequantize", "kv_cache_bytes",
-    "csakv_status_string", "EXPORTED_SYMBOLS",
+    "hca_decode", "kv_quantize_fp4", "kv_quantize_fp8", "kv_cache_write", "kv_dequantize",
+    "kv_cache_bytes", "csakv_status_string", "EXPORTED_SYMBOLS",
 ]
 
 KV_BF16, KV_FP8_MIXED, KV_FP4 = 0, 1, 2
@@ -29,7 +29,7 @@ OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 EXPORTED_SYMBOLS = (
     "csa_decode_workspace_bytes", "csa_decode", "csa_select_topk_workspace_bytes",
     "csa_select_topk", "csa_reindex_topk", "hca_decode_workspace_bytes", "hca_decode",
-    "kv_quantize_fp4", "kv_quantize_fp8", "kv_dequantize", "kv_cache_bytes",
+    "kv_quantize_fp4", "kv_quantize_fp8", "kv_cache_write", "kv_dequantize", "kv_cache_bytes",
     "csakv_status_string",
 )
 
@@ -104,6 +104,8 @@ def lib() -> ctypes.CDLL:
         L.kv_quantize_fp4.restype = I32
         L.kv_quantize_fp8.argtypes = [VP, I64, I32, I32, VP, VP]
         L.kv_quantize_fp8.restype = I32
+        L.kv_cache_write.argtypes = [I32, I32, VP, VP, I64, I64, I32, I32, VP, VP, VP]
+        L.kv_cache_write.restype = I32
         L.kv_dequantize.argtypes = [I32, VP, VP, I64, I32, VP, VP]
         L.kv_dequantize.restype = I32
         L.kv_cache_bytes.argtypes = [P(KvCacheSpec), I64, P(KvCacheBreakdown)]
@@ -220,6 +222,15 @@ def kv_quantize_fp8(x, rows: int, dim: int, nope_dim: int, out, stream=None, che
                                _stream(stream))
     if check:
         _check(st, "kv_quantize_fp8")
+    return st
+
+
+def kv_cache_write(fmt: int, dim: int, codes, scales, seq_stride_rows: int, n_rows: int, batch: int,
+                   n: int, x, dst, stream=None, check: bool = True) -> int:
+    st = lib().kv_cache_write(int(fmt), int(dim), _ptr(codes), _ptr(scales), int(seq_stride_rows),
+                              int(n_rows), int(batch), int(n), _ptr(x), _ptr(dst), _stream(stream))
+    if check:
+        _check(st, "kv_cache_write")
     return st
 
 

@@ -12,6 +12,7 @@ namespace {
 
 constexpr int kKvDim = 512;
 constexpr int kNopeDim = 448;
+constexpr int kIdxDim = 128;
 constexpr size_t kWsAlign = 256;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -216,6 +217,25 @@ csakv_status hca_decode(int32_t batch, int32_t n_q_heads, float softmax_scale,
       kv->fmt, false, static_cast<const uint8_t*>(kv->codes), kv->scales, kv->seq_stride_rows,
       kv->n_rows, q, batch, n_q_heads, softmax_scale, nullptr, 0, 0, a, workspace, out,
       static_cast<hipStream_t>(stream)));
+}
+
+csakv_status kv_cache_write(int32_t fmt, int32_t dim, void* codes, uint8_t* scales,
+                            int64_t seq_stride_rows, int64_t n_rows, int32_t batch, int32_t n,
+                            const uint16_t* x, const int32_t* dst, void* stream) {
+  if (fmt < CSAKV_KV_BF16 || fmt > CSAKV_KV_FP4) return CSAKV_ERR_INVALID;
+  if (dim == kIdxDim) {
+    if (fmt == CSAKV_KV_FP8_MIXED) return CSAKV_ERR_UNSUPPORTED;
+  } else if (dim != kKvDim) {
+    return CSAKV_ERR_UNSUPPORTED;
+  }
+  if (batch < 1 || n < 0 || n_rows < 0 || seq_stride_rows < n_rows) return CSAKV_ERR_INVALID;
+  if (n == 0 || n_rows == 0) return CSAKV_OK;
+  if (!codes || !x || !dst || !aligned(codes, 16) || !aligned(x, 16) || !aligned(dst, 4))
+    return CSAKV_ERR_INVALID;
+  if ((fmt == CSAKV_KV_FP4) != (scales != nullptr)) return CSAKV_ERR_INVALID;
+  if (n_rows > INT32_MAX) return CSAKV_ERR_UNSUPPORTED;
+  return hip_status(csakv::launch_cache_write(fmt, dim, codes, scales, seq_stride_rows, n_rows,
+                                              batch, n, x, dst, static_cast<hipStream_t>(stream)));
 }
 
 csakv_status kv_quantize_fp4(const uint16_t* x, int64_t rows, int32_t dim, uint8_t* codes,

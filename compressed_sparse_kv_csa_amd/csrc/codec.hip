@@ -16,6 +16,43 @@ namespace csakv {
 
 namespace {
 
+// One 16-channel block of bf16 values (two 16-byte words) -> 8 bytes of FP4 codes and
+// the E4M3 scale byte.
+__device__ __forceinline__ void fp4_block(u32x4 w0, u32x4 w1, u32x2* codes, uint32_t* scale) {
+  uint32_t w[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+    v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const uint32_t sc = f32_to_e4m3(amax / 6.0f);
+  const float s = e4m3_to_f32(sc);
+  uint32_t packed[2] = {0u, 0u};
+  if (s != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) packed[i >> 3] |= f32_to_e2m1(v[i] / s) << (4 * (i & 7));
+  }
+  *codes = u32x2{packed[0], packed[1]};
+  *scale = sc;
+}
+
+// 16 bf16 values -> 16 E4M3FN bytes.
+__device__ __forceinline__ u32x4 e4m3_block(u32x4 w0, u32x4 w1) {
+  uint32_t w[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+  uint32_t o[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t lo = f32_to_e4m3(bf16_to_f32(w[i] & 0xFFFFu));
+    const uint32_t hi = f32_to_e4m3(bf16_to_f32(w[i] >> 16));
+    o[i >> 1] |= (lo | (hi << 8)) << (16 * (i & 1));
+  }
+  return u32x4{o[0], o[1], o[2], o[3]};
+}
+
 __global__ __launch_bounds__(256) void quantize_fp4_kernel(const uint16_t* __restrict__ x,
                                                            int64_t n_blocks,
                                                            uint8_t* __restrict__ codes,
@@ -23,25 +60,10 @@ __global__ __launch_bounds__(256) void quantize_fp4_kernel(const uint16_t* __res
   for (int64_t blk = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; blk < n_blocks;
        blk += (int64_t)gridDim.x * blockDim.x) {
     const u32x4* src = reinterpret_cast<const u32x4*>(x + blk * 16);
-    u32x4 w0 = src[0], w1 = src[1];
-    uint32_t w[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-    float v[16];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
-      v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    uint32_t sc = f32_to_e4m3(amax / 6.0f);
-    float s = e4m3_to_f32(sc);
-    uint32_t packed[2] = {0u, 0u};
-    if (s != 0.0f) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) packed[i >> 3] |= f32_to_e2m1(v[i] / s) << (4 * (i & 7));
-    }
-    reinterpret_cast<u32x2*>(codes)[blk] = u32x2{packed[0], packed[1]};
+    u32x2 c;
+    uint32_t sc;
+    fp4_block(src[0], src[1], &c, &sc);
+    reinterpret_cast<u32x2*>(codes)[blk] = c;
     scales[blk] = (uint8_t)sc;
   }
 }
@@ -60,19 +82,56 @@ __global__ __launch_bounds__(256) void quantize_fp8_mixed_kernel(const uint16_t*
     u32x4 w0 = src[0], w1 = src[1];
     uint8_t* dst_row = out + r * row_bytes;
     if (16 * c < nope) {
-      uint32_t w[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-      uint32_t o[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint32_t lo = f32_to_e4m3(bf16_to_f32(w[i] & 0xFFFFu));
-        uint32_t hi = f32_to_e4m3(bf16_to_f32(w[i] >> 16));
-        o[i >> 1] |= (lo | (hi << 8)) << (16 * (i & 1));
-      }
-      *reinterpret_cast<u32x4*>(dst_row + 16 * c) = u32x4{o[0], o[1], o[2], o[3]};
+      *reinterpret_cast<u32x4*>(dst_row + 16 * c) = e4m3_block(w0, w1);
     } else {
       u32x4* dst = reinterpret_cast<u32x4*>(dst_row + nope + 2 * (16 * c - nope));
       dst[0] = w0;
       dst[1] = w1;
+    }
+  }
+}
+
+// Decode-step cache write: one thread per 16-channel block of the B x n new rows.  Row
+// r = b * n + i goes to cache row dst[r] of sequence b (skipped outside [0, n_rows)).
+// FMT is the cache format (0 bf16, 1 mixed with 448 E4M3 dims, 2 FP4).
+template <int FMT>
+__global__ __launch_bounds__(256) void cache_write_kernel(const uint16_t* __restrict__ x,
+                                                          const int32_t* __restrict__ dst,
+                                                          int64_t n_new, int n, int dim,
+                                                          int64_t seq_stride, int64_t n_rows,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
+  const int chunks = dim / 16;
+  const int64_t total = n_new * chunks;
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = t / chunks;
+    const int c = (int)(t - r * chunks);
+    const int32_t d = dst[r];
+    if (d < 0 || d >= n_rows) continue;
+    const int64_t row = (r / n) * seq_stride + d;
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + r * dim + 16 * c);
+    const u32x4 w0 = src[0], w1 = src[1];
+    if (FMT == 0) {
+      u32x4* out = reinterpret_cast<u32x4*>(codes + row * dim * 2 + 32 * c);
+      out[0] = w0;
+      out[1] = w1;
+    } else if (FMT == 1) {
+      constexpr int kNope = 448;
+      uint8_t* out = codes + row * (kNope + 2 * (512 - kNope));
+      if (16 * c < kNope) {
+        *reinterpret_cast<u32x4*>(out + 16 * c) = e4m3_block(w0, w1);
+      } else {
+        u32x4* o = reinterpret_cast<u32x4*>(out + kNope + 2 * (16 * c - kNope));
+        o[0] = w0;
+        o[1] = w1;
+      }
+    } else {
+      u32x2 cw;
+      uint32_t sc;
+      fp4_block(w0, w1, &cw, &sc);
+      *reinterpret_cast<u32x2*>(codes + row * (dim / 2) + 8 * c) = cw;
+      scales[row * (dim / 16) + c] = (uint8_t)sc;
     }
   }
 }
@@ -147,6 +206,23 @@ hipError_t launch_quantize_fp8_mixed(const uint16_t* x, int64_t rows, int dim, i
   if (work == 0) return hipSuccess;
   hipLaunchKernelGGL(quantize_fp8_mixed_kernel, dim3(grid_for(work, 256)), dim3(256), 0, stream, x,
                      rows, dim, nope, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_write(int fmt, int dim, void* codes, uint8_t* scales, int64_t seq_stride,
+                              int64_t n_rows, int batch, int n, const uint16_t* x,
+                              const int32_t* dst, hipStream_t stream) {
+  const int64_t n_new = (int64_t)batch * n;
+  const int64_t work = n_new * (dim / 16);
+  if (work == 0) return hipSuccess;
+  uint8_t* c = static_cast<uint8_t*>(codes);
+#define CSAKV_WRITE(F)                                                                         \
+  hipLaunchKernelGGL((cache_write_kernel<F>), dim3(grid_for(work, 256)), dim3(256), 0, stream, x, \
+                     dst, n_new, n, dim, seq_stride, n_rows, c, scales)
+  if (fmt == 0) CSAKV_WRITE(0);
+  else if (fmt == 1) CSAKV_WRITE(1);
+  else CSAKV_WRITE(2);
+#undef CSAKV_WRITE
   return hipGetLastError();
 }
 

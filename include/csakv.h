@@ -180,6 +180,24 @@ csakv_status kv_quantize_fp4(const uint16_t* x, int64_t rows, int32_t dim,
 csakv_status kv_quantize_fp8(const uint16_t* x, int64_t rows, int32_t dim,
                              int32_t nope_dim, uint8_t* out, void* stream);
 
+/* Decode-step cache write ("DeepSeek-V4 KV Cache 深度分析", section 二: a new entry is
+ * quantised on its way into the cache, its 448 no-RoPE dims to E4M3 and its 64 RoPE
+ * dims kept as bf16; section 十一: the compressed row is then written into the KV
+ * cache).  The n new rows of each sequence, x [B][n][dim] bf16, are encoded in `fmt`
+ * exactly as kv_quantize_fp8 / kv_quantize_fp4 do (bf16 rows are copied) and stored at
+ * row dst[b][i] of sequence b: byte (b * seq_stride_rows + dst[b][i]) * code_bytes of
+ * `codes`, and for FP4 byte (b * seq_stride_rows + dst[b][i]) * dim / 16 of `scales`.
+ *   fmt, dim  a csakv_kv_fmt with dim 512 (shared-KV rows), or CSAKV_KV_BF16 /
+ *             CSAKV_KV_FP4 with dim 128 (indexer-key rows: 256 B, or 64 code bytes
+ *             plus 8 scale bytes).
+ *   dst       [B][n] int32 rows: the ring slot of a new window token, or window + j for
+ *             new compressed entry j.  An entry outside [0, n_rows) writes nothing; two
+ *             entries naming one row of a sequence leave that row undefined.
+ * batch >= 1, n >= 0, n_rows <= seq_stride_rows; the library only writes the named rows. */
+csakv_status kv_cache_write(int32_t fmt, int32_t dim, void* codes, uint8_t* scales,
+                            int64_t seq_stride_rows, int64_t n_rows, int32_t batch, int32_t n,
+                            const uint16_t* x, const int32_t* dst, void* stream);
+
 /* Decode rows of any KV format back to bf16 (exact for every format):
  * fmt is csakv_kv_fmt; dim 512 for FP8_MIXED (nope 448), dim % 16 == 0 otherwise. */
 csakv_status kv_dequantize(int32_t fmt, const void* codes, const uint8_t* scales,

@@ -163,3 +163,21 @@ def test_reindex_rejects_bad_arguments():
     assert call(topk=FAKE + 1024) == ck.ERR_INVALID                       # output overlaps the pool
     huge = ck.Cache(ck.IDX_BF16, 0, 1 << 24, 1 << 24, FAKE, None)         # 4 GiB of keys
     assert call(idx=huge) == ck.ERR_UNSUPPORTED
+
+
+def test_cache_write_rejects_bad_arguments():
+    def call(fmt=ck.KV_BF16, dim=512, codes=FAKE, scales=None, stride=100, rows=100, B=1, n=2,
+             x=FAKE, dst=FAKE):
+        return ck.kv_cache_write(fmt, dim, codes, scales, stride, rows, B, n, x, dst, stream=0,
+                                 check=False)
+
+    assert call(fmt=3) == ck.ERR_INVALID
+    assert call(dim=256) == ck.ERR_UNSUPPORTED
+    assert call(fmt=ck.KV_FP8_MIXED, dim=128) == ck.ERR_UNSUPPORTED
+    assert call(fmt=ck.KV_FP4) == ck.ERR_INVALID                  # FP4 needs scales
+    assert call(scales=FAKE) == ck.ERR_INVALID                    # bf16 takes none
+    assert call(B=0) == ck.ERR_INVALID
+    assert call(stride=50) == ck.ERR_INVALID                      # stride < rows
+    assert call(codes=0) == ck.ERR_INVALID
+    assert call(x=FAKE + 2) == ck.ERR_INVALID                     # misaligned
+    assert call(n=0, codes=0) == ck.OK                            # nothing to write
