@@ -137,11 +137,14 @@ def fp4_quantize(x) -> tuple[np.ndarray, np.ndarray]:
     dim = x.shape[-1]
     assert dim % FP4_BLOCK == 0
     blocks = x.reshape(*x.shape[:-1], dim // FP4_BLOCK, FP4_BLOCK)
-    amax = np.abs(blocks).max(axis=-1)
-    scale_code = e4m3_encode(amax / E2M1_MAX)
+    blocks = blocks.astype(np.float32).astype(np.float64)  # the codec's inputs are fp32 values
+    amax = np.abs(blocks).max(axis=-1).astype(np.float32)
+    # Both divisions are single correctly rounded fp32 divisions; the quotient is then
+    # rounded to the E4M3 / E2M1 grid.
+    scale_code = e4m3_encode((amax / np.float32(E2M1_MAX)).astype(np.float64))
     scale = e4m3_value(scale_code)
     with np.errstate(divide="ignore", invalid="ignore"):
-        ratio = blocks / scale[..., None]
+        ratio = (blocks.astype(np.float32) / scale[..., None].astype(np.float32)).astype(np.float64)
     nib = e2m1_encode(ratio)
     nib = np.where((scale == 0.0)[..., None], 0, nib).astype(np.uint8)
     nib = nib.reshape(*x.shape[:-1], dim)
