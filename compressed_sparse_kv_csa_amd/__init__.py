@@ -12,16 +12,18 @@ import ctypes
 import os
 
 __all__ = [
-    "CsakvError", "KV_BF16", "KV_FP8_MIXED", "KV_FP4", "IDX_BF16", "IDX_FP4", "MODE_FULL",
+    "CsakvError", "KV_BF16", "KV_FP8_MIXED", "KV_FP4", "IDX_BF16", "IDX_FP4", "IDX_FP4_HADAMARD",
+    "MODE_FULL",
     "MODE_REUSE", "MODE_REINDEX", "CsaParams", "Cache", "KvCacheSpec", "KvCacheBreakdown", "lib", "lib_path",
     "cache", "csa_decode_workspace_bytes", "csa_decode", "csa_select_topk_workspace_bytes",
     "csa_select_topk", "csa_reindex_topk", "hca_decode_workspace_bytes",
-    "hca_decode", "kv_quantize_fp4", "kv_quantize_fp8", "kv_cache_write", "kv_dequantize",
+    "hca_decode", "kv_quantize_fp4", "kv_quantize_fp8", "idx_quantize_fp4_hadamard",
+    "kv_cache_write", "kv_dequantize",
     "kv_cache_bytes", "csakv_status_string", "EXPORTED_SYMBOLS",
 ]
 
 KV_BF16, KV_FP8_MIXED, KV_FP4 = 0, 1, 2
-IDX_BF16, IDX_FP4 = 0, 1
+IDX_BF16, IDX_FP4, IDX_FP4_HADAMARD = 0, 1, 2
 MODE_FULL, MODE_REUSE, MODE_REINDEX = 0, 1, 2
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
@@ -29,8 +31,8 @@ OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 EXPORTED_SYMBOLS = (
     "csa_decode_workspace_bytes", "csa_decode", "csa_select_topk_workspace_bytes",
     "csa_select_topk", "csa_reindex_topk", "hca_decode_workspace_bytes", "hca_decode",
-    "kv_quantize_fp4", "kv_quantize_fp8", "kv_cache_write", "kv_dequantize", "kv_cache_bytes",
-    "csakv_status_string",
+    "kv_quantize_fp4", "kv_quantize_fp8", "idx_quantize_fp4_hadamard", "kv_cache_write",
+    "kv_dequantize", "kv_cache_bytes", "csakv_status_string",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -104,6 +106,8 @@ def lib() -> ctypes.CDLL:
         L.kv_quantize_fp4.restype = I32
         L.kv_quantize_fp8.argtypes = [VP, I64, I32, I32, VP, VP]
         L.kv_quantize_fp8.restype = I32
+        L.idx_quantize_fp4_hadamard.argtypes = [VP, I64, VP, VP, VP]
+        L.idx_quantize_fp4_hadamard.restype = I32
         L.kv_cache_write.argtypes = [I32, I32, VP, VP, I64, I64, I32, I32, VP, VP, VP]
         L.kv_cache_write.restype = I32
         L.kv_dequantize.argtypes = [I32, VP, VP, I64, I32, VP, VP]
@@ -222,6 +226,14 @@ def kv_quantize_fp8(x, rows: int, dim: int, nope_dim: int, out, stream=None, che
                                _stream(stream))
     if check:
         _check(st, "kv_quantize_fp8")
+    return st
+
+
+def idx_quantize_fp4_hadamard(x, rows: int, codes, scales, stream=None, check: bool = True) -> int:
+    st = lib().idx_quantize_fp4_hadamard(_ptr(x), int(rows), _ptr(codes), _ptr(scales),
+                                         _stream(stream))
+    if check:
+        _check(st, "idx_quantize_fp4_hadamard")
     return st
 
 

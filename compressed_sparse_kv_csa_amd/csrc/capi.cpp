@@ -23,13 +23,13 @@ csakv_status hip_status(hipError_t e) { return e == hipSuccess ? CSAKV_OK : CSAK
 // Checks a cache descriptor: format, row counts, pointers and alignment.
 csakv_status check_cache(const csakv_cache* c, bool is_kv) {
   if (!c || c->reserved != 0) return CSAKV_ERR_INVALID;
-  const int nfmt = is_kv ? 3 : 2;
+  const int nfmt = 3;  // csakv_kv_fmt, or csakv_idx_fmt
   if (c->fmt < 0 || c->fmt >= nfmt) return CSAKV_ERR_INVALID;
   if (c->n_rows < 0 || c->seq_stride_rows < c->n_rows) return CSAKV_ERR_INVALID;
   // A cache without rows may have null pointers; any pointer given must be aligned.
   const bool empty = c->n_rows == 0;
   if ((!empty && !c->codes) || !aligned(c->codes, 16)) return CSAKV_ERR_INVALID;
-  const bool fp4 = is_kv ? c->fmt == CSAKV_KV_FP4 : c->fmt == CSAKV_IDX_FP4;
+  const bool fp4 = is_kv ? c->fmt == CSAKV_KV_FP4 : c->fmt != CSAKV_IDX_BF16;
   if (fp4) {
     if ((!empty && !c->scales) || !aligned(c->scales, 16)) return CSAKV_ERR_INVALID;
   } else if (c->scales) {
@@ -217,6 +217,15 @@ csakv_status hca_decode(int32_t batch, int32_t n_q_heads, float softmax_scale,
       kv->fmt, false, static_cast<const uint8_t*>(kv->codes), kv->scales, kv->seq_stride_rows,
       kv->n_rows, q, batch, n_q_heads, softmax_scale, nullptr, 0, 0, a, workspace, out,
       static_cast<hipStream_t>(stream)));
+}
+
+csakv_status idx_quantize_fp4_hadamard(const uint16_t* x, int64_t rows, uint8_t* codes,
+                                       uint8_t* scales, void* stream) {
+  if (rows < 0) return CSAKV_ERR_INVALID;
+  if (rows == 0) return CSAKV_OK;
+  if (!x || !codes || !scales || !aligned(x, 16) || !aligned(codes, 8)) return CSAKV_ERR_INVALID;
+  return hip_status(
+      csakv::launch_quantize_fp4h(x, rows, codes, scales, static_cast<hipStream_t>(stream)));
 }
 
 csakv_status kv_cache_write(int32_t fmt, int32_t dim, void* codes, uint8_t* scales,

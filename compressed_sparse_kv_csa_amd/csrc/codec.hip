@@ -19,25 +19,14 @@ namespace {
 // One 16-channel block of bf16 values (two 16-byte words) -> 8 bytes of FP4 codes and
 // the E4M3 scale byte.
 __device__ __forceinline__ void fp4_block(u32x4 w0, u32x4 w1, u32x2* codes, uint32_t* scale) {
-  uint32_t w[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+  const uint32_t w[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
   float v[16];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
     v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
   }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  const uint32_t sc = f32_to_e4m3(amax / 6.0f);
-  const float s = e4m3_to_f32(sc);
-  uint32_t packed[2] = {0u, 0u};
-  if (s != 0.0f) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) packed[i >> 3] |= f32_to_e2m1(v[i] / s) << (4 * (i & 7));
-  }
-  *codes = u32x2{packed[0], packed[1]};
-  *scale = sc;
+  fp4_block_f32(v, codes, scale);
 }
 
 // 16 bf16 values -> 16 E4M3FN bytes.
@@ -136,6 +125,40 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const uint16_t* __rest
   }
 }
 
+// Hadamard-rotated FP4 indexer keys: one thread per 128-wide bf16 row, rotated in
+// registers, then the FP4 block codec on the rotated values.
+__global__ __launch_bounds__(256) void quantize_fp4h_kernel(const uint16_t* __restrict__ x,
+                                                            int64_t rows,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales) {
+#pragma clang fp contract(off)
+  for (int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; r < rows;
+       r += (int64_t)gridDim.x * blockDim.x) {
+    float y[128];
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + r * 128);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const u32x4 w = src[k];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        y[8 * k + 2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
+        y[8 * k + 2 * j + 1] = bf16_to_f32(w[j] >> 16);
+      }
+    }
+    hadamard_stages<128>(y);
+#pragma unroll
+    for (int i = 0; i < 128; ++i) y[i] *= kHadamardScale;
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) {
+      u32x2 c;
+      uint32_t sc;
+      fp4_block_f32(y + 16 * blk, &c, &sc);
+      reinterpret_cast<u32x2*>(codes + r * 64)[blk] = c;
+      scales[r * 8 + blk] = (uint8_t)sc;
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void dequantize_kernel(int fmt, const uint8_t* __restrict__ codes,
                                                          const uint8_t* __restrict__ scales,
                                                          int64_t rows, int dim, int nope,
@@ -206,6 +229,14 @@ hipError_t launch_quantize_fp8_mixed(const uint16_t* x, int64_t rows, int dim, i
   if (work == 0) return hipSuccess;
   hipLaunchKernelGGL(quantize_fp8_mixed_kernel, dim3(grid_for(work, 256)), dim3(256), 0, stream, x,
                      rows, dim, nope, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp4h(const uint16_t* x, int64_t rows, uint8_t* codes, uint8_t* scales,
+                                hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_fp4h_kernel, dim3(grid_for(rows, 256)), dim3(256), 0, stream, x, rows,
+                     codes, scales);
   return hipGetLastError();
 }
 

@@ -81,6 +81,47 @@ __device__ __forceinline__ uint32_t f32_to_e2m1(float r) {
   return sign | c;
 }
 
+// One 16-channel block of fp32 values -> FP4 codes (element 2i in the low nibble of
+// byte i) and the E4M3 scale byte: scale = E4M3(amax / 6), code = E2M1(x / scale), both
+// divisions single fp32 divisions; all codes 0 when the scale decodes to 0.
+__device__ __forceinline__ void fp4_block_f32(const float* v, u32x2* codes, uint32_t* scale) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const uint32_t sc = f32_to_e4m3(amax / 6.0f);
+  const float s = e4m3_to_f32(sc);
+  uint32_t packed[2] = {0u, 0u};
+  if (s != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) packed[i >> 3] |= f32_to_e2m1(v[i] / s) << (4 * (i & 7));
+  }
+  *codes = u32x2{packed[0], packed[1]};
+  *scale = sc;
+}
+
+// ---------------------------------------------------------------- Hadamard rotation
+
+// The indexer's 128-wide Hadamard rotation, H x / sqrt(128) with H the Sylvester matrix,
+// computed as the fast transform in one fixed order (each step one fp32 rounding): for
+// h = 1, 2, ..., 64 every pair (i, i + h) with bit h of i clear becomes
+// (x[i] + x[i+h], x[i] - x[i+h]); then every element is scaled by fp32(1/sqrt(128)).
+constexpr float kHadamardScale = 0x1.6a09e6p-4f;  // fp32(1 / sqrt(128))
+
+// The in-register stages h = 1 .. N/2 of N consecutive channels.
+template <int N>
+__device__ __forceinline__ void hadamard_stages(float* y) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int h = 1; h < N; h *= 2)
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if ((i & h) == 0) {
+        const float a = y[i], b = y[i + h];
+        y[i] = a + b;
+        y[i + h] = a - b;
+      }
+}
+
 // ---------------------------------------------------------------- FP4 block decode
 
 // Eight E2M1 codes (one dword, element 2i in the low nibble of byte i) times the block

@@ -11,6 +11,8 @@ hipError_t launch_quantize_fp4(const uint16_t* x, int64_t rows, int dim, uint8_t
                                uint8_t* scales, hipStream_t stream);
 hipError_t launch_quantize_fp8_mixed(const uint16_t* x, int64_t rows, int dim, int nope,
                                      uint8_t* out, hipStream_t stream);
+hipError_t launch_quantize_fp4h(const uint16_t* x, int64_t rows, uint8_t* codes, uint8_t* scales,
+                                hipStream_t stream);
 hipError_t launch_cache_write(int fmt, int dim, void* codes, uint8_t* scales, int64_t seq_stride,
                               int64_t n_rows, int batch, int n, const uint16_t* x,
                               const int32_t* dst, hipStream_t stream);

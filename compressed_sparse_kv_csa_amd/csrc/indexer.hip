@@ -539,13 +539,70 @@ __device__ __forceinline__ f16x8 q_operand(u32x4 v, float scale, f16x8*) {
 // Query b's indexer query fragments (A operand: head n of each 16-head tile, the lane's
 // K-channels) and the weights of the accumulator rows lane (g, n) holds (heads
 // 16*ht + 4g + i); heads past n_heads get zeros.
-template <class KT, int HT>
-__device__ __forceinline__ void query_frags(const uint16_t* __restrict__ q_idx,
-                                            const float* __restrict__ w_idx, int b, int n_heads,
-                                            int g, int n, typename KT::Op (&qa)[HT][4],
-                                            float (&wv)[HT][4]) {
-  typedef typename KT::Op Op;
-  u32x4 qraw[HT][4];
+// 8 FP4 codes (one dword) times their E4M3 scale, as exact fp16 values.
+__device__ __forceinline__ f16x8 fp4x8_to_f16(uint32_t cw, uint32_t scale_code) {
+  const uint32_t sp = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scale_code, 1.0f, false));
+  const f16x2 sc = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(sp, sp, 0x01000100u));
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 0) * sc);
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1) * sc);
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2) * sc);
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 3) * sc);
+  return as_f16x8(r);
+}
+
+// Hadamard-rotated FP4 indexer queries (keys stored in the same form): the 4 lanes g of
+// head n's row hold its channels 32g .. 32g+31; they rotate the row together (stages
+// h = 1..16 in registers, h = 32 and 64 across lanes g ^ 1 and g ^ 2, in that order, as
+// the codec does), quantise their two 16-channel blocks with the FP4 codec, and keep the
+// decoded values (exact in fp16) as the A operand in the FP4 key tile's channel order.
+template <int HT>
+__device__ __forceinline__ void query_frags_fp4h(const uint16_t* __restrict__ q_idx, int b,
+                                                 int n_heads, int g, int n, f16x8 (&qa)[HT][4]) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const int head = 16 * ht + n;
+    float y[32];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (head < n_heads)
+        v = *reinterpret_cast<const u32x4*>(q_idx + ((int64_t)b * n_heads + head) * kIdxDim + 32 * g + 8 * k);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        y[8 * k + 2 * j] = bf16_to_f32(v[j] & 0xFFFFu);
+        y[8 * k + 2 * j + 1] = bf16_to_f32(v[j] >> 16);
+      }
+    }
+    hadamard_stages<32>(y);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {  // h = 32: channel pairs (i, i + 32) live in lanes g, g ^ 1
+      const float p = __shfl_xor(y[j], 16);
+      y[j] = (g & 1) ? p - y[j] : y[j] + p;
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {  // h = 64: lanes g, g ^ 2
+      const float p = __shfl_xor(y[j], 32);
+      y[j] = (g & 2) ? p - y[j] : y[j] + p;
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) y[j] *= kHadamardScale;
+    u32x2 c0, c1;
+    uint32_t s0, s1;
+    fp4_block_f32(y, &c0, &s0);
+    fp4_block_f32(y + 16, &c1, &s1);
+    qa[ht][0] = fp4x8_to_f16(c0[0], s0);
+    qa[ht][1] = fp4x8_to_f16(c0[1], s0);
+    qa[ht][2] = fp4x8_to_f16(c1[0], s1);
+    qa[ht][3] = fp4x8_to_f16(c1[1], s1);
+  }
+}
+
+// The head weights of the accumulator rows lane (g, n) holds (heads 16*ht + 4g + i).
+template <int HT>
+__device__ __forceinline__ void query_weights(const float* __restrict__ w_idx, int b, int n_heads,
+                                              int g, float (&wv)[HT][4]) {
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
@@ -553,6 +610,16 @@ __device__ __forceinline__ void query_frags(const uint16_t* __restrict__ q_idx,
       const int h = 16 * ht + 4 * g + i;
       wv[ht][i] = h < n_heads ? w_idx[(int64_t)b * n_heads + h] : 0.0f;
     }
+}
+
+template <class KT, int HT>
+__device__ __forceinline__ void query_frags(const uint16_t* __restrict__ q_idx,
+                                            const float* __restrict__ w_idx, int b, int n_heads,
+                                            int g, int n, typename KT::Op (&qa)[HT][4],
+                                            float (&wv)[HT][4]) {
+  typedef typename KT::Op Op;
+  u32x4 qraw[HT][4];
+  query_weights<HT>(w_idx, b, n_heads, g, wv);
   float qmax = 0.0f;
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
@@ -583,6 +650,21 @@ __device__ __forceinline__ void query_frags(const uint16_t* __restrict__ q_idx,
 
 }
 
+// The query fragments and head weights of query b; QH: Hadamard-rotated FP4 queries.
+template <class KT, int HT, bool QH>
+__device__ __forceinline__ void query_setup(const uint16_t* __restrict__ q_idx,
+                                            const float* __restrict__ w_idx, int b, int n_heads,
+                                            int g, int n, typename KT::Op (&qa)[HT][4],
+                                            float (&wv)[HT][4]) {
+  if constexpr (QH) {
+    static_assert(KT::kScales, "rotated FP4 queries meet rotated FP4 keys");
+    query_weights<HT>(w_idx, b, n_heads, g, wv);
+    query_frags_fp4h<HT>(q_idx, b, n_heads, g, n, qa);
+  } else {
+    query_frags<KT, HT>(q_idx, w_idx, b, n_heads, g, n, qa, wv);
+  }
+}
+
 // ------------------------------------------------------------------ scan kernel
 
 constexpr int kSubTiles = 16;                          // tiles per wave per unrolled pass
@@ -597,7 +679,7 @@ struct IndexerWs {
   uint32_t* scores;  // [B][n_c] score key of every row
 };
 
-template <class KT, int HT>
+template <class KT, int HT, bool QH>
 __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t seq_stride,
     int64_t n_c, const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx, int n_heads,
@@ -653,7 +735,7 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
   // Indexer query fragments and head weights.
   Op qa[HT][4];
   float wv[HT][4];
-  query_frags<KT, HT>(q_idx, w_idx, b, n_heads, g, n, qa, wv);
+  query_setup<KT, HT, QH>(q_idx, w_idx, b, n_heads, g, n, qa, wv);
 
   for (int ps = 0; ps < n_pass; ++ps) {
 #pragma unroll
@@ -843,7 +925,7 @@ constexpr int kReindexThreads = 512;
 constexpr int kReindexWaves = kReindexThreads / kWave;
 constexpr uint32_t kAbsentKeyOffset = kReindexMaxSeqBytes;
 
-template <class KT, int HT>
+template <class KT, int HT, bool QH>
 __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t seq_stride,
     int64_t n_c, const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
@@ -866,7 +948,7 @@ __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(
   }
   Op qa[HT][4];
   float wv[HT][4];
-  query_frags<KT, HT>(q_idx, w_idx, b, n_heads, g, n, qa, wv);
+  query_setup<KT, HT, QH>(q_idx, w_idx, b, n_heads, g, n, qa, wv);
   lds_barrier();
 
   const Rsrc rc = make_rsrc(codes + (int64_t)b * seq_stride * KT::kRowBytes,
@@ -952,13 +1034,13 @@ __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(
     if (s_val[p] >= kth && opos < (uint32_t)k1) out[opos++] = key_index(s_val[p]);
 }
 
-template <class KT>
+template <class KT, bool QH>
 void launch_reindex_ht(int ht, hipStream_t stream, const uint8_t* codes, const uint8_t* scales,
                        int64_t seq_stride, int64_t n_c, const uint16_t* q_idx, const float* w_idx,
                        int batch, int n_heads, const int32_t* pool, int n_pool, int top_k,
                        int32_t* topk) {
 #define CSAKV_REINDEX(H)                                                                        \
-  hipLaunchKernelGGL((reindex_kernel<KT, H>), dim3(batch), dim3(kReindexThreads), 0, stream,   \
+  hipLaunchKernelGGL((reindex_kernel<KT, H, QH>), dim3(batch), dim3(kReindexThreads), 0, stream,   \
                      codes, scales, seq_stride, n_c, q_idx, w_idx, n_heads, pool, n_pool, top_k, \
                      topk)
   switch (ht) {
@@ -970,22 +1052,22 @@ void launch_reindex_ht(int ht, hipStream_t stream, const uint8_t* codes, const u
 #undef CSAKV_REINDEX
 }
 
-template <class KT, int HT>
+template <class KT, int HT, bool QH>
 void launch_scan(hipStream_t stream, const uint8_t* codes, const uint8_t* scales,
                  int64_t seq_stride, int64_t n_c, const uint16_t* q_idx, const float* w_idx,
                  int batch, int n_heads, const IndexerPlan& plan, const IndexerWs& ws) {
-  hipLaunchKernelGGL((indexer_scan_kernel<KT, HT>), dim3(batch * plan.wg_per_query),
+  hipLaunchKernelGGL((indexer_scan_kernel<KT, HT, QH>), dim3(batch * plan.wg_per_query),
                      dim3(kScanThreads), 0, stream, codes, scales, seq_stride, n_c, q_idx, w_idx,
                      n_heads, plan.n_slices, plan.slices_per_wg, plan.wg_per_query, plan.prefix,
                      plan.cap, ws);
 }
 
-template <class KT>
+template <class KT, bool QH = false>
 void launch_scan_ht(int ht, hipStream_t stream, const uint8_t* codes, const uint8_t* scales,
                     int64_t seq_stride, int64_t n_c, const uint16_t* q_idx, const float* w_idx,
                     int batch, int n_heads, const IndexerPlan& plan, const IndexerWs& ws) {
 #define CSAKV_SCAN(H) \
-  launch_scan<KT, H>(stream, codes, scales, seq_stride, n_c, q_idx, w_idx, batch, n_heads, plan, ws)
+  launch_scan<KT, H, QH>(stream, codes, scales, seq_stride, n_c, q_idx, w_idx, batch, n_heads, plan, ws)
   switch (ht) {
     case 1: CSAKV_SCAN(1); break;
     case 2: CSAKV_SCAN(2); break;
@@ -1059,9 +1141,12 @@ hipError_t launch_indexer(int key_fmt, const uint8_t* codes, const uint8_t* scal
     if (key_fmt == 0)
       launch_scan_ht<KeyTileBf16>(ht, stream, codes, scales, seq_stride, n_c, q_idx, w_idx, batch,
                                   n_heads, plan, ws);
-    else
+    else if (key_fmt == 1)
       launch_scan_ht<KeyTileFp4>(ht, stream, codes, scales, seq_stride, n_c, q_idx, w_idx, batch,
                                  n_heads, plan, ws);
+    else  // Hadamard-rotated FP4 keys: the query is rotated and quantised the same way
+      launch_scan_ht<KeyTileFp4, true>(ht, stream, codes, scales, seq_stride, n_c, q_idx, w_idx,
+                                       batch, n_heads, plan, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1081,11 +1166,14 @@ hipError_t launch_reindex(int key_fmt, const uint8_t* codes, const uint8_t* scal
                           int n_pool, int top_k, int32_t* topk, hipStream_t stream) {
   const int ht = (n_heads + 15) / 16;
   if (key_fmt == 0)
-    launch_reindex_ht<KeyTileBf16>(ht, stream, codes, scales, seq_stride, n_c, q_idx, w_idx,
-                                   batch, n_heads, pool, n_pool, top_k, topk);
+    launch_reindex_ht<KeyTileBf16, false>(ht, stream, codes, scales, seq_stride, n_c, q_idx, w_idx,
+                                          batch, n_heads, pool, n_pool, top_k, topk);
+  else if (key_fmt == 1)
+    launch_reindex_ht<KeyTileFp4, false>(ht, stream, codes, scales, seq_stride, n_c, q_idx, w_idx,
+                                         batch, n_heads, pool, n_pool, top_k, topk);
   else
-    launch_reindex_ht<KeyTileFp4>(ht, stream, codes, scales, seq_stride, n_c, q_idx, w_idx,
-                                  batch, n_heads, pool, n_pool, top_k, topk);
+    launch_reindex_ht<KeyTileFp4, true>(ht, stream, codes, scales, seq_stride, n_c, q_idx, w_idx,
+                                        batch, n_heads, pool, n_pool, top_k, topk);
   return hipGetLastError();
 }
 

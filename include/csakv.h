@@ -61,8 +61,12 @@ typedef enum { CSAKV_KV_BF16 = 0, CSAKV_KV_FP8_MIXED = 1, CSAKV_KV_FP4 = 2 } csa
 
 /* Storage formats of 128-wide indexer-key rows: BF16 256 bytes; FP4 64 code bytes
  * plus 8 scale bytes in a separate scale plane ("DeepSeek-V4 KV Cache 深度分析",
- * section 四: indexer keys are cached in FP4). */
-typedef enum { CSAKV_IDX_BF16 = 0, CSAKV_IDX_FP4 = 1 } csakv_idx_fmt;
+ * section 四: indexer keys are cached in FP4).  FP4_HADAMARD stores the same bytes for
+ * the FP4 codes of each row's Hadamard rotation (section 四, 结构: a Hadamard rotation,
+ * then FP4 quantisation over all 128 dims; written by idx_quantize_fp4_hadamard); with
+ * it the indexer rotates and FP4-quantises each query row the same way before scoring,
+ * so the QK product is FP4 x FP4 (decoded exactly, accumulated in fp32). */
+typedef enum { CSAKV_IDX_BF16 = 0, CSAKV_IDX_FP4 = 1, CSAKV_IDX_FP4_HADAMARD = 2 } csakv_idx_fmt;
 
 /* Layer modes of CSA2 ("DeepSeek, KV 캐시를 토큰당 890바이트로 줄인 V4.1-Flash 공개",
  * section 핵심 내용; "KV cache 890 bajtów na token", section "Trzy mechanizmy zamiast
@@ -179,6 +183,17 @@ csakv_status kv_quantize_fp4(const uint16_t* x, int64_t rows, int32_t dim,
  * bf16 bytes of x[nope_dim..dim).  nope_dim % 16 == 0, dim % 16 == 0. */
 csakv_status kv_quantize_fp8(const uint16_t* x, int64_t rows, int32_t dim,
                              int32_t nope_dim, uint8_t* out, void* stream);
+
+/* Hadamard-rotated FP4 indexer keys ("DeepSeek-V4 KV Cache 深度分析", section 四, 结构):
+ * each bf16 row x [rows][128] is rotated to H x / sqrt(128), H the Sylvester Hadamard
+ * matrix, computed in fp32 as the fast transform in a fixed order (for h = 1, 2, ...,
+ * 64 each pair (i, i + h) with bit h of i clear becomes (y[i] + y[i+h], y[i] - y[i+h]),
+ * then every element times fp32(1/sqrt(128))), and the rotated row is FP4-quantised as
+ * kv_quantize_fp4 does: codes [rows][64], scales [rows][8].  The rows of a
+ * CSAKV_IDX_FP4_HADAMARD cache.  A decode-step write points codes / scales at the
+ * destination row. */
+csakv_status idx_quantize_fp4_hadamard(const uint16_t* x, int64_t rows, uint8_t* codes,
+                                       uint8_t* scales, void* stream);
 
 /* Decode-step cache write ("DeepSeek-V4 KV Cache 深度分析", section 二: a new entry is
  * quantised on its way into the cache, its 448 no-RoPE dims to E4M3 and its 64 RoPE

@@ -165,6 +165,38 @@ def fp4_dequantize(codes, scales) -> np.ndarray:
     return v * s
 
 
+# ---------------------------------------------------------------- Hadamard-rotated FP4
+
+HADAMARD_DIM = 128
+
+
+def hadamard128_f32(x) -> np.ndarray:
+    """Rows x[..., 128] -> H x / sqrt(128) in fp32, H the Sylvester Hadamard matrix
+    ("DeepSeek-V4 KV Cache 深度分析", section 四, 结构: the indexer rotates its 128-wide
+    vectors with a Hadamard transform before FP4 quantisation).
+
+    Computed as the fast transform in a fixed order, every operation one fp32 rounding:
+    for h = 1, 2, 4, ..., 64, each pair (i, i + h) with bit h of i clear becomes
+    (x[i] + x[i+h], x[i] - x[i+h]); then every element is multiplied by fp32(1/sqrt(128)).
+    """
+    y = np.asarray(x, dtype=np.float32).copy()
+    lead = y.shape[:-1]
+    assert y.shape[-1] == HADAMARD_DIM
+    h = 1
+    while h < HADAMARD_DIM:
+        v = y.reshape(*lead, HADAMARD_DIM // (2 * h), 2, h)
+        a, b = v[..., 0, :], v[..., 1, :]
+        y = np.stack([a + b, a - b], axis=-2).reshape(*lead, HADAMARD_DIM)
+        h *= 2
+    return y * np.float32(1.0 / np.sqrt(HADAMARD_DIM))
+
+
+def fp4h_quantize(x_bf16_bits) -> tuple[np.ndarray, np.ndarray]:
+    """bf16 rows [..., 128] -> FP4 block codes and scales of their Hadamard rotation."""
+    rot = hadamard128_f32(bf16_bits_to_f64(x_bf16_bits))
+    return fp4_quantize(rot.astype(np.float64))
+
+
 # ---------------------------------------------------------------- mixed FP8 / BF16 row
 
 NOPE_DIM = 448

@@ -34,6 +34,9 @@ def _decode_keys(bits: np.ndarray, fmt: str) -> np.ndarray:
     if fmt == "fp4":
         codes, scales = formats.fp4_quantize(vals)
         return formats.fp4_dequantize(codes, scales)
+    if fmt == "fp4h":  # FP4 codes of the Hadamard rotation (halving the source halves them too)
+        codes, scales = formats.fp4h_quantize(bits)
+        return formats.fp4_dequantize(codes, scales)
     raise ValueError(fmt)
 
 
@@ -41,7 +44,8 @@ def make_tie_free(key_bits, q_idx, w_idx, top_k: int, fmt: str, max_iter: int = 
     """Return (adjusted key bf16 bits [B][N_c][d_I], certificates list).
 
     key_bits: uint16 bf16 bit patterns [B][N_c][d_I]; q_idx: [B][H_I][d_I] values;
-    w_idx: [B][H_I] values; fmt: "bf16" or "fp4" (the stored key format).
+    w_idx: [B][H_I] values; fmt: "bf16", "fp4" or "fp4h" (the stored key format; with "fp4h"
+    pass the queries as the indexer uses them, rotated and FP4-decoded).
     """
     keys = np.array(key_bits, dtype=np.uint16, copy=True)
     q_all = np.asarray(q_idx, dtype=np.float64)

@@ -168,3 +168,50 @@ def test_bf16_rounding_matches_torch():
     ours = F.f64_to_bf16_bits(f.astype(np.float64))
     ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(ours, ref)
+
+
+# ------------------------------------------------------------------ Hadamard-rotated FP4
+
+def test_hadamard_matches_the_textbook_matrix():
+    """Integer rows: the fast transform is exact, so H x / sqrt(128) equals scipy's
+    Sylvester matrix product rounded once to fp32."""
+    import scipy.linalg
+    rng = np.random.default_rng(51)
+    x = rng.integers(-8, 9, size=(20, 128)).astype(np.float64)
+    H = scipy.linalg.hadamard(128).astype(np.float64)
+    exact = (x @ H.T).astype(np.float32) * np.float32(1.0 / np.sqrt(128))
+    assert np.array_equal(F.hadamard128_f32(x), exact)
+
+
+def test_hadamard_is_orthonormal_and_an_involution():
+    rng = np.random.default_rng(52)
+    x = rng.standard_normal((50, 128)).astype(np.float32)
+    y = F.hadamard128_f32(x).astype(np.float64)
+    xx = x.astype(np.float64)
+    assert np.allclose((y * y).sum(1), (xx * xx).sum(1), rtol=1e-5)          # norms kept
+    assert np.allclose(F.hadamard128_f32(y), xx, atol=1e-5)                   # R(R(x)) = x
+    # basis vectors map to the Sylvester columns / sqrt(128)
+    e = np.zeros((1, 128)); e[0, 37] = 1.0
+    col = F.hadamard128_f32(e)[0] * np.sqrt(128)
+    assert set(np.round(col).tolist()) == {-1.0, 1.0} and np.round(col[0]) == 1.0
+
+
+def test_hadamard_butterfly_is_within_fp32_rounding_of_fp64():
+    import scipy.linalg
+    rng = np.random.default_rng(53)
+    x = F.bf16_bits_to_f64(F.f64_to_bf16_bits(rng.standard_normal((40, 128)) * 5))
+    ref = x @ scipy.linalg.hadamard(128).T / np.sqrt(128)
+    bound = 9 * 2.0 ** -24 * (np.abs(x).sum(1, keepdims=True) / np.sqrt(128))  # 7 adds + scale
+    assert (np.abs(F.hadamard128_f32(x) - ref) <= bound).all()
+
+
+def test_fp4h_is_the_fp4_codec_of_the_rotation():
+    rng = np.random.default_rng(54)
+    bits = F.f64_to_bf16_bits(rng.standard_normal((30, 128)))
+    c, s = F.fp4h_quantize(bits)
+    c2, s2 = F.fp4_quantize(F.hadamard128_f32(F.bf16_bits_to_f64(bits)).astype(np.float64))
+    assert np.array_equal(c, c2) and np.array_equal(s, s2)
+    # halving the source halves the rotation exactly: same codes, scale one binade lower
+    half = F.f64_to_bf16_bits(F.bf16_bits_to_f64(bits) / 2)
+    ch, sh = F.fp4h_quantize(half)
+    assert np.array_equal(F.fp4_dequantize(ch, sh) * 2, F.fp4_dequantize(c, s))
