@@ -42,6 +42,8 @@ WORKLOADS = {
     # (csa: layer 0 runs the indexer, layers 1.. reuse its top-k over their own caches)
     "csa_mixed_1m": dict(kind="csa", B=4, n_c=262144, window=128, hq=64, hi=64, top_k=512,
                          kv="mixed", idx="fp4", seed=4, context=1 << 20, layers=1),
+    "csa_fp4h_mixed_1m": dict(kind="csa", B=4, n_c=262144, window=128, hq=64, hi=64, top_k=512,
+                              kv="mixed", idx="fp4h", seed=7, context=1 << 20, layers=1),
     "csa_bf16_131k": dict(kind="csa", B=32, n_c=32768, window=128, hq=64, hi=64, top_k=512,
                           kv="bf16", idx="bf16", seed=2, context=131072, layers=1),
     "csa2_stack_fp4_1m": dict(kind="csa", B=8, n_c=262144, window=128, hq=64, hi=64, top_k=512,
@@ -61,7 +63,7 @@ KERNEL_SOURCES = [os.path.join(ROOT, "compressed_sparse_kv_csa_amd", "csrc", f)
 COPY_PROBE_ELEMS = 1 << 28  # float32 elements: 1 GiB read + 1 GiB written
 
 KV_ROW_BYTES = {"bf16": 1024, "mixed": 576, "fp4": 256 + 32}
-IDX_ROW_BYTES = {"bf16": 256, "fp4": 64 + 8}
+IDX_ROW_BYTES = {"bf16": 256, "fp4": 64 + 8, "fp4h": 64 + 8}
 
 
 def algorithmic_bytes(w: dict) -> dict:
@@ -113,10 +115,13 @@ def build_inputs(w: dict, replicas: int):
     k_codes = k_scales = None
     if w["kind"] in ("csa", "csa2r"):
         keys16 = seedgen.bf16_normal(w["seed"], seedgen.tid(T.IDX_KEYS), (B, n_c, 128), dev)
-        if w["idx"] == "fp4":
+        if w["idx"] in ("fp4", "fp4h"):
             k_codes = torch.empty((B, n_c, 64), dtype=torch.uint8, device=dev)
             k_scales = torch.empty((B, n_c, 8), dtype=torch.uint8, device=dev)
-            ck.kv_quantize_fp4(keys16, B * n_c, 128, k_codes, k_scales)
+            if w["idx"] == "fp4h":
+                ck.idx_quantize_fp4_hadamard(keys16, B * n_c, k_codes, k_scales)
+            else:
+                ck.kv_quantize_fp4(keys16, B * n_c, 128, k_codes, k_scales)
             del keys16
         else:
             k_codes = keys16
@@ -134,14 +139,14 @@ def build_inputs(w: dict, replicas: int):
             rep["q"].append(seedgen.bf16_normal(s, seedgen.tid(T.Q, layer), (B, w["hq"], 512), dev))
             rep["out"].append(torch.empty((B, w["hq"], 512), dtype=torch.bfloat16, device=dev))
         if w["kind"] == "csa":
-            idx_fmt = {"bf16": ck.IDX_BF16, "fp4": ck.IDX_FP4}[w["idx"]]
+            idx_fmt = {"bf16": ck.IDX_BF16, "fp4": ck.IDX_FP4, "fp4h": ck.IDX_FP4_HADAMARD}[w["idx"]]
             rep["kc"], rep["ks"] = cp(k_codes), cp(k_scales)
             rep["idx"] = ck.cache(idx_fmt, rep["kc"], n_c, n_c, rep["ks"])
             rep["qi"] = seedgen.bf16_normal(s, seedgen.tid(T.Q_IDX), (B, w["hi"], 128), dev)
             rep["w"] = seedgen.uniform01(s, seedgen.tid(T.W_IDX), (B, w["hi"]), dev)
             rep["topk"] = torch.empty((B, w["top_k"]), dtype=torch.int32, device=dev)
         if w["kind"] == "csa2r":
-            idx_fmt = {"bf16": ck.IDX_BF16, "fp4": ck.IDX_FP4}[w["idx"]]
+            idx_fmt = {"bf16": ck.IDX_BF16, "fp4": ck.IDX_FP4, "fp4h": ck.IDX_FP4_HADAMARD}[w["idx"]]
             rep["kc"], rep["ks"] = cp(k_codes), cp(k_scales)
             rep["idx"] = ck.cache(idx_fmt, rep["kc"], n_c, n_c, rep["ks"])
             rep["qi"] = [seedgen.bf16_normal(s, seedgen.tid(T.Q_IDX, layer), (B, w["hi"], 128), dev)
@@ -344,14 +349,23 @@ def run_cpu_baseline(w: dict, queries: int):
 
     qi = seedgen.bf16_normal(s, seedgen.tid(T.Q_IDX), (B, w["hi"], 128), dev)[:queries]
     wv = seedgen.uniform01(s, seedgen.tid(T.W_IDX), (B, w["hi"]), dev)[:queries]
-    qi = qi.float().cpu().double().numpy()
+    if w["idx"] == "fp4h":  # the queries as the indexer scores them: rotated, FP4, decoded
+        qi = OF.fp4_dequantize(*OF.fp4h_quantize(bits(qi)))
+    else:
+        qi = qi.float().cpu().double().numpy()
     wv = wv.cpu().double().numpy()
     keys = bits(seedgen.bf16_normal(w["seed"], seedgen.tid(T.IDX_KEYS), (B, n_c, 128), dev)[:queries])
+    fp4 = w["idx"] in ("fp4", "fp4h")
+
+    def key_codec(b):
+        if w["idx"] == "fp4h":
+            return OF.fp4h_quantize(keys[b])
+        return OF.fp4_quantize(OF.bf16_bits_to_f64(keys[b])) if fp4 else keys[b]
+
     key_enc, sels = [], []
     for b in range(queries):
-        vals = OF.bf16_bits_to_f64(keys[b])
-        kc = OF.fp4_quantize(vals) if w["idx"] == "fp4" else keys[b]
-        kd = OF.fp4_dequantize(*kc) if w["idx"] == "fp4" else vals
+        kc = key_codec(b)
+        kd = OF.fp4_dequantize(*kc) if fp4 else OF.bf16_bits_to_f64(kc)
         key_enc.append(kc)
         sels.append(OD.topk_indices(OD.indexer_scores(qi[b], wv[b], kd), k))
     rows_enc = [[None] * queries for _ in range(w["layers"])]
@@ -364,7 +378,7 @@ def run_cpu_baseline(w: dict, queries: int):
 
     t0 = time.perf_counter()
     for b in range(queries):
-        kd = OF.fp4_dequantize(*key_enc[b]) if w["idx"] == "fp4" else OF.bf16_bits_to_f64(key_enc[b])
+        kd = OF.fp4_dequantize(*key_enc[b]) if fp4 else OF.bf16_bits_to_f64(key_enc[b])
         OD.topk_indices(OD.indexer_scores(qi[b], wv[b], kd), k)
         for layer in range(w["layers"]):
             OD.attention(qs[layer][b], decode(rows_enc[layer][b]), scale)

@@ -551,18 +551,21 @@ __device__ __forceinline__ f16x8 fp4x8_to_f16(uint32_t cw, uint32_t scale_code) 
   return as_f16x8(r);
 }
 
-// Hadamard-rotated FP4 indexer queries (keys stored in the same form): the 4 lanes g of
-// head n's row hold its channels 32g .. 32g+31; they rotate the row together (stages
-// h = 1..16 in registers, h = 32 and 64 across lanes g ^ 1 and g ^ 2, in that order, as
-// the codec does), quantise their two 16-channel blocks with the FP4 codec, and keep the
-// decoded values (exact in fp16) as the A operand in the FP4 key tile's channel order.
+// Hadamard-rotated FP4 indexer queries (keys stored in the same form).  Wave ht of the
+// workgroup prepares head tile ht: the 4 lanes g of head n's row hold its channels
+// 32g .. 32g+31 and rotate the row together (stages h = 1..16 in registers, h = 32 and 64
+// across lanes g ^ 1 and g ^ 2, in that order, as the codec does), quantise their two
+// 16-channel blocks with the FP4 codec, and leave the decoded values (exact in fp16, in
+// the FP4 key tile's channel order) in LDS, from where every wave takes its A operands.
+// `stage` holds HT * 4 * 64 fragments; it is free again when this returns.
 template <int HT>
 __device__ __forceinline__ void query_frags_fp4h(const uint16_t* __restrict__ q_idx, int b,
-                                                 int n_heads, int g, int n, f16x8 (&qa)[HT][4]) {
+                                                 int n_heads, int wave, int g, int n,
+                                                 f16x8 (&qa)[HT][4], f16x8* stage) {
 #pragma clang fp contract(off)
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    const int head = 16 * ht + n;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (wave < HT) {
+    const int head = 16 * wave + n;
     float y[32];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -592,11 +595,18 @@ __device__ __forceinline__ void query_frags_fp4h(const uint16_t* __restrict__ q_
     uint32_t s0, s1;
     fp4_block_f32(y, &c0, &s0);
     fp4_block_f32(y + 16, &c1, &s1);
-    qa[ht][0] = fp4x8_to_f16(c0[0], s0);
-    qa[ht][1] = fp4x8_to_f16(c0[1], s0);
-    qa[ht][2] = fp4x8_to_f16(c1[0], s1);
-    qa[ht][3] = fp4x8_to_f16(c1[1], s1);
+    f16x8* out = stage + wave * 4 * kWave + lane;
+    out[0 * kWave] = fp4x8_to_f16(c0[0], s0);
+    out[1 * kWave] = fp4x8_to_f16(c0[1], s0);
+    out[2 * kWave] = fp4x8_to_f16(c1[0], s1);
+    out[3 * kWave] = fp4x8_to_f16(c1[1], s1);
   }
+  lds_barrier();
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) qa[ht][t] = stage[(ht * 4 + t) * kWave + lane];
+  lds_barrier();
 }
 
 // The head weights of the accumulator rows lane (g, n) holds (heads 16*ht + 4g + i).
@@ -651,15 +661,16 @@ __device__ __forceinline__ void query_frags(const uint16_t* __restrict__ q_idx,
 }
 
 // The query fragments and head weights of query b; QH: Hadamard-rotated FP4 queries.
+// QH needs every wave of the workgroup (barriers) and `stage`: LDS for HT * 256 fragments.
 template <class KT, int HT, bool QH>
 __device__ __forceinline__ void query_setup(const uint16_t* __restrict__ q_idx,
                                             const float* __restrict__ w_idx, int b, int n_heads,
-                                            int g, int n, typename KT::Op (&qa)[HT][4],
-                                            float (&wv)[HT][4]) {
+                                            int wave, int g, int n, typename KT::Op (&qa)[HT][4],
+                                            float (&wv)[HT][4], void* stage) {
   if constexpr (QH) {
     static_assert(KT::kScales, "rotated FP4 queries meet rotated FP4 keys");
     query_weights<HT>(w_idx, b, n_heads, g, wv);
-    query_frags_fp4h<HT>(q_idx, b, n_heads, g, n, qa);
+    query_frags_fp4h<HT>(q_idx, b, n_heads, wave, g, n, qa, static_cast<f16x8*>(stage));
   } else {
     query_frags<KT, HT>(q_idx, w_idx, b, n_heads, g, n, qa, wv);
   }
@@ -735,7 +746,8 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
   // Indexer query fragments and head weights.
   Op qa[HT][4];
   float wv[HT][4];
-  query_setup<KT, HT, QH>(q_idx, w_idx, b, n_heads, g, n, qa, wv);
+  static_assert(sizeof(uint32_t) * (kSliceRows + kWave) >= sizeof(f16x8) * 4 * 4 * kWave, "query stage");
+  query_setup<KT, HT, QH>(q_idx, w_idx, b, n_heads, wave, g, n, qa, wv, s_score);
 
   for (int ps = 0; ps < n_pass; ++ps) {
 #pragma unroll
@@ -948,7 +960,7 @@ __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(
   }
   Op qa[HT][4];
   float wv[HT][4];
-  query_setup<KT, HT, QH>(q_idx, w_idx, b, n_heads, g, n, qa, wv);
+  query_setup<KT, HT, QH>(q_idx, w_idx, b, n_heads, wave, g, n, qa, wv, s_val);
   lds_barrier();
 
   const Rsrc rc = make_rsrc(codes + (int64_t)b * seq_stride * KT::kRowBytes,

@@ -17,7 +17,7 @@ import seedgen
 from oracle import decode as OD, formats as OF, tiefree
 
 KV_FMTS = {"bf16": 0, "mixed": 1, "fp4": 2}
-IDX_FMTS = {"bf16": 0, "fp4": 1}
+IDX_FMTS = {"bf16": 0, "fp4": 1, "fp4h": 2}
 D, DI = 512, 128
 
 

@@ -99,6 +99,8 @@ def make_indexer(seed: int, layer: int, B: int, n_c: int, hi: int, top_k: int, f
     w = seedgen.uniform01(seed, seedgen.tid(T.W_IDX, layer), (B, hi))
     keys = seedgen.bf16_normal(seed, seedgen.tid(T.IDX_KEYS, layer), (B, n_c, DI), DEV)
     qv = qi.double().numpy()
+    if fmt == "fp4h":  # the queries as the indexer scores them: rotated, FP4, decoded
+        qv = OF.fp4_dequantize(*OF.fp4h_quantize(bf16_bits(qi)))
     wv = w.double().numpy()
     chk = np.array(check)
     sub = bf16_bits(keys[torch.from_numpy(chk).to(DEV)])
@@ -114,9 +116,13 @@ def make_indexer(seed: int, layer: int, B: int, n_c: int, hi: int, top_k: int, f
     else:
         codes = torch.empty((B, n_c, 64), dtype=torch.uint8, device=DEV)
         scales = torch.empty((B, n_c, 8), dtype=torch.uint8, device=DEV)
-        ck.kv_quantize_fp4(keys, B * n_c, DI, codes, scales)
+        if fmt == "fp4h":
+            ck.idx_quantize_fp4_hadamard(keys, B * n_c, codes, scales)
+        else:
+            ck.kv_quantize_fp4(keys, B * n_c, DI, codes, scales)
         for i, b in enumerate(check):
-            c, s = OF.fp4_quantize(OF.bf16_bits_to_f64(adj[i]))
+            c, s = (OF.fp4h_quantize(adj[i]) if fmt == "fp4h"
+                    else OF.fp4_quantize(OF.bf16_bits_to_f64(adj[i])))
             codes[b] = _dev(c)
             scales[b] = _dev(s)
             key_values[b] = OF.fp4_dequantize(c, s)

@@ -121,6 +121,12 @@ def test_csa2_reindex_fp4_1m():
         assert ok, (b, err)
 
 
+def test_csa_fp4h_mixed_1m():
+    # The 1M mixed workload with Hadamard-rotated FP4 indexer keys (the indexer rotates and
+    # FP4-quantises the queries itself); queries 0 and 3 checked.
+    _csa_full_layer(7, 4, 262144, 128, 64, 64, 512, "mixed", "fp4h", [0, 3], "csa fp4h mixed 1M")
+
+
 def test_hca_1m():
     # HCA: 1M tokens at ratio 128 -> 8192 entries + 128 window rows, bf16, 16 tokens
     seed, B, rows, hq = 3, 16, 8192 + 128, 64
