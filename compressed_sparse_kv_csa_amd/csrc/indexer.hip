@@ -622,57 +622,74 @@ __device__ __forceinline__ void query_weights(const float* __restrict__ w_idx, i
     }
 }
 
+
+// The query fragments and head weights of query b; QH: Hadamard-rotated FP4 queries.
+// bf16 indexer queries, prepared once per workgroup: wave ht loads head tile ht and its
+// largest magnitude; all waves then agree on the query's power-of-two scale (fp16 path),
+// wave ht converts its fragments into LDS, and every wave takes all of them.  `red` holds
+// HT floats, `stage` HT * 256 fragments; both are free again when this returns.
 template <class KT, int HT>
-__device__ __forceinline__ void query_frags(const uint16_t* __restrict__ q_idx,
-                                            const float* __restrict__ w_idx, int b, int n_heads,
-                                            int g, int n, typename KT::Op (&qa)[HT][4],
-                                            float (&wv)[HT][4]) {
+__device__ __forceinline__ void query_frags_staged(const uint16_t* __restrict__ q_idx, int b,
+                                                   int n_heads, int wave, int g, int n,
+                                                   typename KT::Op (&qa)[HT][4], u32x4* stage,
+                                                   float* red) {
   typedef typename KT::Op Op;
-  u32x4 qraw[HT][4];
-  query_weights<HT>(w_idx, b, n_heads, g, wv);
-  float qmax = 0.0f;
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    const int head = 16 * ht + n;
+  const int lane = threadIdx.x & (kWave - 1);
+  u32x4 raw[4];
+  if (wave < HT) {
+    const int head = 16 * wave + n;
+    float qmax = 0.0f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (head < n_heads)
         v = *reinterpret_cast<const u32x4*>(q_idx + ((int64_t)b * n_heads + head) * kIdxDim +
                                             KT::q_channel(g, t));
-      qraw[ht][t] = v;
+      raw[t] = v;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         qmax = fmaxf(qmax, fmaxf(fabsf(bf16_to_f32(v[i] & 0xFFFFu)), fabsf(bf16_to_f32(v[i] >> 16))));
     }
-  }
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, off));
+    for (int off = 32; off > 0; off >>= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, off));
+    if (lane == 0) red[wave] = qmax;
+  }
+  lds_barrier();
+  float qmax = red[0];
+#pragma unroll
+  for (int ht = 1; ht < HT; ++ht) qmax = fmaxf(qmax, red[ht]);
   // Power of two putting max|q| in [2^14, 2^15) (used by the fp16 path only).
   int p = 0;
   if (qmax > 0.0f) p = 14 - ((int)((__float_as_uint(qmax) >> 23) & 0xFF) - 127);
   p = max(-100, min(p, 100));
   const float qscale = __builtin_ldexpf(1.0f, p);
+  if (wave < HT) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      stage[(wave * 4 + t) * kWave + lane] = __builtin_bit_cast(u32x4, q_operand(raw[t], qscale, (Op*)nullptr));
+  }
+  lds_barrier();
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) qa[ht][t] = q_operand(qraw[ht][t], qscale, (Op*)nullptr);
-
+    for (int t = 0; t < 4; ++t) qa[ht][t] = __builtin_bit_cast(Op, stage[(ht * 4 + t) * kWave + lane]);
+  lds_barrier();
 }
 
-// The query fragments and head weights of query b; QH: Hadamard-rotated FP4 queries.
-// QH needs every wave of the workgroup (barriers) and `stage`: LDS for HT * 256 fragments.
+// The query fragments and head weights of query b, prepared once per workgroup (every
+// wave must call this: it holds barriers).  QH: Hadamard-rotated FP4 queries.  `stage`:
+// LDS for HT * 256 fragments; `red`: LDS for HT floats.
 template <class KT, int HT, bool QH>
 __device__ __forceinline__ void query_setup(const uint16_t* __restrict__ q_idx,
                                             const float* __restrict__ w_idx, int b, int n_heads,
                                             int wave, int g, int n, typename KT::Op (&qa)[HT][4],
-                                            float (&wv)[HT][4], void* stage) {
+                                            float (&wv)[HT][4], void* stage, float* red) {
+  query_weights<HT>(w_idx, b, n_heads, g, wv);
   if constexpr (QH) {
     static_assert(KT::kScales, "rotated FP4 queries meet rotated FP4 keys");
-    query_weights<HT>(w_idx, b, n_heads, g, wv);
     query_frags_fp4h<HT>(q_idx, b, n_heads, wave, g, n, qa, static_cast<f16x8*>(stage));
   } else {
-    query_frags<KT, HT>(q_idx, w_idx, b, n_heads, g, n, qa, wv);
+    query_frags_staged<KT, HT>(q_idx, b, n_heads, wave, g, n, qa, static_cast<u32x4*>(stage), red);
   }
 }
 
@@ -747,7 +764,8 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
   Op qa[HT][4];
   float wv[HT][4];
   static_assert(sizeof(uint32_t) * (kSliceRows + kWave) >= sizeof(f16x8) * 4 * 4 * kWave, "query stage");
-  query_setup<KT, HT, QH>(q_idx, w_idx, b, n_heads, wave, g, n, qa, wv, s_score);
+  query_setup<KT, HT, QH>(q_idx, w_idx, b, n_heads, wave, g, n, qa, wv, s_score,
+                          reinterpret_cast<float*>(sm.red32));
 
   for (int ps = 0; ps < n_pass; ++ps) {
 #pragma unroll
@@ -960,7 +978,8 @@ __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(
   }
   Op qa[HT][4];
   float wv[HT][4];
-  query_setup<KT, HT, QH>(q_idx, w_idx, b, n_heads, wave, g, n, qa, wv, s_val);
+  query_setup<KT, HT, QH>(q_idx, w_idx, b, n_heads, wave, g, n, qa, wv, s_val,
+                          reinterpret_cast<float*>(sm.red32));
   lds_barrier();
 
   const Rsrc rc = make_rsrc(codes + (int64_t)b * seq_stride * KT::kRowBytes,
