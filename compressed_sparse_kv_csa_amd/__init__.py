@@ -17,7 +17,7 @@ __all__ = [
     "MODE_REUSE", "MODE_REINDEX", "CsaParams", "Cache", "KvCacheSpec", "KvCacheBreakdown", "lib", "lib_path",
     "cache", "csa_decode_workspace_bytes", "csa_decode", "csa_select_topk_workspace_bytes",
     "csa_select_topk", "csa_reindex_topk", "hca_decode_workspace_bytes",
-    "hca_decode", "kv_quantize_fp4", "kv_quantize_fp8", "idx_quantize_fp4_hadamard",
+    "hca_decode", "rope_output", "kv_quantize_fp4", "kv_quantize_fp8", "idx_quantize_fp4_hadamard",
     "kv_cache_write", "kv_dequantize",
     "kv_cache_bytes", "csakv_status_string", "EXPORTED_SYMBOLS",
 ]
@@ -31,7 +31,7 @@ OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 EXPORTED_SYMBOLS = (
     "csa_decode_workspace_bytes", "csa_decode", "csa_select_topk_workspace_bytes",
     "csa_select_topk", "csa_reindex_topk", "hca_decode_workspace_bytes", "hca_decode",
-    "kv_quantize_fp4", "kv_quantize_fp8", "idx_quantize_fp4_hadamard", "kv_cache_write",
+    "rope_output", "kv_quantize_fp4", "kv_quantize_fp8", "idx_quantize_fp4_hadamard", "kv_cache_write",
     "kv_dequantize", "kv_cache_bytes", "csakv_status_string",
 )
 
@@ -106,6 +106,8 @@ def lib() -> ctypes.CDLL:
         L.kv_quantize_fp4.restype = I32
         L.kv_quantize_fp8.argtypes = [VP, I64, I32, I32, VP, VP]
         L.kv_quantize_fp8.restype = I32
+        L.rope_output.argtypes = [VP, I32, I32, VP, ctypes.c_double, VP]
+        L.rope_output.restype = I32
         L.idx_quantize_fp4_hadamard.argtypes = [VP, I64, VP, VP, VP]
         L.idx_quantize_fp4_hadamard.restype = I32
         L.kv_cache_write.argtypes = [I32, I32, VP, VP, I64, I64, I32, I32, VP, VP, VP]
@@ -226,6 +228,15 @@ def kv_quantize_fp8(x, rows: int, dim: int, nope_dim: int, out, stream=None, che
                                _stream(stream))
     if check:
         _check(st, "kv_quantize_fp8")
+    return st
+
+
+def rope_output(out, batch: int, n_heads: int, positions, base: float, stream=None,
+                check: bool = True) -> int:
+    st = lib().rope_output(_ptr(out), int(batch), int(n_heads), _ptr(positions), float(base),
+                           _stream(stream))
+    if check:
+        _check(st, "rope_output")
     return st
 
 

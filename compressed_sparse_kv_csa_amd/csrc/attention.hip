@@ -26,6 +26,8 @@
 #include "csakv_device.h"
 #include "csakv_launch.h"
 
+#include <algorithm>
+
 namespace csakv {
 
 namespace {
@@ -490,7 +492,44 @@ void launch_chunks(hipStream_t stream, const uint8_t* codes, const uint8_t* scal
 #undef CSAKV_CHUNK
 }
 
+// Output RoPE with position -i on the 64 RoPE dims of every output row, in place: one
+// thread per (query, head, pair k); pair (448 + 2k, 448 + 2k + 1) turns by angle
+// -position * base^(-2k/64).  The angle and its sine and cosine are computed in fp64
+// (positions reach 2^20 and beyond), the rotation in fp32, the result rounded to bf16.
+__global__ __launch_bounds__(256) void rope_output_kernel(uint16_t* __restrict__ out,
+                                                          int64_t n_items, int n_heads,
+                                                          const int64_t* __restrict__ positions,
+                                                          double base) {
+#pragma clang fp contract(off)
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n_items;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int k = (int)(t & 31);
+    const int64_t bh = t >> 5;
+    const int64_t b = bh / n_heads;
+    const double theta = pow(base, -2.0 * k / 64.0);
+    double sd, cd;
+    sincos(-(double)positions[b] * theta, &sd, &cd);
+    uint32_t* p = reinterpret_cast<uint32_t*>(out + bh * kDim + kNope + 2 * k);
+    const uint32_t w = *p;
+    const float x = bf16_to_f32(w & 0xFFFFu), y = bf16_to_f32(w >> 16);
+    const float c = (float)cd, sn = (float)sd;
+    const float rx = x * c - y * sn;
+    const float ry = x * sn + y * c;
+    *p = f32_to_bf16_rne(rx) | (f32_to_bf16_rne(ry) << 16);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_rope_output(uint16_t* out, int batch, int n_heads, const int64_t* positions,
+                              double base, hipStream_t stream) {
+  const int64_t items = (int64_t)batch * n_heads * 32;
+  if (items == 0) return hipSuccess;
+  const int64_t grid = std::min<int64_t>((items + 255) / 256, 4096);
+  hipLaunchKernelGGL(rope_output_kernel, dim3((unsigned)grid), dim3(256), 0, stream, out, items,
+                     n_heads, positions, base);
+  return hipGetLastError();
+}
 
 AttnPlan plan_attention(int batch, int64_t n_list, bool csa, int n_heads) {
   AttnPlan p{};

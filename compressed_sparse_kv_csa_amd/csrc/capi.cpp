@@ -219,6 +219,14 @@ csakv_status hca_decode(int32_t batch, int32_t n_q_heads, float softmax_scale,
       static_cast<hipStream_t>(stream)));
 }
 
+csakv_status rope_output(uint16_t* out, int32_t batch, int32_t n_heads, const int64_t* positions,
+                         double base, void* stream) {
+  if (batch < 1 || n_heads < 1 || !std::isfinite(base) || base <= 0.0) return CSAKV_ERR_INVALID;
+  if (!out || !positions || !aligned(out, 16) || !aligned(positions, 8)) return CSAKV_ERR_INVALID;
+  return hip_status(csakv::launch_rope_output(out, batch, n_heads, positions, base,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 csakv_status idx_quantize_fp4_hadamard(const uint16_t* x, int64_t rows, uint8_t* codes,
                                        uint8_t* scales, void* stream) {
   if (rows < 0) return CSAKV_ERR_INVALID;

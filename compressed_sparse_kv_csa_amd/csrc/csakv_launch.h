@@ -74,6 +74,8 @@ AttnPlan plan_attention(int batch, int64_t n_list, bool csa, int n_heads);
 bool attention_supported(const AttnPlan& plan, int kv_fmt, int64_t n_rows);
 size_t attention_workspace_bytes(int batch, int n_heads, const AttnPlan& plan);
 
+hipError_t launch_rope_output(uint16_t* out, int batch, int n_heads, const int64_t* positions,
+                              double base, hipStream_t stream);
 hipError_t launch_attention(int kv_fmt, bool csa, const uint8_t* codes, const uint8_t* scales,
                             int64_t seq_stride, int64_t n_rows, const uint16_t* q, int batch,
                             int n_heads, float softmax_scale, const int32_t* topk, int top_k,

@@ -171,6 +171,18 @@ csakv_status hca_decode(int32_t batch, int32_t n_q_heads, float softmax_scale,
                         const csakv_cache* kv, const uint16_t* q, uint16_t* out,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* Output RoPE with position -i ("DeepSeek-V4 KV Cache 深度分析", section 五: the core
+ * attention output o_{t,i} gets RoPE at position -i on its last 64 dims, which turns the
+ * absolute positions R(j) that the entries carry into relative positions R(j - i)).
+ * In place on out [B][n_heads][512] bf16 (for example csa_decode's or hca_decode's
+ * output): for query b, pair (448 + 2k, 448 + 2k + 1), k < 32, of every head turns by
+ * angle -positions[b] * base^(-2k/64), i.e. (x, y) -> (x cos - y sin, x sin + y cos).
+ * positions [B] int64 (device).  base > 0 (the pages give none; 10000 is customary).
+ * Angles, sines and cosines are fp64; the rotation is fp32, rounded to bf16 (nearest
+ * even). */
+csakv_status rope_output(uint16_t* out, int32_t batch, int32_t n_heads, const int64_t* positions,
+                         double base, void* stream);
+
 /* FP4 block quantisation of bf16 rows x [rows][dim] (dim % 16 == 0):
  * scale = E4M3FN(amax/6) per 16 channels (round to nearest even, saturating);
  * code  = E2M1(x / scale), or 0 for every element when the scale decodes to 0.

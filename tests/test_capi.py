@@ -181,3 +181,15 @@ def test_cache_write_rejects_bad_arguments():
     assert call(codes=0) == ck.ERR_INVALID
     assert call(x=FAKE + 2) == ck.ERR_INVALID                     # misaligned
     assert call(n=0, codes=0) == ck.OK                            # nothing to write
+
+
+def test_rope_output_rejects_bad_arguments():
+    def call(out=FAKE, B=2, H=64, pos=FAKE, base=10000.0):
+        return ck.rope_output(out, B, H, pos, base, stream=0, check=False)
+
+    assert call(B=0) == ck.ERR_INVALID
+    assert call(H=0) == ck.ERR_INVALID
+    assert call(base=0.0) == ck.ERR_INVALID
+    assert call(base=float("inf")) == ck.ERR_INVALID
+    assert call(out=0) == ck.ERR_INVALID
+    assert call(pos=FAKE + 4) == ck.ERR_INVALID
