@@ -228,14 +228,12 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
     int n_chunks, int n_pairs, float* __restrict__ part_o, float* __restrict__ part_ml) {
   constexpr int kTileElems = kStepRows * kPitch;
   constexpr int kTileBytes = NB * kTileElems * 2;
-  constexpr int kQBytes = 16 * kPitch * 2;
   constexpr int kOutBytes = 16 * kOutPitch * 4;
-  constexpr int kSmem = kTileBytes + kQBytes > kOutBytes ? kTileBytes + kQBytes : kOutBytes;
+  constexpr int kSmem = kTileBytes > kOutBytes ? kTileBytes : kOutBytes;
   __shared__ __attribute__((aligned(16))) uint8_t s_mem[kSmem];
   __shared__ __attribute__((aligned(16))) int s_rows[kMaxChunkRows + 2 * kStepRows];
   __shared__ __attribute__((aligned(16))) float s_logit[2][kStepRows][16];  // per K half
   uint16_t* const s_kv0 = reinterpret_cast<uint16_t*>(s_mem);
-  uint16_t* const s_q = reinterpret_cast<uint16_t*>(s_mem + kTileBytes);
   float* const s_out = reinterpret_cast<float*>(s_mem);
 
   int b, chunk, hg;
@@ -265,22 +263,19 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
     }
     s_rows[i] = row;
   }
-  // The group's 16 query rows as fp16 in LDS (B operand of the logits).
+  // The wave's logit B operands, kept in registers: wave w multiplies row tile w & 1
+  // over dims 256 * (w >> 1) .. +255, lane (g, n) supplying head n, dims
+  // 256 * (w >> 1) + 32t + 8g .. +7 of K-step t, as fp16.
+  f16x8 qf[8];
   {
-    constexpr int kQIters = 16 * (kDim / 8) / kAttnThreads;
-    u32x4 qv[kQIters];
-    const uint16_t* qb = q + ((int64_t)b * n_heads + 16 * hg) * kDim;
+    const uint16_t* qr = q + ((int64_t)b * n_heads + 16 * hg + n) * kDim + 256 * (wave >> 1) + 8 * g;
+    u32x4 qv[8];
 #pragma unroll
-    for (int k = 0; k < kQIters; ++k)
-      qv[k] = *reinterpret_cast<const u32x4*>(qb + 8 * (threadIdx.x + k * kAttnThreads));
+    for (int t = 0; t < 8; ++t) qv[t] = *reinterpret_cast<const u32x4*>(qr + 32 * t);
 #pragma unroll
-    for (int k = 0; k < kQIters; ++k) {
-      const int i = threadIdx.x + k * kAttnThreads;
-      const int h = i / (kDim / 8), c8 = i - h * (kDim / 8);
-      *reinterpret_cast<u32x4*>(s_q + h * kPitch + 8 * c8) =
-          u32x4{bf16x2_to_f16x2(qv[k][0]), bf16x2_to_f16x2(qv[k][1]), bf16x2_to_f16x2(qv[k][2]),
-                bf16x2_to_f16x2(qv[k][3])};
-    }
+    for (int t = 0; t < 8; ++t)
+      qf[t] = as_f16x8(u32x4{bf16x2_to_f16x2(qv[t][0]), bf16x2_to_f16x2(qv[t][1]),
+                             bf16x2_to_f16x2(qv[t][2]), bf16x2_to_f16x2(qv[t][3])});
   }
   lds_barrier();
 
@@ -318,13 +313,11 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
     // meet in LDS and every wave reads the full 32 x 16 block.
     {
       const int rt = wave & 1, kh = wave >> 1;
-      const uint16_t* qr = s_q + n * kPitch + 256 * kh + 8 * g;
       const uint16_t* kr = tile + (16 * rt + n) * kPitch + 256 * kh + 8 * g;
       f32x4 part = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < 8; ++t)
-        part = mfma16x16x32_f16(as_f16x8(*reinterpret_cast<const u32x4*>(kr + 32 * t)),
-                                as_f16x8(*reinterpret_cast<const u32x4*>(qr + 32 * t)), part);
+        part = mfma16x16x32_f16(as_f16x8(*reinterpret_cast<const u32x4*>(kr + 32 * t)), qf[t], part);
 #pragma unroll
       for (int i = 0; i < 4; ++i) s_logit[kh][16 * rt + 4 * g + i][n] = part[i];
     }

@@ -485,14 +485,15 @@ struct KeyTileBf16 {
   static __device__ __forceinline__ f32x4 mma(Op a, Op b, f32x4 c) { return mfma16x16x32(a, b, c); }
 };
 
-// FP4 rows: the lane loads channels 32g .. 32g + 31 (16 code bytes) and their two
-// scales; in K-step t it supplies channels 32g + 8t .. 32g + 8t + 7 as exact fp16.
+// FP4 rows: the lane loads channels 32g .. 32g + 31 (16 code bytes) and the dword of
+// scale bytes holding their two scales; in K-step t it supplies channels
+// 32g + 8t .. 32g + 8t + 7 as exact fp16.
 struct KeyTileFp4 {
   typedef f16x8 Op;
   u32x4 c;
-  uint32_t s;  // the dword of scale bytes holding blocks 2g and 2g + 1
-  int hi;      // 1 when those two bytes are the dword's upper half (odd g)
-  __device__ __forceinline__ void set_lane(int g) { hi = g & 1; }
+  uint32_t s;   // scales of blocks 4(g >> 1) .. 4(g >> 1) + 3, one byte each
+  uint32_t sh;  // 16 for odd g: the lane's two scale bytes are the dword's upper half
+  __device__ __forceinline__ void set_lane(int g) { sh = 16u * (g & 1); }
   static constexpr int kRowBytes = kIdxDim / 2;
   static constexpr bool kScales = true;
   static __device__ __forceinline__ int code_offset(int n, int g) { return n * kRowBytes + 16 * g; }
@@ -502,15 +503,11 @@ struct KeyTileFp4 {
     s = __builtin_amdgcn_raw_buffer_load_b32(rs, so, 0, 0);
   }
   __device__ __forceinline__ void decode(Op* op) const {
-    // Both E4M3 scales as an fp16 pair (exact), then each broadcast to a pair.
-    const uint32_t sp = __builtin_bit_cast(
-        uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 1.0f, true)
-                     : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 1.0f, false));
-    const uint32_t s0 = __builtin_amdgcn_perm(sp, sp, 0x01000100u);
-    const uint32_t s1 = __builtin_amdgcn_perm(sp, sp, 0x03020302u);
+    // Both E4M3 scales as an fp16 pair (exact); each multiply broadcasts one of them.
+    const f16x2 sp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s >> sh, 1.0f, false);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const f16x2 sc = __builtin_bit_cast(f16x2, t < 2 ? s0 : s1);
+      const f16x2 sc = t < 2 ? f16x2{sp[0], sp[0]} : f16x2{sp[1], sp[1]};
       u32x4 r;
       r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[t], 1.0f, 0) * sc);
       r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[t], 1.0f, 1) * sc);
@@ -609,19 +606,16 @@ __device__ __forceinline__ void query_frags_fp4h(const uint16_t* __restrict__ q_
   lds_barrier();
 }
 
-// The head weights of the accumulator rows lane (g, n) holds (heads 16*ht + 4g + i).
+// Head weight h = threadIdx.x of query b (threads below 16 * HT; zero past n_heads),
+// loaded at kernel entry ahead of the key loads.  The weights reach every lane through
+// LDS: loaded straight into the registers the tile loop reads, their completion would be
+// waited for behind the key prefetches at the top of every pass.
 template <int HT>
-__device__ __forceinline__ void query_weights(const float* __restrict__ w_idx, int b, int n_heads,
-                                              int g, float (&wv)[HT][4]) {
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 16 * ht + 4 * g + i;
-      wv[ht][i] = h < n_heads ? w_idx[(int64_t)b * n_heads + h] : 0.0f;
-    }
+__device__ __forceinline__ float query_weight_load(const float* __restrict__ w_idx, int b,
+                                                   int n_heads) {
+  const int h = threadIdx.x;
+  return (h < 16 * HT && h < n_heads) ? w_idx[(int64_t)b * n_heads + h] : 0.0f;
 }
-
 
 // The query fragments and head weights of query b; QH: Hadamard-rotated FP4 queries.
 // bf16 indexer queries, prepared once per workgroup: wave ht loads head tile ht and its
@@ -678,19 +672,39 @@ __device__ __forceinline__ void query_frags_staged(const uint16_t* __restrict__ 
 
 // The query fragments and head weights of query b, prepared once per workgroup (every
 // wave must call this: it holds barriers).  QH: Hadamard-rotated FP4 queries.  `stage`:
-// LDS for HT * 256 fragments; `red`: LDS for HT floats.
+// LDS for HT * 256 fragments; `red`: LDS for HT floats; `s_w`: LDS for 16 * HT floats,
+// which the caller keeps until every wave has left this function.  `w_pre`: this
+// thread's query_weight_load.  wv gets the weights of the accumulator rows lane (g, n)
+// holds (heads 16*ht + 4g + i).
 template <class KT, int HT, bool QH>
-__device__ __forceinline__ void query_setup(const uint16_t* __restrict__ q_idx,
-                                            const float* __restrict__ w_idx, int b, int n_heads,
-                                            int wave, int g, int n, typename KT::Op (&qa)[HT][4],
-                                            float (&wv)[HT][4], void* stage, float* red) {
-  query_weights<HT>(w_idx, b, n_heads, g, wv);
+__device__ __forceinline__ void query_setup(const uint16_t* __restrict__ q_idx, float w_pre,
+                                            int b, int n_heads, int wave, int g, int n,
+                                            typename KT::Op (&qa)[HT][4], float (&wv)[HT][4],
+                                            void* stage, float* red, float* s_w) {
+  if (threadIdx.x < 16 * HT) s_w[threadIdx.x] = w_pre;  // ordered by the barriers below
   if constexpr (QH) {
     static_assert(KT::kScales, "rotated FP4 queries meet rotated FP4 keys");
     query_frags_fp4h<HT>(q_idx, b, n_heads, wave, g, n, qa, static_cast<f16x8*>(stage));
   } else {
     query_frags_staged<KT, HT>(q_idx, b, n_heads, wave, g, n, qa, static_cast<u32x4*>(stage), red);
   }
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[ht][i] = s_w[16 * ht + 4 * g + i];
+}
+
+// Lane (g, n)'s share of the score of its tile row n: the sum over the heads it holds
+// (16 * ht + 4g + i) of w_h * ReLU(acc).  The four lane groups' shares add up to the
+// score.  ReLU is a signed-integer max: negative floats (and -0) have the sign bit set.
+template <int HT>
+__device__ __forceinline__ float weighted_relu_share(const f32x4 (&acc)[HT], const float (&wv)[HT][4]) {
+  float sc = 0.0f;
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc += wv[ht][i] * __int_as_float(max(__float_as_int(acc[ht][i]), 0));
+  return sc;
 }
 
 // ------------------------------------------------------------------ scan kernel
@@ -713,13 +727,16 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
     int64_t n_c, const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx, int n_heads,
     int n_slices, int slices_per_wg, int wg_per_query, int prefix, int cap, IndexerWs ws) {
   typedef typename KT::Op Op;
-  __shared__ uint32_t s_score[kSliceRows + kWave];  // + one dummy slot per lane
+  // Per row of the current slice, the four lane groups' shares of its score (float4);
+  // first the query setup's staging area.
+  __shared__ __attribute__((aligned(16))) float s_part[kSliceRows * 4];
+  __shared__ uint32_t s_score[kSliceRows];  // order keys of the slice's scores
   __shared__ SelectSmem sm;
 
   const int b = blockIdx.x / wg_per_query;
   const int slice0 = (blockIdx.x - b * wg_per_query) * slices_per_wg;
   const int n_sl = min(slices_per_wg, n_slices - slice0);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // scalar tile math
   const int lane = threadIdx.x & (kWave - 1);
   const int g = lane >> 4;
   const int n = lane & 15;
@@ -729,9 +746,10 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
   const int64_t seq_row0 = (int64_t)b * seq_stride + row_base;
 
   // The wave's tile sequence: slot k -> pass k / kSubTiles, tile wave + 8m of that pass
-  // (m = k % kSubTiles).  Every slot loads (rows clamped into range) and computes, so the
-  // loads are straight-line code and the ring keeps kRing tiles in flight across passes
-  // and slices; only valid rows store a score.  A pass is unrolled whole so that the
+  // (m = k % kSubTiles).  Every slot loads (rows past the end read zeros) and computes, so
+  // the loads are straight-line code and the ring keeps kRing tiles in flight across
+  // passes and slices.  A row past the end lands in its slice's buffer at or after the
+  // slice's last row, where nothing reads it.  A pass is unrolled whole so that the
   // ring's waits are counted exactly.
   const int total = n_pass * kSubTiles;
   auto slot_tile = [&](int k) -> int {
@@ -743,8 +761,10 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
   const int lane_co = KT::code_offset(n, g), lane_so = KT::scale_offset(n, g);
   const int rows_wg = (int)rows_total;  // at most 512 slices of 4096 rows: 32-bit math
   auto load_slot = [&](KT& kt, int k) {
-    const int r0 = __builtin_amdgcn_readfirstlane(slot_tile(k)) * 16;  // wave-uniform
-    const int live = __builtin_amdgcn_readfirstlane(min(max(rows_wg - r0, 0), 16));  // rows that exist
+    const int r0 = slot_tile(k) * 16;  // wave-uniform (scalar)
+    // The resource covers the rows from r0 to the end of the workgroup's rows; the tile
+    // reads at most 16 of them.
+    const int live = max(rows_wg - r0, 0);
     const Rsrc rc = make_rsrc(kcodes + (int64_t)r0 * KT::kRowBytes, (uint32_t)(live * KT::kRowBytes));
     const Rsrc rs = KT::kScales ? make_rsrc(kscales + (int64_t)r0 * (kIdxDim / 16),
                                             (uint32_t)(live * (kIdxDim / 16)))
@@ -752,6 +772,7 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
     kt.load(rc, rs, lane_co, lane_so);
   };
 
+  const float w_pre = query_weight_load<HT>(w_idx, b, n_heads);
   // The ring's first loads go out before the query setup, which they overlap.
   KT ring[kRing];
 #pragma unroll
@@ -763,15 +784,24 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
   // Indexer query fragments and head weights.
   Op qa[HT][4];
   float wv[HT][4];
-  static_assert(sizeof(uint32_t) * (kSliceRows + kWave) >= sizeof(f16x8) * 4 * 4 * kWave, "query stage");
-  query_setup<KT, HT, QH>(q_idx, w_idx, b, n_heads, wave, g, n, qa, wv, s_score,
-                          reinterpret_cast<float*>(sm.red32));
+  static_assert(sizeof(s_part) >= sizeof(f16x8) * 4 * 4 * kWave, "query stage");
+  static_assert(sizeof(sm.hist) >= sizeof(float) * 16 * HT, "weight stage");
+  query_setup<KT, HT, QH>(q_idx, w_pre, b, n_heads, wave, g, n, qa, wv, s_part,
+                          reinterpret_cast<float*>(sm.red32), reinterpret_cast<float*>(sm.hist));
 
+  // Lane (g, n)'s share of tile row r of a pass goes to s_part[4 * r + g]: the slot of
+  // tile wave + 8m of pass ps is row (ps % kPassesPerSlice) * kSubRows + 16 * (wave + 8m)
+  // + n of the slice, so within a pass the address is a per-lane base plus a constant.
+  const int lane_part = 4 * (16 * wave + n) + g;
   for (int ps = 0; ps < n_pass; ++ps) {
+    float* const pass_part = s_part + 4 * (ps % kPassesPerSlice) * kSubRows + lane_part;
 #pragma unroll
     for (int m = 0; m < kSubTiles; ++m) {
       const int d = m % kRing;
       const int k = ps * kSubTiles + m;
+      // Keep each tile's instructions together: hoisting a later tile's decode above
+      // this point would wait on that tile's key load, which is still in flight.
+      __builtin_amdgcn_sched_barrier(0);
       Op kb[4];
       ring[d].decode(kb);
       load_slot(ring[d], k + kRing);  // past the end: reads zeros
@@ -782,19 +812,8 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) acc[ht] = KT::mma(qa[ht][t], kb[t], acc[ht]);
-      // ReLU as a signed-integer max: negative floats (and -0) have the sign bit set.
-      float sc = 0.0f;
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sc += wv[ht][i] * __int_as_float(max(__float_as_int(acc[ht][i]), 0));
-      sc = wave_sum_rows(sc);
-      // Every lane stores (no branch, so a pass stays one basic block): the lanes of
-      // group 0 holding a valid row store its score, the others a dummy slot.
-      const int row = slot_tile(k) * 16 + n;  // within the workgroup's rows
-      const bool keep = g == 0 && row < rows_wg;
-      s_score[keep ? (row & (kSliceRows - 1)) : kSliceRows + lane] = f32_order_key(sc);
+      // Each lane stores its share; the shares are added when the slice is complete.
+      pass_part[4 * 16 * kScanWaves * m] = weighted_relu_share<HT>(acc, wv);
     }
     if ((ps + 1) % kPassesPerSlice != 0 && ps + 1 < n_pass) continue;  // more passes in this slice
 
@@ -805,7 +824,13 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
     const int64_t si = (int64_t)b * n_slices + slice0 + j;
     lds_barrier();
     uint32_t* sc_out = ws.scores + (int64_t)b * n_c + srow0;
-    for (int i = threadIdx.x; i < rows; i += kScanThreads) sc_out[i] = s_score[i];
+    for (int i = threadIdx.x; i < rows; i += kScanThreads) {
+      const f32x4 p = *reinterpret_cast<const f32x4*>(s_part + 4 * i);
+      const uint32_t key = f32_order_key((p[0] + p[1]) + (p[2] + p[3]));
+      s_score[i] = key;
+      sc_out[i] = key;
+    }
+    lds_barrier();
     const int pe = min(prefix, rows);
     uint32_t t32 = 0u, cnt = (uint32_t)rows;
     if (pe < rows) slice_threshold<kScanThreads>(s_score, rows, pe, sm, &t32, &cnt);
@@ -978,8 +1003,9 @@ __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(
   }
   Op qa[HT][4];
   float wv[HT][4];
-  query_setup<KT, HT, QH>(q_idx, w_idx, b, n_heads, wave, g, n, qa, wv, s_val,
-                          reinterpret_cast<float*>(sm.red32));
+  query_setup<KT, HT, QH>(q_idx, query_weight_load<HT>(w_idx, b, n_heads), b, n_heads, wave,
+                          g, n, qa, wv, s_val, reinterpret_cast<float*>(sm.red32),
+                          reinterpret_cast<float*>(sm.hist));
   lds_barrier();
 
   const Rsrc rc = make_rsrc(codes + (int64_t)b * seq_stride * KT::kRowBytes,
@@ -1021,13 +1047,7 @@ __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(
       for (int k = 0; k < 4; ++k)
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) acc[ht] = KT::mma(qa[ht][k], kb[k], acc[ht]);
-      float sc = 0.0f;
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sc += wv[ht][i] * __int_as_float(max(__float_as_int(acc[ht][i]), 0));
-      sc = wave_sum_rows(sc);
+      const float sc = wave_sum_rows(weighted_relu_share<HT>(acc, wv));
       const int pos = 16 * t + n;
       if (g == 0 && pos < n_pool) {
         const int row = s_row[pos];
