@@ -51,7 +51,8 @@ class CsakvError(RuntimeError):
 class Cache(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("n_rows", ctypes.c_int64), ("seq_stride_rows", ctypes.c_int64),
-                ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+                ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("seq_rows", ctypes.c_void_p)]
 
 
 class CsaParams(ctypes.Structure):
@@ -147,10 +148,16 @@ def _check(status: int, what: str):
         raise CsakvError(status, what)
 
 
-def cache(fmt: int, codes, n_rows: int, seq_stride_rows: int | None = None, scales=None) -> Cache:
-    """Cache descriptor for a tensor of B sequences (see ``csakv_cache`` in the header)."""
-    return Cache(fmt, 0, int(n_rows), int(n_rows if seq_stride_rows is None else seq_stride_rows),
-                 _ptr(codes), _ptr(scales))
+def cache(fmt: int, codes, n_rows: int, seq_stride_rows: int | None = None, scales=None,
+          seq_rows=None) -> Cache:
+    """Cache descriptor for a tensor of B sequences (see ``csakv_cache`` in the header).
+
+    ``seq_rows``: None, or a device int32 tensor [B] of per-sequence row counts.  The
+    descriptor keeps references to the tensors it points at, so they outlive it."""
+    c = Cache(fmt, 0, int(n_rows), int(n_rows if seq_stride_rows is None else seq_stride_rows),
+              _ptr(codes), _ptr(scales), _ptr(seq_rows))
+    c._tensors = (codes, scales, seq_rows)
+    return c
 
 
 def csakv_status_string(status: int) -> str:

@@ -223,7 +223,8 @@ __device__ __forceinline__ bool attn_block(int n_pairs, int n_groups, int n_chun
 template <int KVFMT, bool CSA, int NB>
 __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t seq_stride,
-    int64_t n_rows, const uint16_t* __restrict__ q, int n_heads, float scale_log2,
+    int64_t n_rows_max, const int32_t* __restrict__ seq_rows, const uint16_t* __restrict__ q,
+    int n_heads, float scale_log2,
     const int32_t* __restrict__ topk, int top_k, int window, int64_t n_list, int rows_per_chunk,
     int n_chunks, int n_pairs, float* __restrict__ part_o, float* __restrict__ part_ml) {
   constexpr int kTileElems = kStepRows * kPitch;
@@ -246,6 +247,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
   const int64_t p_begin = (int64_t)chunk * rows_per_chunk;
   const int64_t p_end = min(p_begin + rows_per_chunk, n_list);
   const int n_steps = (int)((p_end - p_begin + kStepRows - 1) / kStepRows);
+  const int64_t n_rows = seq_len(seq_rows, b, n_rows_max);  // this sequence's rows
   const int64_t n_c = n_rows - window;
 
   // Sequence row of every list position of the chunk (-1: absent or out of range), and
@@ -255,7 +257,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
     int row = -1;
     if (p < p_end) {
       if (!CSA || p < window) {
-        row = (int)p;
+        row = p < n_rows ? (int)p : -1;
       } else {
         const int32_t j = topk[(int64_t)b * top_k + (p - window)];
         row = (j >= 0 && j < n_c) ? window + j : -1;
@@ -469,14 +471,15 @@ int attention_blocks(int batch, int n_heads, const AttnPlan& plan) {
 
 template <int KVFMT, bool CSA>
 void launch_chunks(hipStream_t stream, const uint8_t* codes, const uint8_t* scales,
-                   int64_t seq_stride, int64_t n_rows, const uint16_t* q, int batch, int n_heads,
+                   int64_t seq_stride, int64_t n_rows, const int32_t* seq_rows, const uint16_t* q,
+                   int batch, int n_heads,
                    float scale_log2, const int32_t* topk, int top_k, int window,
                    const AttnPlan& plan, float* part_o, float* part_ml) {
   const dim3 grid(attention_blocks(batch, n_heads, plan));
   const int n_pairs = batch * plan.n_chunks;
 #define CSAKV_CHUNK(NB)                                                                         \
   hipLaunchKernelGGL((attention_chunk_kernel<KVFMT, CSA, NB>), grid, dim3(kAttnThreads), 0,      \
-                     stream, codes, scales, seq_stride, n_rows, q, n_heads, scale_log2, topk,    \
+                     stream, codes, scales, seq_stride, n_rows, seq_rows, q, n_heads, scale_log2, topk, \
                      top_k, window, plan.n_list, plan.rows_per_chunk, plan.n_chunks, n_pairs,   \
                      part_o, part_ml)
   // One decode tile (55 KB of LDS: two workgroups per CU); the second tile's one barrier
@@ -556,7 +559,8 @@ size_t attention_workspace_bytes(int batch, int n_heads, const AttnPlan& plan) {
 }
 
 hipError_t launch_attention(int kv_fmt, bool csa, const uint8_t* codes, const uint8_t* scales,
-                            int64_t seq_stride, int64_t n_rows, const uint16_t* q, int batch,
+                            int64_t seq_stride, int64_t n_rows, const int32_t* seq_rows,
+                            const uint16_t* q, int batch,
                             int n_heads, float softmax_scale, const int32_t* topk, int top_k,
                             int window, const AttnPlan& plan, void* workspace, uint16_t* out,
                             hipStream_t stream) {
@@ -565,7 +569,7 @@ hipError_t launch_attention(int kv_fmt, bool csa, const uint8_t* codes, const ui
   const float sl2 = softmax_scale * kLog2e;
   if (plan.n_chunks > 0) {
 #define CSAKV_ATTN(F, C)                                                                        \
-  launch_chunks<F, C>(stream, codes, scales, seq_stride, n_rows, q, batch, n_heads, sl2, topk, \
+  launch_chunks<F, C>(stream, codes, scales, seq_stride, n_rows, seq_rows, q, batch, n_heads, sl2, topk, \
                       top_k, window, plan, part_o, part_ml)
     if (csa) {
       if (kv_fmt == 0) CSAKV_ATTN(0, true);

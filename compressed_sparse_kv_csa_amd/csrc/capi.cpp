@@ -29,6 +29,7 @@ csakv_status check_cache(const csakv_cache* c, bool is_kv) {
   // A cache without rows may have null pointers; any pointer given must be aligned.
   const bool empty = c->n_rows == 0;
   if ((!empty && !c->codes) || !aligned(c->codes, 16)) return CSAKV_ERR_INVALID;
+  if (!aligned(c->seq_rows, 4)) return CSAKV_ERR_INVALID;
   const bool fp4 = is_kv ? c->fmt == CSAKV_KV_FP4 : c->fmt != CSAKV_IDX_BF16;
   if (fp4) {
     if ((!empty && !c->scales) || !aligned(c->scales, 16)) return CSAKV_ERR_INVALID;
@@ -127,13 +128,14 @@ csakv_status csa_decode(const csakv_csa_params* p, const csakv_cache* kv,
   if (full) {
     hipError_t e = csakv::launch_indexer(
         idx_keys->fmt, static_cast<const uint8_t*>(idx_keys->codes), idx_keys->scales,
-        idx_keys->seq_stride_rows, n_c, q_idx, w_idx, p->batch, p->n_idx_heads, p->top_k, L.idx,
-        ws, topk, s);
+        idx_keys->seq_stride_rows, n_c, idx_keys->seq_rows, q_idx, w_idx, p->batch,
+        p->n_idx_heads, p->top_k, L.idx, ws, topk, s);
     if (e != hipSuccess) return CSAKV_ERR_HIP;
   }
   return hip_status(csakv::launch_attention(
       kv->fmt, true, static_cast<const uint8_t*>(kv->codes), kv->scales, kv->seq_stride_rows,
-      kv->n_rows, q, p->batch, p->n_q_heads, p->softmax_scale, topk, p->top_k, p->window, L.attn,
+      kv->n_rows, kv->seq_rows, q, p->batch, p->n_q_heads, p->softmax_scale, topk, p->top_k,
+      p->window, L.attn,
       ws + L.attn_offset, out, s));
 }
 
@@ -162,7 +164,8 @@ csakv_status csa_select_topk(const csakv_csa_params* p, const csakv_cache* idx_k
   if (need > 0 && (!workspace || !aligned(workspace, kWsAlign))) return CSAKV_ERR_INVALID;
   return hip_status(csakv::launch_indexer(
       idx_keys->fmt, static_cast<const uint8_t*>(idx_keys->codes), idx_keys->scales,
-      idx_keys->seq_stride_rows, n_c, q_idx, w_idx, p->batch, p->n_idx_heads, p->top_k, plan,
+      idx_keys->seq_stride_rows, n_c, idx_keys->seq_rows, q_idx, w_idx, p->batch, p->n_idx_heads,
+      p->top_k, plan,
       workspace, topk, static_cast<hipStream_t>(stream)));
 }
 
@@ -187,7 +190,8 @@ csakv_status csa_reindex_topk(const csakv_csa_params* p, const csakv_cache* idx_
   if (pb < te && tb < pe) return CSAKV_ERR_INVALID;
   return hip_status(csakv::launch_reindex(
       idx_keys->fmt, static_cast<const uint8_t*>(idx_keys->codes), idx_keys->scales,
-      idx_keys->seq_stride_rows, n_c, q_idx, w_idx, p->batch, p->n_idx_heads, pool, n_pool,
+      idx_keys->seq_stride_rows, n_c, idx_keys->seq_rows, q_idx, w_idx, p->batch, p->n_idx_heads,
+      pool, n_pool,
       p->top_k, topk, static_cast<hipStream_t>(stream)));
 }
 
@@ -215,7 +219,7 @@ csakv_status hca_decode(int32_t batch, int32_t n_q_heads, float softmax_scale,
   csakv::AttnPlan a = csakv::plan_attention(batch, kv->n_rows, false, n_q_heads);
   return hip_status(csakv::launch_attention(
       kv->fmt, false, static_cast<const uint8_t*>(kv->codes), kv->scales, kv->seq_stride_rows,
-      kv->n_rows, q, batch, n_q_heads, softmax_scale, nullptr, 0, 0, a, workspace, out,
+      kv->n_rows, kv->seq_rows, q, batch, n_q_heads, softmax_scale, nullptr, 0, 0, a, workspace, out,
       static_cast<hipStream_t>(stream)));
 }
 

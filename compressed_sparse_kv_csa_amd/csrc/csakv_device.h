@@ -136,6 +136,16 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16(uint32_t codes, float s) {
                pack_bf16_exact(e2[0] * s, e2[1] * s), pack_bf16_exact(e3[0] * s, e3[1] * s)};
 }
 
+// ---------------------------------------------------------------- sequence lengths
+
+// Rows of sequence b: n, or seq_rows[b] clamped to [0, n] when per-sequence lengths
+// are given.
+__device__ __forceinline__ int64_t seq_len(const int32_t* seq_rows, int b, int64_t n) {
+  if (!seq_rows) return n;
+  const int64_t r = seq_rows[b];
+  return r < 0 ? 0 : (r > n ? n : r);
+}
+
 // ---------------------------------------------------------------- order keys
 
 // Monotone map fp32 -> uint32 (larger float -> larger key).

@@ -724,8 +724,9 @@ struct IndexerWs {
 template <class KT, int HT, bool QH>
 __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t seq_stride,
-    int64_t n_c, const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx, int n_heads,
-    int n_slices, int slices_per_wg, int wg_per_query, int prefix, int cap, IndexerWs ws) {
+    int64_t n_c, const int32_t* __restrict__ seq_rows, const uint16_t* __restrict__ q_idx,
+    const float* __restrict__ w_idx, int n_heads, int n_slices, int slices_per_wg,
+    int wg_per_query, int prefix, int cap, IndexerWs ws) {
   typedef typename KT::Op Op;
   // Per row of the current slice, the four lane groups' shares of its score (float4);
   // first the query setup's staging area.
@@ -741,9 +742,18 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
   const int g = lane >> 4;
   const int n = lane & 15;
   const int64_t row_base = (int64_t)slice0 * kSliceRows;              // compressed row index
-  const int64_t rows_total = min((int64_t)n_sl * kSliceRows, n_c - row_base);
+  const int64_t n_cb = seq_len(seq_rows, b, n_c);                     // this sequence's rows
+  const int64_t rows_total = max(min((int64_t)n_sl * kSliceRows, n_cb - row_base), (int64_t)0);
   const int n_pass = (int)((rows_total + kSubRows - 1) / kSubRows);
   const int64_t seq_row0 = (int64_t)b * seq_stride + row_base;
+  // Slices of the run past the sequence's end send nothing.
+  const int n_done = (int)((rows_total + kSliceRows - 1) / kSliceRows);
+  if (threadIdx.x < n_sl - n_done) {
+    const int64_t si = (int64_t)b * n_slices + slice0 + n_done + threadIdx.x;
+    ws.count[si] = 0u;
+    ws.bound[si] = 0ull;
+  }
+  if (n_done == 0) return;  // the whole workgroup: no barrier is left waiting
 
   // The wave's tile sequence: slot k -> pass k / kSubTiles, tile wave + 8m of that pass
   // (m = k % kSubTiles).  Every slot loads (rows past the end read zeros) and computes, so
@@ -820,7 +830,7 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
     // ---- slice complete: emit its candidates, its bound and its scores
     const int j = ps / kPassesPerSlice;
     const int64_t srow0 = row_base + (int64_t)j * kSliceRows;
-    const int rows = (int)min((int64_t)kSliceRows, n_c - srow0);
+    const int rows = (int)min((int64_t)kSliceRows, n_cb - srow0);
     const int64_t si = (int64_t)b * n_slices + slice0 + j;
     lds_barrier();
     uint32_t* sc_out = ws.scores + (int64_t)b * n_c + srow0;
@@ -870,7 +880,8 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
 // ------------------------------------------------------------------ merge kernel
 
 __global__ __launch_bounds__(kMergeThreads) void indexer_merge_kernel(
-    IndexerWs ws, int64_t n_c, int top_k, int n_slices, int cap, int32_t* __restrict__ topk) {
+    IndexerWs ws, int64_t n_c, const int32_t* __restrict__ seq_rows, int top_k, int n_slices,
+    int cap, int32_t* __restrict__ topk) {
   __shared__ uint64_t s_buf[kMergeCap];
   __shared__ uint64_t s_list[kMergeListCap];
   __shared__ uint64_t s_bound[kMaxMergeSlices];
@@ -881,7 +892,8 @@ __global__ __launch_bounds__(kMergeThreads) void indexer_merge_kernel(
 
   const int b = blockIdx.x;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int k1 = (int)min((int64_t)top_k, n_c);
+  const int64_t n_cb = seq_len(seq_rows, b, n_c);  // this sequence's rows
+  const int k1 = (int)min((int64_t)top_k, n_cb);
   int32_t* out = topk + (int64_t)b * top_k;
   for (int i = k1 + threadIdx.x; i < top_k; i += NT) out[i] = -1;
   if (k1 == 0) return;
@@ -933,7 +945,7 @@ __global__ __launch_bounds__(kMergeThreads) void indexer_merge_kernel(
       // Append the slice's unsent keys >= kth, read back from its stored scores.
       {
         const int64_t srow0 = (int64_t)s * kSliceRows;
-        const int rows = (int)min((int64_t)kSliceRows, n_c - srow0);
+        const int rows = (int)min((int64_t)kSliceRows, n_cb - srow0);
         const uint32_t* sc = ws.scores + (int64_t)b * n_c + srow0;
         const uint64_t bnd = s_bound[s];
         const int chunk = (rows + NT - 1) / NT;
@@ -983,9 +995,9 @@ constexpr uint32_t kAbsentKeyOffset = kReindexMaxSeqBytes;
 template <class KT, int HT, bool QH>
 __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t seq_stride,
-    int64_t n_c, const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
-    int n_heads, const int32_t* __restrict__ pool, int n_pool, int top_k,
-    int32_t* __restrict__ topk) {
+    int64_t n_c_max, const int32_t* __restrict__ seq_rows, const uint16_t* __restrict__ q_idx,
+    const float* __restrict__ w_idx, int n_heads, const int32_t* __restrict__ pool, int n_pool,
+    int top_k, int32_t* __restrict__ topk) {
   typedef typename KT::Op Op;
   constexpr int NT = kReindexThreads;
   __shared__ int s_row[kMaxPool];        // pool rows, -1 for an empty slot
@@ -996,6 +1008,7 @@ __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(
   const int b = blockIdx.x;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int g = lane >> 4, n = lane & 15;
+  const int64_t n_c = seq_len(seq_rows, b, n_c_max);  // this sequence's rows
 
   for (int i = threadIdx.x; i < n_pool; i += NT) {
     const int32_t r = pool[(int64_t)b * n_pool + i];
@@ -1087,12 +1100,12 @@ __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(
 
 template <class KT, bool QH>
 void launch_reindex_ht(int ht, hipStream_t stream, const uint8_t* codes, const uint8_t* scales,
-                       int64_t seq_stride, int64_t n_c, const uint16_t* q_idx, const float* w_idx,
+                       int64_t seq_stride, int64_t n_c, const int32_t* seq_rows, const uint16_t* q_idx, const float* w_idx,
                        int batch, int n_heads, const int32_t* pool, int n_pool, int top_k,
                        int32_t* topk) {
 #define CSAKV_REINDEX(H)                                                                        \
   hipLaunchKernelGGL((reindex_kernel<KT, H, QH>), dim3(batch), dim3(kReindexThreads), 0, stream,   \
-                     codes, scales, seq_stride, n_c, q_idx, w_idx, n_heads, pool, n_pool, top_k, \
+                     codes, scales, seq_stride, n_c, seq_rows, q_idx, w_idx, n_heads, pool, n_pool, top_k, \
                      topk)
   switch (ht) {
     case 1: CSAKV_REINDEX(1); break;
@@ -1105,20 +1118,20 @@ void launch_reindex_ht(int ht, hipStream_t stream, const uint8_t* codes, const u
 
 template <class KT, int HT, bool QH>
 void launch_scan(hipStream_t stream, const uint8_t* codes, const uint8_t* scales,
-                 int64_t seq_stride, int64_t n_c, const uint16_t* q_idx, const float* w_idx,
+                 int64_t seq_stride, int64_t n_c, const int32_t* seq_rows, const uint16_t* q_idx, const float* w_idx,
                  int batch, int n_heads, const IndexerPlan& plan, const IndexerWs& ws) {
   hipLaunchKernelGGL((indexer_scan_kernel<KT, HT, QH>), dim3(batch * plan.wg_per_query),
-                     dim3(kScanThreads), 0, stream, codes, scales, seq_stride, n_c, q_idx, w_idx,
+                     dim3(kScanThreads), 0, stream, codes, scales, seq_stride, n_c, seq_rows, q_idx, w_idx,
                      n_heads, plan.n_slices, plan.slices_per_wg, plan.wg_per_query, plan.prefix,
                      plan.cap, ws);
 }
 
 template <class KT, bool QH = false>
 void launch_scan_ht(int ht, hipStream_t stream, const uint8_t* codes, const uint8_t* scales,
-                    int64_t seq_stride, int64_t n_c, const uint16_t* q_idx, const float* w_idx,
+                    int64_t seq_stride, int64_t n_c, const int32_t* seq_rows, const uint16_t* q_idx, const float* w_idx,
                     int batch, int n_heads, const IndexerPlan& plan, const IndexerWs& ws) {
 #define CSAKV_SCAN(H) \
-  launch_scan<KT, H, QH>(stream, codes, scales, seq_stride, n_c, q_idx, w_idx, batch, n_heads, plan, ws)
+  launch_scan<KT, H, QH>(stream, codes, scales, seq_stride, n_c, seq_rows, q_idx, w_idx, batch, n_heads, plan, ws)
   switch (ht) {
     case 1: CSAKV_SCAN(1); break;
     case 2: CSAKV_SCAN(2); break;
@@ -1182,7 +1195,7 @@ bool indexer_supported(const IndexerPlan& plan) {
 }
 
 hipError_t launch_indexer(int key_fmt, const uint8_t* codes, const uint8_t* scales,
-                          int64_t seq_stride, int64_t n_c, const uint16_t* q_idx,
+                          int64_t seq_stride, int64_t n_c, const int32_t* seq_rows, const uint16_t* q_idx,
                           const float* w_idx, int batch, int n_heads, int top_k,
                           const IndexerPlan& plan, void* workspace, int32_t* topk,
                           hipStream_t stream) {
@@ -1190,18 +1203,18 @@ hipError_t launch_indexer(int key_fmt, const uint8_t* codes, const uint8_t* scal
   if (plan.n_slices > 0) {
     const int ht = (n_heads + 15) / 16;
     if (key_fmt == 0)
-      launch_scan_ht<KeyTileBf16>(ht, stream, codes, scales, seq_stride, n_c, q_idx, w_idx, batch,
+      launch_scan_ht<KeyTileBf16>(ht, stream, codes, scales, seq_stride, n_c, seq_rows, q_idx, w_idx, batch,
                                   n_heads, plan, ws);
     else if (key_fmt == 1)
-      launch_scan_ht<KeyTileFp4>(ht, stream, codes, scales, seq_stride, n_c, q_idx, w_idx, batch,
+      launch_scan_ht<KeyTileFp4>(ht, stream, codes, scales, seq_stride, n_c, seq_rows, q_idx, w_idx, batch,
                                  n_heads, plan, ws);
     else  // Hadamard-rotated FP4 keys: the query is rotated and quantised the same way
-      launch_scan_ht<KeyTileFp4, true>(ht, stream, codes, scales, seq_stride, n_c, q_idx, w_idx,
+      launch_scan_ht<KeyTileFp4, true>(ht, stream, codes, scales, seq_stride, n_c, seq_rows, q_idx, w_idx,
                                        batch, n_heads, plan, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(indexer_merge_kernel, dim3(batch), dim3(kMergeThreads), 0, stream, ws, n_c,
+  hipLaunchKernelGGL(indexer_merge_kernel, dim3(batch), dim3(kMergeThreads), 0, stream, ws, n_c, seq_rows,
                      top_k, plan.n_slices, plan.cap, topk);
   return hipGetLastError();
 }
@@ -1212,18 +1225,18 @@ bool reindex_supported(int key_fmt, int64_t n_c) {
 }
 
 hipError_t launch_reindex(int key_fmt, const uint8_t* codes, const uint8_t* scales,
-                          int64_t seq_stride, int64_t n_c, const uint16_t* q_idx,
+                          int64_t seq_stride, int64_t n_c, const int32_t* seq_rows, const uint16_t* q_idx,
                           const float* w_idx, int batch, int n_heads, const int32_t* pool,
                           int n_pool, int top_k, int32_t* topk, hipStream_t stream) {
   const int ht = (n_heads + 15) / 16;
   if (key_fmt == 0)
-    launch_reindex_ht<KeyTileBf16, false>(ht, stream, codes, scales, seq_stride, n_c, q_idx, w_idx,
+    launch_reindex_ht<KeyTileBf16, false>(ht, stream, codes, scales, seq_stride, n_c, seq_rows, q_idx, w_idx,
                                           batch, n_heads, pool, n_pool, top_k, topk);
   else if (key_fmt == 1)
-    launch_reindex_ht<KeyTileFp4, false>(ht, stream, codes, scales, seq_stride, n_c, q_idx, w_idx,
+    launch_reindex_ht<KeyTileFp4, false>(ht, stream, codes, scales, seq_stride, n_c, seq_rows, q_idx, w_idx,
                                          batch, n_heads, pool, n_pool, top_k, topk);
   else
-    launch_reindex_ht<KeyTileFp4, true>(ht, stream, codes, scales, seq_stride, n_c, q_idx, w_idx,
+    launch_reindex_ht<KeyTileFp4, true>(ht, stream, codes, scales, seq_stride, n_c, seq_rows, q_idx, w_idx,
                                         batch, n_heads, pool, n_pool, top_k, topk);
   return hipGetLastError();
 }

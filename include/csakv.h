@@ -80,14 +80,21 @@ typedef enum { CSAKV_MODE_FULL = 0, CSAKV_MODE_REUSE = 1, CSAKV_MODE_REINDEX = 2
  * (b * seq_stride_rows + r) * code_bytes(fmt) of `codes`; for FP4 its scales start
  * at byte (b * seq_stride_rows + r) * (dim / 16) of `scales` (NULL otherwise).
  * Shared-KV rows of a sequence are [window rows | compressed rows]: top-k index j
- * names row window + j.  A cache with n_rows == 0 may pass NULL pointers. */
+ * names row window + j.  A cache with n_rows == 0 may pass NULL pointers.
+ * Variable lengths: with seq_rows == NULL every sequence holds n_rows rows; otherwise
+ * seq_rows is a device array [B] of int32 and sequence b holds rows
+ * [0, seq_rows[b]) (values are clamped to [0, n_rows], so n_rows is the capacity).
+ * For a CSA layer the shared-KV lengths are window + N_c(b) and the indexer-key
+ * lengths N_c(b); each query selects among, and attends over, its own rows only
+ * (a sequence shorter than the window attends over the window rows it holds). */
 typedef struct {
   int32_t fmt;              /* csakv_kv_fmt for shared-KV, csakv_idx_fmt for keys */
   int32_t reserved;         /* must be 0                                            */
-  int64_t n_rows;           /* rows per sequence                                    */
+  int64_t n_rows;           /* rows per sequence (the capacity with seq_rows)       */
   int64_t seq_stride_rows;  /* rows between consecutive sequences, >= n_rows        */
   const void* codes;
   const uint8_t* scales;
+  const int32_t* seq_rows;  /* NULL, or [B] device int32 rows of each sequence      */
 } csakv_cache;
 
 typedef struct {

@@ -124,6 +124,8 @@ def test_csa_rejects_bad_pointers_and_shapes():
     assert _call(p, kv=short, idx=IDX) == ck.ERR_INVALID
     stride = ck.Cache(ck.KV_BF16, 0, 1152, 1000, FAKE, None)               # stride < rows
     assert _call(p, kv=stride, idx=IDX) == ck.ERR_INVALID
+    lens_misaligned = ck.Cache(ck.IDX_BF16, 0, 1024, 1024, FAKE, None, FAKE + 2)
+    assert _call(p, idx=lens_misaligned) == ck.ERR_INVALID                 # per-sequence lengths
     need = ck.csa_decode_workspace_bytes(p, 1024)
     assert need > 0
     assert _call(p, idx=IDX, ws_bytes=need - 1) == ck.ERR_WORKSPACE
