@@ -38,6 +38,7 @@ constexpr int kStepRows = 32;
 constexpr int kPitch = kDim + 16;     // fp16 elements per LDS row (32-byte pad)
 constexpr int kOutPitch = kDim + 4;   // floats per LDS row when staging the output
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyLog2 = 8.0f;  // rescale the accumulators once the maximum grows by 2^8
 // Buffer offset given to an absent row: at or past the end of every sequence the
 // launcher accepts (sequence bytes are checked against it on the host).
 constexpr uint32_t kAbsentOffset = kAttnMaxSeqBytes;
@@ -94,13 +95,12 @@ struct StepRaw<0> {
       load16(w + 4 * k, rc, row_offset(row, kRowBytes, 16 * lane));
     }
   }
-  __device__ __forceinline__ void store(uint16_t* tile, int tid) const {
+  __device__ __forceinline__ void store(uint16_t* tile, int tid) const {  // as bf16
     const int wave = tid / kWave, lane = tid & (kWave - 1);
 #pragma unroll
     for (int k = 0; k < 8; ++k)
-      store16(tile + (8 * wave + k) * kPitch + 8 * lane, bf16x2_to_f16x2(w[4 * k]),
-              bf16x2_to_f16x2(w[4 * k + 1]), bf16x2_to_f16x2(w[4 * k + 2]),
-              bf16x2_to_f16x2(w[4 * k + 3]));
+      store16(tile + (8 * wave + k) * kPitch + 8 * lane, w[4 * k], w[4 * k + 1], w[4 * k + 2],
+              w[4 * k + 3]);
   }
 };
 
@@ -191,13 +191,53 @@ struct StepRaw<2> {
 // and 16+4g..16+4g+3 of the tile): two transposing reads.  Within each 16-lane group
 // the hardware hands lane i, slot j, element i%4 of the 8 bytes addressed by lane
 // 4j + i/4; lane k therefore addresses row base + k/4, dims 16*dt + 4*(k%4).
-__device__ __forceinline__ f16x8 v_fragment(const uint16_t* tile, int g, int k, int dt) {
+__device__ __forceinline__ u32x4 v_fragment(const uint16_t* tile, int g, int k, int dt) {
   const uint16_t* p = tile + (4 * g + (k >> 2)) * kPitch + 16 * dt + 4 * (k & 3);
   const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
   const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 16 * kPitch));
   const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-  return as_f16x8(u32x4{l2[0], l2[1], h2[0], h2[1]});
+  return u32x4{l2[0], l2[1], h2[0], h2[1]};
 }
+
+// The tile's arithmetic.  bf16 rows stay bf16 in the tile and meet the bf16 queries on
+// bf16 MFMA; their probabilities go in as two bf16 terms (high part, then the rounded
+// remainder: 16 significant bits).  FP8 and FP4 rows decode exactly to fp16 and meet
+// fp16 queries on fp16 MFMA with one fp16 term per probability.
+template <int KVFMT>
+struct TileMath {
+  typedef f16x8 Op;
+  static __device__ __forceinline__ Op q_op(u32x4 v) {
+    return as_f16x8(u32x4{bf16x2_to_f16x2(v[0]), bf16x2_to_f16x2(v[1]), bf16x2_to_f16x2(v[2]),
+                          bf16x2_to_f16x2(v[3])});
+  }
+  static __device__ __forceinline__ Op op(u32x4 v) { return as_f16x8(v); }
+  static __device__ __forceinline__ f32x4 mma(Op a, Op b, f32x4 c) { return mfma16x16x32_f16(a, b, c); }
+  static constexpr int kPTerms = 1;
+  // The probabilities of K-slots 8g .. 8g + 7 (rows 4g..4g+3, 16+4g..16+4g+3) as term `t`.
+  static __device__ __forceinline__ Op p_term(const float (&pv)[8], int) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = f32_to_f16_bits(pv[2 * i]) | (f32_to_f16_bits(pv[2 * i + 1]) << 16);
+    return as_f16x8(r);
+  }
+};
+template <>
+struct TileMath<0> {
+  typedef bf16x8 Op;
+  static __device__ __forceinline__ Op q_op(u32x4 v) { return as_bf16x8(v); }
+  static __device__ __forceinline__ Op op(u32x4 v) { return as_bf16x8(v); }
+  static __device__ __forceinline__ f32x4 mma(Op a, Op b, f32x4 c) { return mfma16x16x32(a, b, c); }
+  static constexpr int kPTerms = 2;
+  static __device__ __forceinline__ Op p_term(const float (&pv)[8], int t) {
+    Op r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const __bf16 hi = (__bf16)pv[i];  // round to nearest even
+      r[i] = t == 0 ? hi : (__bf16)(pv[i] - (float)hi);  // the remainder is exact in fp32
+    }
+    return r;
+  }
+};
 
 constexpr int kAttnThreads = 256;  // 4 waves
 constexpr int kDimsPerWave = kDim / 4;
@@ -267,17 +307,16 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
   }
   // The wave's logit B operands, kept in registers: wave w multiplies row tile w & 1
   // over dims 256 * (w >> 1) .. +255, lane (g, n) supplying head n, dims
-  // 256 * (w >> 1) + 32t + 8g .. +7 of K-step t, as fp16.
-  f16x8 qf[8];
+  // 256 * (w >> 1) + 32t + 8g .. +7 of K-step t, in the tile's operand type.
+  typedef TileMath<KVFMT> TM;
+  typename TM::Op qf[8];
   {
     const uint16_t* qr = q + ((int64_t)b * n_heads + 16 * hg + n) * kDim + 256 * (wave >> 1) + 8 * g;
     u32x4 qv[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) qv[t] = *reinterpret_cast<const u32x4*>(qr + 32 * t);
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-      qf[t] = as_f16x8(u32x4{bf16x2_to_f16x2(qv[t][0]), bf16x2_to_f16x2(qv[t][1]),
-                             bf16x2_to_f16x2(qv[t][2]), bf16x2_to_f16x2(qv[t][3])});
+    for (int t = 0; t < 8; ++t) qf[t] = TM::q_op(qv[t]);
   }
   lds_barrier();
 
@@ -319,7 +358,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
       f32x4 part = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < 8; ++t)
-        part = mfma16x16x32_f16(as_f16x8(*reinterpret_cast<const u32x4*>(kr + 32 * t)), qf[t], part);
+        part = TM::mma(TM::op(*reinterpret_cast<const u32x4*>(kr + 32 * t)), qf[t], part);
 #pragma unroll
       for (int i = 0; i < 4; ++i) s_logit[kh][16 * rt + 4 * g + i][n] = part[i];
     }
@@ -330,7 +369,10 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         sacc[rt][i] = s_logit[0][16 * rt + 4 * g + i][n] + s_logit[1][16 * rt + 4 * g + i][n];
-    // ---- online softmax (log2 domain)
+    // ---- online softmax (log2 domain).  Row r of the step is present when bit r of
+    // `present` is set; a step whose rows are all present skips the masking.
+    const uint64_t present =
+        __ballot(s_rows[step * kStepRows + (lane & (kStepRows - 1))] >= 0) & 0xFFFFFFFFull;
     float x[8];
     float mloc = -INFINITY;
 #pragma unroll
@@ -338,41 +380,45 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * g + i;
-        const float v = s_rows[step * kStepRows + r] >= 0 ? sacc[rt][i] * scale_log2 : -INFINITY;
+        float v = sacc[rt][i] * scale_log2;
+        if (present != 0xFFFFFFFFull && !((present >> r) & 1ull)) v = -INFINITY;
         x[4 * rt + i] = v;
         mloc = fmaxf(mloc, v);
       }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
+    // The reference maximum m_run moves only when a step's maximum exceeds it by more
+    // than 2^kLazyLog2: the probabilities then stay below 2^kLazyLog2 (within fp16's
+    // range, rounded with its full precision), and the accumulators are rescaled only on
+    // those rare steps instead of whenever a head's maximum grows.
+    const bool grow = mloc > m_run + kLazyLog2;  // m_run = -inf: any present row
+    float alpha = 1.0f;
+    if (grow) {
+      alpha = m_run == -INFINITY ? 0.0f : exp2f(m_run - mloc);
+      m_run = mloc;
+    }
     float psum = 0.0f;
-    uint32_t pw[4];
-    if (m_new == -INFINITY) {
-      pw[0] = pw[1] = pw[2] = pw[3] = 0u;
-    } else {
-      float pv[8];
+    float pv[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pv[i] = exp2f(x[i] - m_new);
-        psum += pv[i];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pw[i] = f32_to_f16_bits(pv[2 * i]) | (f32_to_f16_bits(pv[2 * i + 1]) << 16);
+    for (int i = 0; i < 8; ++i) {
+      pv[i] = m_run == -INFINITY ? 0.0f : exp2f(x[i] - m_run);
+      psum += pv[i];
     }
     psum += __shfl_xor(psum, 16);
     psum += __shfl_xor(psum, 32);
-    const float alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
     l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (alpha != 1.0f) {
+    if (__any(grow)) {
 #pragma unroll
       for (int i = 0; i < kDimsPerWave / 16; ++i) o[i] *= alpha;
     }
     // ---- O^T += V^T P^T over this wave's dims (K-slots 8g+s <-> rows 4g+s, 16+4g+s-4)
-    const f16x8 pb = as_f16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
 #pragma unroll
-    for (int i = 0; i < kDimsPerWave / 16; ++i)
-      o[i] = mfma16x16x32_f16(v_fragment(tile, g, n, (kDimsPerWave / 16) * wave + i), pb, o[i]);
+    for (int t = 0; t < TM::kPTerms; ++t) {
+      const typename TM::Op pb = TM::p_term(pv, t);
+#pragma unroll
+      for (int i = 0; i < kDimsPerWave / 16; ++i)
+        o[i] = TM::mma(TM::op(v_fragment(tile, g, n, (kDimsPerWave / 16) * wave + i)), pb, o[i]);
+    }
   };
 
   fetch(raw0, 0);
