@@ -52,7 +52,8 @@ class Cache(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("n_rows", ctypes.c_int64), ("seq_stride_rows", ctypes.c_int64),
                 ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
-                ("seq_rows", ctypes.c_void_p)]
+                ("seq_rows", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("page_rows", ctypes.c_int32), ("table_stride", ctypes.c_int32)]
 
 
 class CsaParams(ctypes.Structure):
@@ -149,14 +150,18 @@ def _check(status: int, what: str):
 
 
 def cache(fmt: int, codes, n_rows: int, seq_stride_rows: int | None = None, scales=None,
-          seq_rows=None) -> Cache:
+          seq_rows=None, block_table=None, page_rows: int = 0) -> Cache:
     """Cache descriptor for a tensor of B sequences (see ``csakv_cache`` in the header).
 
-    ``seq_rows``: None, or a device int32 tensor [B] of per-sequence row counts.  The
-    descriptor keeps references to the tensors it points at, so they outlive it."""
-    c = Cache(fmt, 0, int(n_rows), int(n_rows if seq_stride_rows is None else seq_stride_rows),
-              _ptr(codes), _ptr(scales), _ptr(seq_rows))
-    c._tensors = (codes, scales, seq_rows)
+    ``seq_rows``: None, or a device int32 tensor [B] of per-sequence row counts.
+    ``block_table``: None, or a device int32 tensor [B][table_stride] of page ids into the
+    page pool held by ``codes``/``scales`` (``page_rows`` rows per page).  The descriptor
+    keeps references to the tensors it points at, so they outlive it."""
+    stride = int(n_rows if seq_stride_rows is None else seq_stride_rows)
+    table_stride = int(block_table.shape[-1]) if block_table is not None else 0
+    c = Cache(fmt, 0, int(n_rows), stride, _ptr(codes), _ptr(scales), _ptr(seq_rows),
+              _ptr(block_table), int(page_rows), table_stride)
+    c._tensors = (codes, scales, seq_rows, block_table)
     return c
 
 

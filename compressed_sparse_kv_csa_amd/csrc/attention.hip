@@ -6,21 +6,24 @@
 // over the rows r of one query: CSA = the window rows plus the selected compressed
 // rows (one softmax over their union), HCA = every row of the sequence.
 //
-// Structure: grid (chunks, B).  A workgroup owns one chunk of a query's row list and
-// all heads (one wave per 16 heads).  It first resolves the chunk's row indices into
-// LDS, then per 32-row step gathers whole rows (coalesced 16-byte loads, the next
-// step's rows in flight while the current one computes), decodes them to fp16 into
-// one of two row-major LDS tiles, and runs
-//   S^T[32 rows x 16 heads] = K[32 x 512] . Q^T            (16x16x32 f16 MFMA)
-//   O^T[512 x 16 heads]    += V^T[512 x 32] . P^T[32 x 16]  (16x16x32 f16 MFMA)
-// with an online softmax in fp32 (exp2 domain).  The same tile serves both products:
+// Structure: one workgroup per (query, chunk of its row list, 16-head group); the head
+// groups of one chunk run on one XCD and share its L2 for the gathered rows.  A
+// workgroup first resolves the chunk's row indices into LDS, then per 32-row step
+// gathers whole rows (coalesced 16-byte loads, two steps ahead of the one computing),
+// stores them into a row-major LDS tile (bf16 rows as they are, FP8 and FP4 rows
+// decoded exactly to fp16), and runs
+//   S^T[32 rows x 16 heads] = K[32 x 512] . Q^T            (16x16x32 MFMA)
+//   O^T[512 x 16 heads]    += V^T[512 x 32] . P^T[32 x 16]  (16x16x32 MFMA)
+// with an online softmax in fp32 (exp2 domain) whose reference maximum moves only when
+// a step's maximum exceeds it by more than 2^8.  The same tile serves both products:
 // K fragments are plain 16-byte LDS reads, V^T fragments come from transposing LDS
 // reads (ds_read_b64_tr_b16), so no transposed copy is ever written.
 //
-// Precision: FP8 (E4M3) and FP4 (E2M1 x E4M3) values are exact in fp16; bf16 values
-// are exact in fp16 from 2^-14 to 65504 (smaller magnitudes keep an absolute error
-// below 2^-25).  q is rounded to fp16 the same way.  Products are exact in fp32 and
-// accumulate in fp32; the probabilities (in [0, 1]) keep 11 significant bits.
+// Precision: bf16 rows meet the bf16 query on bf16 MFMA, each probability entering P.V
+// as two bf16 terms (about 16 significant bits).  FP8 (E4M3) and FP4 (E2M1 x E4M3)
+// values are exact in fp16 and meet the query rounded to fp16 (exact from 2^-14 to
+// 65504; smaller magnitudes keep an absolute error below 2^-25), probabilities as one
+// fp16 term.  Products are exact in fp32 and accumulate in fp32.
 // Each chunk writes (max, sum, unnormalised O) per head; a combine kernel merges the
 // chunks and rounds to bf16.
 #include "csakv_device.h"
@@ -260,10 +263,11 @@ __device__ __forceinline__ bool attn_block(int n_pairs, int n_groups, int n_chun
 // decode; each wave then computes the logits of all 16 heads (the K tile and the query
 // rows are shared in LDS) and the output for its own 128 dims.  NB = decode tiles (2
 // when the chunk has several steps, so that one barrier per step suffices).
-template <int KVFMT, bool CSA, int NB>
+template <int KVFMT, bool CSA, int NB, bool PG>
 __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t seq_stride,
-    int64_t n_rows_max, const int32_t* __restrict__ seq_rows, const uint16_t* __restrict__ q,
+    Paging pg, int64_t n_rows_max, const int32_t* __restrict__ seq_rows,
+    const uint16_t* __restrict__ q,
     int n_heads, float scale_log2,
     const int32_t* __restrict__ topk, int top_k, int window, int64_t n_list, int rows_per_chunk,
     int n_chunks, int n_pairs, float* __restrict__ part_o, float* __restrict__ part_ml) {
@@ -291,7 +295,8 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
   const int64_t n_c = n_rows - window;
 
   // Sequence row of every list position of the chunk (-1: absent or out of range), and
-  // two steps of -1 past the end for the fetches that run ahead of the last step.
+  // two steps of -1 past the end for the fetches that run ahead of the last step; for a
+  // paged cache, the row's place in the page pool instead.
   for (int i = threadIdx.x; i < (n_steps + 2) * kStepRows; i += kAttnThreads) {
     const int64_t p = p_begin + i;
     int row = -1;
@@ -303,6 +308,9 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
         row = (j >= 0 && j < n_c) ? window + j : -1;
       }
     }
+    if (PG && row >= 0)
+      row = (pg.table[(int64_t)b * pg.table_stride + (row >> pg.page_shift)] << pg.page_shift) +
+            (row & ((1 << pg.page_shift) - 1));
     s_rows[i] = row;
   }
   // The wave's logit B operands, kept in registers: wave w multiplies row tile w & 1
@@ -333,12 +341,14 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
   // loads, both fetched steps stay in flight across the step being computed.
   typedef StepRaw<KVFMT> Raw;
   Raw raw0, raw1;
-  const Rsrc rc = make_rsrc(codes + (int64_t)b * seq_stride * Raw::kRowBytes,
-                            (uint32_t)(n_rows * Raw::kRowBytes));
-  const Rsrc rs = Raw::kScaleRowBytes == 0
-                      ? rc
-                      : make_rsrc(scales + (int64_t)b * seq_stride * Raw::kScaleRowBytes,
-                                  (uint32_t)(n_rows * Raw::kScaleRowBytes));
+  // Rows are addressed inside the sequence's rows, or inside the page pool when paged.
+  const Rsrc rc = PG ? make_rsrc(codes, kAttnMaxSeqBytes)
+                           : make_rsrc(codes + (int64_t)b * seq_stride * Raw::kRowBytes,
+                                       (uint32_t)(n_rows * Raw::kRowBytes));
+  const Rsrc rs = Raw::kScaleRowBytes == 0 ? rc
+                  : PG ? make_rsrc(scales, kAttnMaxSeqBytes)
+                             : make_rsrc(scales + (int64_t)b * seq_stride * Raw::kScaleRowBytes,
+                                         (uint32_t)(n_rows * Raw::kScaleRowBytes));
   auto fetch = [&](Raw& raw, int step) { raw.load(rc, rs, s_rows + step * kStepRows, threadIdx.x); };
 
   auto run_step = [&](Raw& raw, int step) {
@@ -517,20 +527,24 @@ int attention_blocks(int batch, int n_heads, const AttnPlan& plan) {
 
 template <int KVFMT, bool CSA>
 void launch_chunks(hipStream_t stream, const uint8_t* codes, const uint8_t* scales,
-                   int64_t seq_stride, int64_t n_rows, const int32_t* seq_rows, const uint16_t* q,
-                   int batch, int n_heads,
+                   int64_t seq_stride, const Paging& pg, int64_t n_rows, const int32_t* seq_rows,
+                   const uint16_t* q, int batch, int n_heads,
                    float scale_log2, const int32_t* topk, int top_k, int window,
                    const AttnPlan& plan, float* part_o, float* part_ml) {
   const dim3 grid(attention_blocks(batch, n_heads, plan));
   const int n_pairs = batch * plan.n_chunks;
-#define CSAKV_CHUNK(NB)                                                                         \
-  hipLaunchKernelGGL((attention_chunk_kernel<KVFMT, CSA, NB>), grid, dim3(kAttnThreads), 0,      \
-                     stream, codes, scales, seq_stride, n_rows, seq_rows, q, n_heads, scale_log2, topk, \
-                     top_k, window, plan.n_list, plan.rows_per_chunk, plan.n_chunks, n_pairs,   \
-                     part_o, part_ml)
-  // One decode tile (55 KB of LDS: two workgroups per CU); the second tile's one barrier
-  // per step saved less than the halved occupancy cost.
-  CSAKV_CHUNK(1);
+#define CSAKV_CHUNK(NB, PG)                                                                     \
+  hipLaunchKernelGGL((attention_chunk_kernel<KVFMT, CSA, NB, PG>), grid, dim3(kAttnThreads), 0,  \
+                     stream, codes, scales, seq_stride, pg, n_rows, seq_rows, q, n_heads,         \
+                     scale_log2, topk, top_k, window, plan.n_list, plan.rows_per_chunk,           \
+                     plan.n_chunks, n_pairs, part_o, part_ml)
+  // One decode tile (42 KB of LDS); a second tile's one barrier per step saved less than
+  // the lower occupancy cost.  A paged cache has its own kernel so that the contiguous
+  // one carries no trace of the page lookup.
+  if (pg.table)
+    CSAKV_CHUNK(1, true);
+  else
+    CSAKV_CHUNK(1, false);
 #undef CSAKV_CHUNK
 }
 
@@ -605,8 +619,8 @@ size_t attention_workspace_bytes(int batch, int n_heads, const AttnPlan& plan) {
 }
 
 hipError_t launch_attention(int kv_fmt, bool csa, const uint8_t* codes, const uint8_t* scales,
-                            int64_t seq_stride, int64_t n_rows, const int32_t* seq_rows,
-                            const uint16_t* q, int batch,
+                            int64_t seq_stride, const Paging& pg, int64_t n_rows,
+                            const int32_t* seq_rows, const uint16_t* q, int batch,
                             int n_heads, float softmax_scale, const int32_t* topk, int top_k,
                             int window, const AttnPlan& plan, void* workspace, uint16_t* out,
                             hipStream_t stream) {
@@ -615,7 +629,7 @@ hipError_t launch_attention(int kv_fmt, bool csa, const uint8_t* codes, const ui
   const float sl2 = softmax_scale * kLog2e;
   if (plan.n_chunks > 0) {
 #define CSAKV_ATTN(F, C)                                                                        \
-  launch_chunks<F, C>(stream, codes, scales, seq_stride, n_rows, seq_rows, q, batch, n_heads, sl2, topk, \
+  launch_chunks<F, C>(stream, codes, scales, seq_stride, pg, n_rows, seq_rows, q, batch, n_heads, sl2, topk, \
                       top_k, window, plan, part_o, part_ml)
     if (csa) {
       if (kv_fmt == 0) CSAKV_ATTN(0, true);

@@ -25,7 +25,15 @@ csakv_status check_cache(const csakv_cache* c, bool is_kv) {
   if (!c || c->reserved != 0) return CSAKV_ERR_INVALID;
   const int nfmt = 3;  // csakv_kv_fmt, or csakv_idx_fmt
   if (c->fmt < 0 || c->fmt >= nfmt) return CSAKV_ERR_INVALID;
-  if (c->n_rows < 0 || c->seq_stride_rows < c->n_rows) return CSAKV_ERR_INVALID;
+  if (c->n_rows < 0) return CSAKV_ERR_INVALID;
+  if (c->block_table) {  // paged: power-of-two pages of at least 16 rows, a table row per sequence
+    const int32_t pr = c->page_rows;
+    if (pr < 16 || (pr & (pr - 1)) != 0 || !aligned(c->block_table, 4)) return CSAKV_ERR_INVALID;
+    if ((int64_t)c->table_stride * pr < c->n_rows || c->table_stride < 0) return CSAKV_ERR_INVALID;
+  } else {
+    if (c->page_rows != 0 || c->table_stride != 0) return CSAKV_ERR_INVALID;
+    if (c->seq_stride_rows < c->n_rows) return CSAKV_ERR_INVALID;
+  }
   // A cache without rows may have null pointers; any pointer given must be aligned.
   const bool empty = c->n_rows == 0;
   if ((!empty && !c->codes) || !aligned(c->codes, 16)) return CSAKV_ERR_INVALID;
@@ -37,6 +45,14 @@ csakv_status check_cache(const csakv_cache* c, bool is_kv) {
     return CSAKV_ERR_INVALID;
   }
   return CSAKV_OK;
+}
+
+// The paging descriptor of a validated cache.
+csakv::Paging paging(const csakv_cache* c) {
+  csakv::Paging pg{c->block_table, 0, c->table_stride};
+  if (c->block_table)
+    while ((1 << pg.page_shift) < c->page_rows) ++pg.page_shift;
+  return pg;
 }
 
 struct CsaLayout {
@@ -128,13 +144,14 @@ csakv_status csa_decode(const csakv_csa_params* p, const csakv_cache* kv,
   if (full) {
     hipError_t e = csakv::launch_indexer(
         idx_keys->fmt, static_cast<const uint8_t*>(idx_keys->codes), idx_keys->scales,
-        idx_keys->seq_stride_rows, n_c, idx_keys->seq_rows, q_idx, w_idx, p->batch,
-        p->n_idx_heads, p->top_k, L.idx, ws, topk, s);
+        idx_keys->seq_stride_rows, paging(idx_keys), n_c, idx_keys->seq_rows, q_idx, w_idx,
+        p->batch, p->n_idx_heads, p->top_k, L.idx, ws, topk, s);
     if (e != hipSuccess) return CSAKV_ERR_HIP;
   }
   return hip_status(csakv::launch_attention(
       kv->fmt, true, static_cast<const uint8_t*>(kv->codes), kv->scales, kv->seq_stride_rows,
-      kv->n_rows, kv->seq_rows, q, p->batch, p->n_q_heads, p->softmax_scale, topk, p->top_k,
+      paging(kv), kv->n_rows, kv->seq_rows, q, p->batch, p->n_q_heads, p->softmax_scale, topk,
+      p->top_k,
       p->window, L.attn,
       ws + L.attn_offset, out, s));
 }
@@ -164,8 +181,8 @@ csakv_status csa_select_topk(const csakv_csa_params* p, const csakv_cache* idx_k
   if (need > 0 && (!workspace || !aligned(workspace, kWsAlign))) return CSAKV_ERR_INVALID;
   return hip_status(csakv::launch_indexer(
       idx_keys->fmt, static_cast<const uint8_t*>(idx_keys->codes), idx_keys->scales,
-      idx_keys->seq_stride_rows, n_c, idx_keys->seq_rows, q_idx, w_idx, p->batch, p->n_idx_heads,
-      p->top_k, plan,
+      idx_keys->seq_stride_rows, paging(idx_keys), n_c, idx_keys->seq_rows, q_idx, w_idx, p->batch,
+      p->n_idx_heads, p->top_k, plan,
       workspace, topk, static_cast<hipStream_t>(stream)));
 }
 
@@ -190,8 +207,8 @@ csakv_status csa_reindex_topk(const csakv_csa_params* p, const csakv_cache* idx_
   if (pb < te && tb < pe) return CSAKV_ERR_INVALID;
   return hip_status(csakv::launch_reindex(
       idx_keys->fmt, static_cast<const uint8_t*>(idx_keys->codes), idx_keys->scales,
-      idx_keys->seq_stride_rows, n_c, idx_keys->seq_rows, q_idx, w_idx, p->batch, p->n_idx_heads,
-      pool, n_pool,
+      idx_keys->seq_stride_rows, paging(idx_keys), n_c, idx_keys->seq_rows, q_idx, w_idx, p->batch,
+      p->n_idx_heads, pool, n_pool,
       p->top_k, topk, static_cast<hipStream_t>(stream)));
 }
 
@@ -219,7 +236,8 @@ csakv_status hca_decode(int32_t batch, int32_t n_q_heads, float softmax_scale,
   csakv::AttnPlan a = csakv::plan_attention(batch, kv->n_rows, false, n_q_heads);
   return hip_status(csakv::launch_attention(
       kv->fmt, false, static_cast<const uint8_t*>(kv->codes), kv->scales, kv->seq_stride_rows,
-      kv->n_rows, kv->seq_rows, q, batch, n_q_heads, softmax_scale, nullptr, 0, 0, a, workspace, out,
+      paging(kv), kv->n_rows, kv->seq_rows, q, batch, n_q_heads, softmax_scale, nullptr, 0, 0, a,
+      workspace, out,
       static_cast<hipStream_t>(stream)));
 }
 

@@ -6,6 +6,15 @@
 
 namespace csakv {
 
+// Paged cache layout: row r of sequence b lives at pool row
+// table[b * table_stride + (r >> page_shift)] << page_shift | (r & (2^page_shift - 1)).
+// table == nullptr: each sequence's rows are contiguous at its seq_stride offset.
+struct Paging {
+  const int32_t* table;
+  int32_t page_shift;    // log2(rows per page), >= 4
+  int32_t table_stride;  // table entries per sequence
+};
+
 // ------------------------------------------------------------------ codecs
 hipError_t launch_quantize_fp4(const uint16_t* x, int64_t rows, int dim, uint8_t* codes,
                                uint8_t* scales, hipStream_t stream);
@@ -45,7 +54,7 @@ bool reindex_supported(int key_fmt, int64_t n_c);
 // seq_rows (here and below): NULL, or [B] device int32 rows of each sequence (clamped to
 // [0, n_c] or [0, n_rows]).
 hipError_t launch_reindex(int key_fmt, const uint8_t* codes, const uint8_t* scales,
-                          int64_t seq_stride, int64_t n_c, const int32_t* seq_rows,
+                          int64_t seq_stride, const Paging& pg, int64_t n_c, const int32_t* seq_rows,
                           const uint16_t* q_idx,
                           const float* w_idx, int batch, int n_heads, const int32_t* pool,
                           int n_pool, int top_k, int32_t* topk, hipStream_t stream);
@@ -55,7 +64,7 @@ bool indexer_supported(const IndexerPlan& plan);
 size_t indexer_workspace_bytes(int batch, const IndexerPlan& plan);
 
 hipError_t launch_indexer(int key_fmt, const uint8_t* codes, const uint8_t* scales,
-                          int64_t seq_stride, int64_t n_c, const int32_t* seq_rows,
+                          int64_t seq_stride, const Paging& pg, int64_t n_c, const int32_t* seq_rows,
                           const uint16_t* q_idx,
                           const float* w_idx, int batch, int n_heads, int top_k,
                           const IndexerPlan& plan, void* workspace, int32_t* topk,
@@ -81,8 +90,8 @@ size_t attention_workspace_bytes(int batch, int n_heads, const AttnPlan& plan);
 hipError_t launch_rope_output(uint16_t* out, int batch, int n_heads, const int64_t* positions,
                               double base, hipStream_t stream);
 hipError_t launch_attention(int kv_fmt, bool csa, const uint8_t* codes, const uint8_t* scales,
-                            int64_t seq_stride, int64_t n_rows, const int32_t* seq_rows,
-                            const uint16_t* q, int batch,
+                            int64_t seq_stride, const Paging& pg, int64_t n_rows,
+                            const int32_t* seq_rows, const uint16_t* q, int batch,
                             int n_heads, float softmax_scale, const int32_t* topk, int top_k,
                             int window, const AttnPlan& plan, void* workspace, uint16_t* out,
                             hipStream_t stream);

@@ -721,10 +721,11 @@ struct IndexerWs {
   uint32_t* scores;  // [B][n_c] score key of every row
 };
 
-template <class KT, int HT, bool QH>
+template <class KT, int HT, bool QH, bool PG>
 __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t seq_stride,
-    int64_t n_c, const int32_t* __restrict__ seq_rows, const uint16_t* __restrict__ q_idx,
+    const int32_t* __restrict__ page_table, int page_shift, int table_stride, int64_t n_c,
+    const int32_t* __restrict__ seq_rows, const uint16_t* __restrict__ q_idx,
     const float* __restrict__ w_idx, int n_heads, int n_slices, int slices_per_wg,
     int wg_per_query, int prefix, int cap, IndexerWs ws) {
   typedef typename KT::Op Op;
@@ -775,10 +776,20 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
     // The resource covers the rows from r0 to the end of the workgroup's rows; the tile
     // reads at most 16 of them.
     const int live = max(rows_wg - r0, 0);
-    const Rsrc rc = make_rsrc(kcodes + (int64_t)r0 * KT::kRowBytes, (uint32_t)(live * KT::kRowBytes));
-    const Rsrc rs = KT::kScales ? make_rsrc(kscales + (int64_t)r0 * (kIdxDim / 16),
-                                            (uint32_t)(live * (kIdxDim / 16)))
-                                : rc;
+    const uint8_t* tc = kcodes + (int64_t)r0 * KT::kRowBytes;
+    const uint8_t* ts = KT::kScales ? kscales + (int64_t)r0 * (kIdxDim / 16) : nullptr;
+    if constexpr (PG) {  // paged: a 16-row tile lies within one page (pages hold 2^k >= 16 rows)
+      const int64_t r = row_base + r0;  // row of the sequence
+      // (a tile past the end reads nothing; its table index is kept inside the table)
+      // (read-only and wave-uniform: a scalar load, waited for apart from the key loads)
+      const int64_t e = min(r >> page_shift, (int64_t)table_stride - 1);
+      const int64_t pr = ((int64_t)page_table[(int64_t)b * table_stride + e] << page_shift) +
+                         (r & ((1 << page_shift) - 1));
+      tc = codes + pr * KT::kRowBytes;
+      if (KT::kScales) ts = scales + pr * (kIdxDim / 16);
+    }
+    const Rsrc rc = make_rsrc(tc, (uint32_t)(live * KT::kRowBytes));
+    const Rsrc rs = KT::kScales ? make_rsrc(ts, (uint32_t)(live * (kIdxDim / 16))) : rc;
     kt.load(rc, rs, lane_co, lane_so);
   };
 
@@ -995,12 +1006,13 @@ constexpr uint32_t kAbsentKeyOffset = kReindexMaxSeqBytes;
 template <class KT, int HT, bool QH>
 __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t seq_stride,
-    int64_t n_c_max, const int32_t* __restrict__ seq_rows, const uint16_t* __restrict__ q_idx,
-    const float* __restrict__ w_idx, int n_heads, const int32_t* __restrict__ pool, int n_pool,
-    int top_k, int32_t* __restrict__ topk) {
+    Paging pg, int64_t n_c_max, const int32_t* __restrict__ seq_rows,
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx, int n_heads,
+    const int32_t* __restrict__ pool, int n_pool, int top_k, int32_t* __restrict__ topk) {
   typedef typename KT::Op Op;
   constexpr int NT = kReindexThreads;
   __shared__ int s_row[kMaxPool];        // pool rows, -1 for an empty slot
+  __shared__ int s_at[kMaxPool];         // where each pool row is stored (its page row if paged)
   __shared__ uint64_t s_key[kMaxPool];   // selection key of every slot, 0 when empty
   __shared__ uint64_t s_val[kMaxPool];   // the non-empty keys, in pool order
   __shared__ uint64_t s_list[kMergeListCap];
@@ -1012,7 +1024,12 @@ __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(
 
   for (int i = threadIdx.x; i < n_pool; i += NT) {
     const int32_t r = pool[(int64_t)b * n_pool + i];
-    s_row[i] = (r >= 0 && r < n_c) ? r : -1;
+    const int32_t row = (r >= 0 && r < n_c) ? r : -1;
+    s_row[i] = row;
+    s_at[i] = row < 0 || !pg.table
+                  ? row
+                  : (pg.table[(int64_t)b * pg.table_stride + (row >> pg.page_shift)] << pg.page_shift) +
+                        (row & ((1 << pg.page_shift) - 1));
   }
   Op qa[HT][4];
   float wv[HT][4];
@@ -1021,15 +1038,18 @@ __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(
                           reinterpret_cast<float*>(sm.hist));
   lds_barrier();
 
-  const Rsrc rc = make_rsrc(codes + (int64_t)b * seq_stride * KT::kRowBytes,
-                            (uint32_t)(n_c * KT::kRowBytes));
-  const Rsrc rs = KT::kScales ? make_rsrc(scales + (int64_t)b * seq_stride * (kIdxDim / 16),
-                                          (uint32_t)(n_c * (kIdxDim / 16)))
-                              : rc;
+  // Rows are addressed inside the sequence's rows, or inside the page pool when paged.
+  const Rsrc rc = pg.table ? make_rsrc(codes, kReindexMaxSeqBytes)
+                           : make_rsrc(codes + (int64_t)b * seq_stride * KT::kRowBytes,
+                                       (uint32_t)(n_c * KT::kRowBytes));
+  const Rsrc rs = !KT::kScales ? rc
+                  : pg.table   ? make_rsrc(scales, kReindexMaxSeqBytes)
+                               : make_rsrc(scales + (int64_t)b * seq_stride * (kIdxDim / 16),
+                                           (uint32_t)(n_c * (kIdxDim / 16)));
   const int n_tiles = (n_pool + 15) / 16;
-  auto slot_row = [&](int t) -> int {  // pool row of lane n in tile t (-1: none)
+  auto slot_row = [&](int t) -> int {  // stored row of lane n's pool row in tile t (-1: none)
     const int pos = 16 * t + n;
-    return pos < n_pool ? s_row[pos < kMaxPool ? pos : kMaxPool - 1] : -1;
+    return pos < n_pool ? s_at[pos < kMaxPool ? pos : kMaxPool - 1] : -1;
   };
   auto load_tile = [&](KT& kt, int t) {
     const int row = slot_row(t);
@@ -1100,13 +1120,13 @@ __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(
 
 template <class KT, bool QH>
 void launch_reindex_ht(int ht, hipStream_t stream, const uint8_t* codes, const uint8_t* scales,
-                       int64_t seq_stride, int64_t n_c, const int32_t* seq_rows, const uint16_t* q_idx, const float* w_idx,
-                       int batch, int n_heads, const int32_t* pool, int n_pool, int top_k,
-                       int32_t* topk) {
-#define CSAKV_REINDEX(H)                                                                        \
-  hipLaunchKernelGGL((reindex_kernel<KT, H, QH>), dim3(batch), dim3(kReindexThreads), 0, stream,   \
-                     codes, scales, seq_stride, n_c, seq_rows, q_idx, w_idx, n_heads, pool, n_pool, top_k, \
-                     topk)
+                       int64_t seq_stride, const Paging& pg, int64_t n_c, const int32_t* seq_rows,
+                       const uint16_t* q_idx, const float* w_idx, int batch, int n_heads,
+                       const int32_t* pool, int n_pool, int top_k, int32_t* topk) {
+#define CSAKV_REINDEX(H)                                                                      \
+  hipLaunchKernelGGL((reindex_kernel<KT, H, QH>), dim3(batch), dim3(kReindexThreads), 0, stream, \
+                     codes, scales, seq_stride, pg, n_c, seq_rows, q_idx, w_idx, n_heads, pool,  \
+                     n_pool, top_k, topk)
   switch (ht) {
     case 1: CSAKV_REINDEX(1); break;
     case 2: CSAKV_REINDEX(2); break;
@@ -1118,20 +1138,33 @@ void launch_reindex_ht(int ht, hipStream_t stream, const uint8_t* codes, const u
 
 template <class KT, int HT, bool QH>
 void launch_scan(hipStream_t stream, const uint8_t* codes, const uint8_t* scales,
-                 int64_t seq_stride, int64_t n_c, const int32_t* seq_rows, const uint16_t* q_idx, const float* w_idx,
-                 int batch, int n_heads, const IndexerPlan& plan, const IndexerWs& ws) {
-  hipLaunchKernelGGL((indexer_scan_kernel<KT, HT, QH>), dim3(batch * plan.wg_per_query),
-                     dim3(kScanThreads), 0, stream, codes, scales, seq_stride, n_c, seq_rows, q_idx, w_idx,
-                     n_heads, plan.n_slices, plan.slices_per_wg, plan.wg_per_query, plan.prefix,
-                     plan.cap, ws);
+                 int64_t seq_stride, const Paging& pg, int64_t n_c, const int32_t* seq_rows,
+                 const uint16_t* q_idx, const float* w_idx, int batch, int n_heads,
+                 const IndexerPlan& plan, const IndexerWs& ws) {
+  // The paged variant is its own kernel: a table lookup behind a branch in the tile
+  // loop would make the compiler wait for every key load in flight at each tile.
+  if (pg.table)
+    hipLaunchKernelGGL((indexer_scan_kernel<KT, HT, QH, true>), dim3(batch * plan.wg_per_query),
+                       dim3(kScanThreads), 0, stream, codes, scales, seq_stride, pg.table, pg.page_shift,
+                       pg.table_stride, n_c, seq_rows,
+                       q_idx, w_idx, n_heads, plan.n_slices, plan.slices_per_wg, plan.wg_per_query,
+                       plan.prefix, plan.cap, ws);
+  else
+    hipLaunchKernelGGL((indexer_scan_kernel<KT, HT, QH, false>), dim3(batch * plan.wg_per_query),
+                       dim3(kScanThreads), 0, stream, codes, scales, seq_stride, pg.table, pg.page_shift,
+                       pg.table_stride, n_c, seq_rows,
+                       q_idx, w_idx, n_heads, plan.n_slices, plan.slices_per_wg, plan.wg_per_query,
+                       plan.prefix, plan.cap, ws);
 }
 
 template <class KT, bool QH = false>
 void launch_scan_ht(int ht, hipStream_t stream, const uint8_t* codes, const uint8_t* scales,
-                    int64_t seq_stride, int64_t n_c, const int32_t* seq_rows, const uint16_t* q_idx, const float* w_idx,
-                    int batch, int n_heads, const IndexerPlan& plan, const IndexerWs& ws) {
-#define CSAKV_SCAN(H) \
-  launch_scan<KT, H, QH>(stream, codes, scales, seq_stride, n_c, seq_rows, q_idx, w_idx, batch, n_heads, plan, ws)
+                    int64_t seq_stride, const Paging& pg, int64_t n_c, const int32_t* seq_rows,
+                    const uint16_t* q_idx, const float* w_idx, int batch, int n_heads,
+                    const IndexerPlan& plan, const IndexerWs& ws) {
+#define CSAKV_SCAN(H)                                                                         \
+  launch_scan<KT, H, QH>(stream, codes, scales, seq_stride, pg, n_c, seq_rows, q_idx, w_idx,    \
+                         batch, n_heads, plan, ws)
   switch (ht) {
     case 1: CSAKV_SCAN(1); break;
     case 2: CSAKV_SCAN(2); break;
@@ -1195,21 +1228,21 @@ bool indexer_supported(const IndexerPlan& plan) {
 }
 
 hipError_t launch_indexer(int key_fmt, const uint8_t* codes, const uint8_t* scales,
-                          int64_t seq_stride, int64_t n_c, const int32_t* seq_rows, const uint16_t* q_idx,
-                          const float* w_idx, int batch, int n_heads, int top_k,
-                          const IndexerPlan& plan, void* workspace, int32_t* topk,
-                          hipStream_t stream) {
+                          int64_t seq_stride, const Paging& pg, int64_t n_c,
+                          const int32_t* seq_rows, const uint16_t* q_idx, const float* w_idx,
+                          int batch, int n_heads, int top_k, const IndexerPlan& plan,
+                          void* workspace, int32_t* topk, hipStream_t stream) {
   const IndexerWs ws = carve_indexer_ws(workspace, batch, plan);
   if (plan.n_slices > 0) {
     const int ht = (n_heads + 15) / 16;
     if (key_fmt == 0)
-      launch_scan_ht<KeyTileBf16>(ht, stream, codes, scales, seq_stride, n_c, seq_rows, q_idx, w_idx, batch,
+      launch_scan_ht<KeyTileBf16>(ht, stream, codes, scales, seq_stride, pg, n_c, seq_rows, q_idx, w_idx, batch,
                                   n_heads, plan, ws);
     else if (key_fmt == 1)
-      launch_scan_ht<KeyTileFp4>(ht, stream, codes, scales, seq_stride, n_c, seq_rows, q_idx, w_idx, batch,
+      launch_scan_ht<KeyTileFp4>(ht, stream, codes, scales, seq_stride, pg, n_c, seq_rows, q_idx, w_idx, batch,
                                  n_heads, plan, ws);
     else  // Hadamard-rotated FP4 keys: the query is rotated and quantised the same way
-      launch_scan_ht<KeyTileFp4, true>(ht, stream, codes, scales, seq_stride, n_c, seq_rows, q_idx, w_idx,
+      launch_scan_ht<KeyTileFp4, true>(ht, stream, codes, scales, seq_stride, pg, n_c, seq_rows, q_idx, w_idx,
                                        batch, n_heads, plan, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1225,18 +1258,19 @@ bool reindex_supported(int key_fmt, int64_t n_c) {
 }
 
 hipError_t launch_reindex(int key_fmt, const uint8_t* codes, const uint8_t* scales,
-                          int64_t seq_stride, int64_t n_c, const int32_t* seq_rows, const uint16_t* q_idx,
-                          const float* w_idx, int batch, int n_heads, const int32_t* pool,
-                          int n_pool, int top_k, int32_t* topk, hipStream_t stream) {
+                          int64_t seq_stride, const Paging& pg, int64_t n_c,
+                          const int32_t* seq_rows, const uint16_t* q_idx, const float* w_idx,
+                          int batch, int n_heads, const int32_t* pool, int n_pool, int top_k,
+                          int32_t* topk, hipStream_t stream) {
   const int ht = (n_heads + 15) / 16;
   if (key_fmt == 0)
-    launch_reindex_ht<KeyTileBf16, false>(ht, stream, codes, scales, seq_stride, n_c, seq_rows, q_idx, w_idx,
+    launch_reindex_ht<KeyTileBf16, false>(ht, stream, codes, scales, seq_stride, pg, n_c, seq_rows, q_idx, w_idx,
                                           batch, n_heads, pool, n_pool, top_k, topk);
   else if (key_fmt == 1)
-    launch_reindex_ht<KeyTileFp4, false>(ht, stream, codes, scales, seq_stride, n_c, seq_rows, q_idx, w_idx,
+    launch_reindex_ht<KeyTileFp4, false>(ht, stream, codes, scales, seq_stride, pg, n_c, seq_rows, q_idx, w_idx,
                                          batch, n_heads, pool, n_pool, top_k, topk);
   else
-    launch_reindex_ht<KeyTileFp4, true>(ht, stream, codes, scales, seq_stride, n_c, seq_rows, q_idx, w_idx,
+    launch_reindex_ht<KeyTileFp4, true>(ht, stream, codes, scales, seq_stride, pg, n_c, seq_rows, q_idx, w_idx,
                                         batch, n_heads, pool, n_pool, top_k, topk);
   return hipGetLastError();
 }

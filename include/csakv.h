@@ -86,7 +86,15 @@ typedef enum { CSAKV_MODE_FULL = 0, CSAKV_MODE_REUSE = 1, CSAKV_MODE_REINDEX = 2
  * [0, seq_rows[b]) (values are clamped to [0, n_rows], so n_rows is the capacity).
  * For a CSA layer the shared-KV lengths are window + N_c(b) and the indexer-key
  * lengths N_c(b); each query selects among, and attends over, its own rows only
- * (a sequence shorter than the window attends over the window rows it holds). */
+ * (a sequence shorter than the window attends over the window rows it holds).
+ * Paged layout (block_table != NULL): `codes` (and `scales`) hold a pool of pages of
+ * page_rows rows each, page p's rows starting at row p * page_rows of the pool; row r
+ * of sequence b lives at row r % page_rows of page block_table[b * table_stride +
+ * r / page_rows].  page_rows is a multiple of 16; table_stride >= ceil(n_rows /
+ * page_rows); seq_stride_rows is then unused; every page id a sequence's rows reach
+ * must name a page of the pool, and the pool's codes (and scales) must span at most
+ * 4 GiB - 256 bytes.  Decode-step writes into a paged pool go through kv_cache_write
+ * with the pool viewed as one sequence and physical rows (page * page_rows + offset). */
 typedef struct {
   int32_t fmt;              /* csakv_kv_fmt for shared-KV, csakv_idx_fmt for keys */
   int32_t reserved;         /* must be 0                                            */
@@ -95,6 +103,9 @@ typedef struct {
   const void* codes;
   const uint8_t* scales;
   const int32_t* seq_rows;  /* NULL, or [B] device int32 rows of each sequence      */
+  const int32_t* block_table; /* NULL (contiguous), or [B][table_stride] page ids   */
+  int32_t page_rows;        /* paged: rows per page (multiple of 16); else 0        */
+  int32_t table_stride;     /* paged: page-table entries per sequence; else 0       */
 } csakv_cache;
 
 typedef struct {

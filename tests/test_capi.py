@@ -126,6 +126,14 @@ def test_csa_rejects_bad_pointers_and_shapes():
     assert _call(p, kv=stride, idx=IDX) == ck.ERR_INVALID
     lens_misaligned = ck.Cache(ck.IDX_BF16, 0, 1024, 1024, FAKE, None, FAKE + 2)
     assert _call(p, idx=lens_misaligned) == ck.ERR_INVALID                 # per-sequence lengths
+    # paged layouts: pages of 2^k >= 16 rows, a table row covering n_rows, an aligned table
+    for pr, ts, table in [(48, 32, FAKE), (8, 128, FAKE), (64, 15, FAKE), (64, 16, FAKE + 2)]:
+        paged = ck.Cache(ck.IDX_BF16, 0, 1024, 0, FAKE, None, None, table, pr, ts)
+        assert _call(p, idx=paged) == ck.ERR_INVALID, (pr, ts)
+    pages_without_table = ck.Cache(ck.IDX_BF16, 0, 1024, 1024, FAKE, None, None, None, 64, 16)
+    assert _call(p, idx=pages_without_table) == ck.ERR_INVALID
+    paged_ok = ck.Cache(ck.IDX_BF16, 0, 1024, 0, FAKE, None, None, FAKE, 64, 16)
+    assert _call(p, idx=paged_ok, ws_bytes=0) == ck.ERR_WORKSPACE          # accepted up to the workspace
     need = ck.csa_decode_workspace_bytes(p, 1024)
     assert need > 0
     assert _call(p, idx=IDX, ws_bytes=need - 1) == ck.ERR_WORKSPACE
