@@ -288,38 +288,20 @@ __device__ void block_select2(KeyAt key_at, int n, int ra, int rb, SelectSmem& s
   *tb = t[1];
 }
 
-// Lower edge *t of the histogram bin that holds the P-th largest of the 32-bit values
-// v[0..n) (1 <= P <= n), and *cnt = how many values are >= *t.  The 2048 bins split
-// [min, max] evenly (by a power of two), so one pass places P; no ranking inside the bin.
-template <int NT>
-__device__ void slice_threshold(const uint32_t* v, int n, int P, SelectSmem& sm, uint32_t* t,
-                                uint32_t* cnt) {
-  constexpr int nw = NT / kWave;
+// Lower edge *t of the histogram bin that holds the P-th largest of the block's valid
+// 32-bit keys (thread t holds key[r] of row t + NT*r, valid when that row is below n;
+// 1 <= P <= n), and *cnt = how many keys are >= *t.  mn and mx are the keys' minimum
+// and maximum; sm.hist must be zero.  The 2048 bins split [mn, mx] evenly (by a power
+// of two), so one pass places P; no ranking inside the bin.
+template <int NT, int R>
+__device__ void slice_threshold(const uint32_t (&key)[R], int n, int P, uint32_t mn, uint32_t mx,
+                                SelectSmem& sm, uint32_t* t, uint32_t* cnt) {
   constexpr int bpt = kHistBins / NT;
-  const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  uint32_t mn = ~0u, mx = 0u;
-  for (int i = threadIdx.x; i < n; i += NT) {
-    const uint32_t x = v[i];
-    mn = x < mn ? x : mn;
-    mx = x > mx ? x : mx;
-  }
-  for (int i = threadIdx.x; i < kHistBins; i += NT) sm.hist[i] = 0;
-  wave_minmax_u32(mn, mx);
-  if (lane == 0) {
-    sm.red32[w] = mn;
-    sm.red32[16 + w] = mx;
-  }
-  lds_barrier();
-  mn = sm.red32[0];
-  mx = sm.red32[16];
-#pragma unroll
-  for (int i = 1; i < nw; ++i) {
-    mn = sm.red32[i] < mn ? sm.red32[i] : mn;
-    mx = sm.red32[16 + i] > mx ? sm.red32[16 + i] : mx;
-  }
   const uint32_t range = mx - mn;
   const int sh = range == 0 ? 0 : max(0, 32 - __builtin_clz(range) - 11);
-  for (int i = threadIdx.x; i < n; i += NT) atomicAdd(&sm.hist[(v[i] - mn) >> sh], 1u);
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if ((int)threadIdx.x + NT * r < n) atomicAdd(&sm.hist[(key[r] - mn) >> sh], 1u);
   lds_barrier();
   const int b0 = threadIdx.x * bpt;
   uint32_t own = 0;
@@ -843,28 +825,71 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
     const int64_t srow0 = row_base + (int64_t)j * kSliceRows;
     const int rows = (int)min((int64_t)kSliceRows, n_cb - srow0);
     const int64_t si = (int64_t)b * n_slices + slice0 + j;
-    lds_barrier();
+    lds_barrier();  // every wave's shares of the slice are in
+    // Thread t adds up the shares of rows t + 512r and keeps their keys in registers, on
+    // the way clearing the histogram and taking the keys' minimum and maximum.
+    constexpr int kRpt = kSliceRows / kScanThreads;
     uint32_t* sc_out = ws.scores + (int64_t)b * n_c + srow0;
-    for (int i = threadIdx.x; i < rows; i += kScanThreads) {
-      const f32x4 p = *reinterpret_cast<const f32x4*>(s_part + 4 * i);
-      const uint32_t key = f32_order_key((p[0] + p[1]) + (p[2] + p[3]));
-      s_score[i] = key;
-      sc_out[i] = key;
+    uint32_t key[kRpt];
+    uint32_t mn = ~0u, mx = 0u;
+#pragma unroll
+    for (int r = 0; r < kRpt; ++r) {
+      const int i = threadIdx.x + kScanThreads * r;
+      key[r] = 0u;
+      if (i < rows) {
+        const f32x4 p = *reinterpret_cast<const f32x4*>(s_part + 4 * i);
+        key[r] = f32_order_key((p[0] + p[1]) + (p[2] + p[3]));
+        s_score[i] = key[r];
+        sc_out[i] = key[r];
+        mn = key[r] < mn ? key[r] : mn;
+        mx = key[r] > mx ? key[r] : mx;
+      }
+    }
+    for (int i = threadIdx.x; i < kHistBins; i += kScanThreads) sm.hist[i] = 0;
+    wave_minmax_u32(mn, mx);
+    if (lane == 0) {
+      sm.red32[wave] = mn;
+      sm.red32[16 + wave] = mx;
     }
     lds_barrier();
+    mn = sm.red32[0];
+    mx = sm.red32[16];
+#pragma unroll
+    for (int w = 1; w < kScanWaves; ++w) {
+      mn = sm.red32[w] < mn ? sm.red32[w] : mn;
+      mx = sm.red32[16 + w] > mx ? sm.red32[16 + w] : mx;
+    }
     const int pe = min(prefix, rows);
     uint32_t t32 = 0u, cnt = (uint32_t)rows;
-    if (pe < rows) slice_threshold<kScanThreads>(s_score, rows, pe, sm, &t32, &cnt);
+    if (pe < rows) slice_threshold<kScanThreads>(key, rows, pe, mn, mx, sm, &t32, &cnt);
     uint64_t* dst = ws.cand + si * cap;
     uint64_t bound;
     uint32_t emitted;
-    if (cnt <= (uint32_t)cap) {  // every key whose score is >= t32
-      uint32_t c = 0;
-      for (int i = threadIdx.x; i < rows; i += kScanThreads) c += s_score[i] >= t32;
-      uint32_t pos = block_exclusive_scan<kScanThreads>(c, sm.wsum, &emitted);
-      for (int i = threadIdx.x; i < rows; i += kScanThreads) {
-        const uint32_t v = s_score[i];
-        if (v >= t32) dst[pos++] = compose_key(v, (uint32_t)(srow0 + i));
+    if (cnt <= (uint32_t)cap) {  // every key whose score is >= t32, wave by wave, row order
+      uint32_t wc = 0;
+#pragma unroll
+      for (int r = 0; r < kRpt; ++r)
+        wc += (uint32_t)__builtin_popcountll(
+            __ballot((int)threadIdx.x + kScanThreads * r < rows && key[r] >= t32));
+      if (lane == 0) sm.wsum[wave] = wc;
+      lds_barrier();
+      uint32_t pos = 0;
+      emitted = 0;
+#pragma unroll
+      for (int w = 0; w < kScanWaves; ++w) {
+        const uint32_t c = sm.wsum[w];
+        pos += w < wave ? c : 0u;
+        emitted += c;
+      }
+#pragma unroll
+      for (int r = 0; r < kRpt; ++r) {
+        const int i = threadIdx.x + kScanThreads * r;
+        const bool take = i < rows && key[r] >= t32;
+        const uint64_t m = __ballot(take);
+        if (take)
+          dst[pos + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] =
+              compose_key(key[r], (uint32_t)(srow0 + i));
+        pos += (uint32_t)__builtin_popcountll(m);
       }
       bound = pe < rows ? ((uint64_t)t32 << 32) : 0ull;
     } else {  // too many keys share the boundary bin: the exact top-cap instead
