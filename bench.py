@@ -188,6 +188,8 @@ def run_gpu(w: dict, steps: int, warmup: int, replicas: int | None):
         ws_bytes = max(ck.csa_select_topk_workspace_bytes(p_pool, w["n_c"]),
                        ck.csa_decode_workspace_bytes(p_reuse, w["n_c"]))
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+        rx_bytes = ck.csa_reindex_topk_workspace_bytes(p_rx, P)
+        rx_ws = torch.empty(rx_bytes, dtype=torch.uint8, device="cuda")
 
         def step(i):
             r = reps[i % R]
@@ -195,7 +197,7 @@ def run_gpu(w: dict, steps: int, warmup: int, replicas: int | None):
                                stream=sh)
             for layer in range(w["layers"]):
                 ck.csa_reindex_topk(p_rx, r["idx"], r["qi"][layer], r["w"][layer], r["pool"], P,
-                                    r["topk"], stream=sh)
+                                    r["topk"], rx_ws, rx_bytes, stream=sh)
                 ck.csa_decode(p_reuse, r["kv"][layer], None, r["q"][layer], None, None, r["topk"],
                               r["out"][layer], ws, ws_bytes, stream=sh)
 

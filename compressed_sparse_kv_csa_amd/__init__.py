@@ -16,7 +16,8 @@ __all__ = [
     "MODE_FULL",
     "MODE_REUSE", "MODE_REINDEX", "CsaParams", "Cache", "KvCacheSpec", "KvCacheBreakdown", "lib", "lib_path",
     "cache", "csa_decode_workspace_bytes", "csa_decode", "csa_select_topk_workspace_bytes",
-    "csa_select_topk", "csa_reindex_topk", "hca_decode_workspace_bytes",
+    "csa_select_topk", "csa_reindex_topk", "csa_reindex_topk_workspace_bytes",
+    "hca_decode_workspace_bytes",
     "hca_decode", "rope_output", "kv_quantize_fp4", "kv_quantize_fp8", "idx_quantize_fp4_hadamard",
     "kv_cache_write", "kv_dequantize",
     "kv_cache_bytes", "csakv_status_string", "EXPORTED_SYMBOLS",
@@ -30,8 +31,8 @@ OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 
 EXPORTED_SYMBOLS = (
     "csa_decode_workspace_bytes", "csa_decode", "csa_select_topk_workspace_bytes",
-    "csa_select_topk", "csa_reindex_topk", "hca_decode_workspace_bytes", "hca_decode",
-    "rope_output", "kv_quantize_fp4", "kv_quantize_fp8", "idx_quantize_fp4_hadamard", "kv_cache_write",
+    "csa_select_topk", "csa_reindex_topk", "csa_reindex_topk_workspace_bytes",
+    "hca_decode_workspace_bytes", "hca_decode", "rope_output", "kv_quantize_fp4", "kv_quantize_fp8", "idx_quantize_fp4_hadamard", "kv_cache_write",
     "kv_dequantize", "kv_cache_bytes", "csakv_status_string",
 )
 
@@ -98,8 +99,10 @@ def lib() -> ctypes.CDLL:
         L.csa_select_topk_workspace_bytes.restype = SZ
         L.csa_select_topk.argtypes = [P(CsaParams), P(Cache), VP, VP, VP, VP, SZ, VP]
         L.csa_select_topk.restype = I32
-        L.csa_reindex_topk.argtypes = [P(CsaParams), P(Cache), VP, VP, VP, I32, VP, VP]
+        L.csa_reindex_topk.argtypes = [P(CsaParams), P(Cache), VP, VP, VP, I32, VP, VP, SZ, VP]
         L.csa_reindex_topk.restype = I32
+        L.csa_reindex_topk_workspace_bytes.argtypes = [P(CsaParams), I32]
+        L.csa_reindex_topk_workspace_bytes.restype = SZ
         L.hca_decode_workspace_bytes.argtypes = [I32, I32, I64]
         L.hca_decode_workspace_bytes.restype = SZ
         L.hca_decode.argtypes = [I32, I32, F, P(Cache), VP, VP, VP, SZ, VP]
@@ -202,11 +205,19 @@ def csa_select_topk(params: CsaParams, idx_keys: Cache, q_idx, w_idx, topk, work
     return st
 
 
+def csa_reindex_topk_workspace_bytes(params: CsaParams, n_pool: int) -> int:
+    return int(lib().csa_reindex_topk_workspace_bytes(ctypes.byref(params), int(n_pool)))
+
+
 def csa_reindex_topk(params: CsaParams, idx_keys: Cache, q_idx, w_idx, pool, n_pool: int, topk,
-                     stream=None, check: bool = True) -> int:
+                     workspace, workspace_bytes: int | None = None, stream=None,
+                     check: bool = True) -> int:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     keys = ctypes.byref(idx_keys) if idx_keys is not None else None
     st = lib().csa_reindex_topk(ctypes.byref(params), keys, _ptr(q_idx),
-                                _ptr(w_idx), _ptr(pool), int(n_pool), _ptr(topk), _stream(stream))
+                                _ptr(w_idx), _ptr(pool), int(n_pool), _ptr(topk),
+                                _ptr(workspace), int(workspace_bytes), _stream(stream))
     if check:
         _check(st, "csa_reindex_topk")
     return st

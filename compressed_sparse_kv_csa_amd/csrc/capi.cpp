@@ -186,9 +186,17 @@ csakv_status csa_select_topk(const csakv_csa_params* p, const csakv_cache* idx_k
       workspace, topk, static_cast<hipStream_t>(stream)));
 }
 
+size_t csa_reindex_topk_workspace_bytes(const csakv_csa_params* p, int32_t n_pool) {
+  if (!p || p->mode != CSAKV_MODE_REINDEX || check_select_params(p) != CSAKV_OK || n_pool < 1 ||
+      n_pool > csakv::kMaxPool)
+    return 0;
+  return round_up(csakv::reindex_workspace_bytes(p->batch, n_pool), kWsAlign);
+}
+
 csakv_status csa_reindex_topk(const csakv_csa_params* p, const csakv_cache* idx_keys,
                               const uint16_t* q_idx, const float* w_idx, const int32_t* pool,
-                              int32_t n_pool, int32_t* topk, void* stream) {
+                              int32_t n_pool, int32_t* topk, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   if (!p || p->mode != CSAKV_MODE_REINDEX) return CSAKV_ERR_INVALID;
   csakv_status st = check_select_params(p);
   if (st != CSAKV_OK) return st;
@@ -205,11 +213,14 @@ csakv_status csa_reindex_topk(const csakv_csa_params* p, const csakv_cache* idx_
   const uintptr_t pb = reinterpret_cast<uintptr_t>(pool), tb = reinterpret_cast<uintptr_t>(topk);
   const uintptr_t pe = pb + (uintptr_t)p->batch * n_pool * 4, te = tb + (uintptr_t)p->batch * p->top_k * 4;
   if (pb < te && tb < pe) return CSAKV_ERR_INVALID;
+  const size_t need = round_up(csakv::reindex_workspace_bytes(p->batch, n_pool), kWsAlign);
+  if (workspace_bytes < need) return CSAKV_ERR_WORKSPACE;
+  if (!workspace || !aligned(workspace, kWsAlign)) return CSAKV_ERR_INVALID;
   return hip_status(csakv::launch_reindex(
       idx_keys->fmt, static_cast<const uint8_t*>(idx_keys->codes), idx_keys->scales,
       idx_keys->seq_stride_rows, paging(idx_keys), n_c, idx_keys->seq_rows, q_idx, w_idx, p->batch,
       p->n_idx_heads, pool, n_pool,
-      p->top_k, topk, static_cast<hipStream_t>(stream)));
+      p->top_k, topk, workspace, static_cast<hipStream_t>(stream)));
 }
 
 size_t hca_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int64_t n_rows) {

@@ -53,11 +53,14 @@ constexpr uint32_t kReindexMaxSeqBytes = 0xFFFFFF00u;
 bool reindex_supported(int key_fmt, int64_t n_c);
 // seq_rows (here and below): NULL, or [B] device int32 rows of each sequence (clamped to
 // [0, n_c] or [0, n_rows]).
+// The workspace holds the selection key of every pool slot ([B][n_pool] uint64).
+size_t reindex_workspace_bytes(int batch, int n_pool);
 hipError_t launch_reindex(int key_fmt, const uint8_t* codes, const uint8_t* scales,
                           int64_t seq_stride, const Paging& pg, int64_t n_c, const int32_t* seq_rows,
                           const uint16_t* q_idx,
                           const float* w_idx, int batch, int n_heads, const int32_t* pool,
-                          int n_pool, int top_k, int32_t* topk, hipStream_t stream);
+                          int n_pool, int top_k, int32_t* topk, void* workspace,
+                          hipStream_t stream);
 
 IndexerPlan plan_indexer(int batch, int64_t n_c, int top_k);
 bool indexer_supported(const IndexerPlan& plan);

@@ -1018,51 +1018,48 @@ __global__ __launch_bounds__(kMergeThreads) void indexer_merge_kernel(
 
 // ------------------------------------------------------------------ CSA2 reindex
 
-// One workgroup per query re-ranks the query's candidate pool with its own indexer
-// query: lane (g, n) of a 16-row tile reads pool row pool[16t + n], the tile is scored
-// exactly as in the scan, and the top-k of the pool is selected in LDS.  Rows are
-// addressed by 32-bit offsets inside a buffer resource over the query's sequence; an
-// empty slot (and every tile past the end) is read past that range, which returns
-// zeros without touching memory.
-constexpr int kReindexThreads = 512;
-constexpr int kReindexWaves = kReindexThreads / kWave;
+// Two launches.  The score kernel spreads the pool over many workgroups: each one scores
+// kReindexPartRows pool slots of one query, lane (g, n) of wave w reading pool row
+// pool[part * kReindexPartRows + 16w + n], exactly as the scan scores a tile, and leaves
+// every slot's selection key (0 for an empty slot) in the workspace.  The select kernel
+// then keeps the top-k of each query's keys in LDS.  Rows are addressed by 32-bit
+// offsets inside a buffer resource over the query's sequence (or the page pool); an
+// empty slot is read past that range, which returns zeros without touching memory.
+constexpr int kReindexScoreWaves = 4;
+constexpr int kReindexScoreThreads = kReindexScoreWaves * kWave;
+constexpr int kReindexPartRows = 16 * kReindexScoreWaves;  // one tile per wave
+constexpr int kReindexThreads = 512;                        // select kernel
 constexpr uint32_t kAbsentKeyOffset = kReindexMaxSeqBytes;
 
 template <class KT, int HT, bool QH>
-__global__ __launch_bounds__(kReindexThreads) void reindex_kernel(
+__global__ __launch_bounds__(kReindexScoreThreads) void reindex_score_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t seq_stride,
     Paging pg, int64_t n_c_max, const int32_t* __restrict__ seq_rows,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx, int n_heads,
-    const int32_t* __restrict__ pool, int n_pool, int top_k, int32_t* __restrict__ topk) {
+    const int32_t* __restrict__ pool, int n_pool, int n_parts, uint64_t* __restrict__ keys) {
   typedef typename KT::Op Op;
-  constexpr int NT = kReindexThreads;
-  __shared__ int s_row[kMaxPool];        // pool rows, -1 for an empty slot
-  __shared__ int s_at[kMaxPool];         // where each pool row is stored (its page row if paged)
-  __shared__ uint64_t s_key[kMaxPool];   // selection key of every slot, 0 when empty
-  __shared__ uint64_t s_val[kMaxPool];   // the non-empty keys, in pool order
-  __shared__ uint64_t s_list[kMergeListCap];
-  __shared__ SelectSmem sm;
-  const int b = blockIdx.x;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  __shared__ u32x4 s_stage[4 * 4 * kWave];  // query fragments of up to 4 head tiles
+  __shared__ float s_red[4];
+  __shared__ float s_w[64];
+  const int b = blockIdx.x / n_parts;
+  const int part = blockIdx.x - b * n_parts;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x & (kWave - 1);
   const int g = lane >> 4, n = lane & 15;
   const int64_t n_c = seq_len(seq_rows, b, n_c_max);  // this sequence's rows
 
-  for (int i = threadIdx.x; i < n_pool; i += NT) {
-    const int32_t r = pool[(int64_t)b * n_pool + i];
-    const int32_t row = (r >= 0 && r < n_c) ? r : -1;
-    s_row[i] = row;
-    s_at[i] = row < 0 || !pg.table
-                  ? row
-                  : (pg.table[(int64_t)b * pg.table_stride + (row >> pg.page_shift)] << pg.page_shift) +
-                        (row & ((1 << pg.page_shift) - 1));
-  }
+  const int pos = part * kReindexPartRows + 16 * wave + n;  // lane n's pool slot
+  const int32_t r = pos < n_pool ? pool[(int64_t)b * n_pool + pos] : -1;
+  const float w_pre = query_weight_load<HT>(w_idx, b, n_heads);
   Op qa[HT][4];
   float wv[HT][4];
-  query_setup<KT, HT, QH>(q_idx, query_weight_load<HT>(w_idx, b, n_heads), b, n_heads, wave,
-                          g, n, qa, wv, s_val, reinterpret_cast<float*>(sm.red32),
-                          reinterpret_cast<float*>(sm.hist));
-  lds_barrier();
+  query_setup<KT, HT, QH>(q_idx, w_pre, b, n_heads, wave, g, n, qa, wv, s_stage, s_red, s_w);
 
+  const int row = (r >= 0 && r < n_c) ? r : -1;
+  const int at = row < 0 || !pg.table
+                     ? row
+                     : (pg.table[(int64_t)b * pg.table_stride + (row >> pg.page_shift)] << pg.page_shift) +
+                           (row & ((1 << pg.page_shift) - 1));
   // Rows are addressed inside the sequence's rows, or inside the page pool when paged.
   const Rsrc rc = pg.table ? make_rsrc(codes, kReindexMaxSeqBytes)
                            : make_rsrc(codes + (int64_t)b * seq_stride * KT::kRowBytes,
@@ -1071,61 +1068,48 @@ __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(
                   : pg.table   ? make_rsrc(scales, kReindexMaxSeqBytes)
                                : make_rsrc(scales + (int64_t)b * seq_stride * (kIdxDim / 16),
                                            (uint32_t)(n_c * (kIdxDim / 16)));
-  const int n_tiles = (n_pool + 15) / 16;
-  auto slot_row = [&](int t) -> int {  // stored row of lane n's pool row in tile t (-1: none)
-    const int pos = 16 * t + n;
-    return pos < n_pool ? s_at[pos < kMaxPool ? pos : kMaxPool - 1] : -1;
-  };
-  auto load_tile = [&](KT& kt, int t) {
-    const int row = slot_row(t);
-    kt.load(rc, rs,
-            row >= 0 ? (uint32_t)row * KT::kRowBytes + KT::code_offset(0, g) : kAbsentKeyOffset,
-            row >= 0 ? (uint32_t)row * (kIdxDim / 16) + KT::scale_offset(0, g) : kAbsentKeyOffset);
-  };
+  KT kt;
+  kt.set_lane(g);
+  kt.load(rc, rs,
+          at >= 0 ? (uint32_t)at * KT::kRowBytes + KT::code_offset(0, g) : kAbsentKeyOffset,
+          at >= 0 ? (uint32_t)at * (kIdxDim / 16) + KT::scale_offset(0, g) : kAbsentKeyOffset);
+  Op kb[4];
+  kt.decode(kb);
+  f32x4 acc[HT];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) acc[ht] = KT::mma(qa[ht][k], kb[k], acc[ht]);
+  const float sc = wave_sum_rows(weighted_relu_share<HT>(acc, wv));
+  if (g == 0 && pos < n_pool)
+    keys[(int64_t)b * n_pool + pos] = row >= 0 ? compose_key(f32_order_key(sc), (uint32_t)row) : 0ull;
+}
 
-  // The wave's tiles are wave + 8m; kRing of them are in flight.
-  const int my_tiles = n_tiles > wave ? (n_tiles - wave + kReindexWaves - 1) / kReindexWaves : 0;
-  KT ring[kRing];
-#pragma unroll
-  for (int d = 0; d < kRing; ++d) {
-    ring[d].set_lane(g);
-    load_tile(ring[d], wave + kReindexWaves * d);
-  }
-  for (int m0 = 0; m0 < my_tiles; m0 += kRing) {
-#pragma unroll
-    for (int d = 0; d < kRing; ++d) {
-      const int t = wave + kReindexWaves * (m0 + d);
-      Op kb[4];
-      ring[d].decode(kb);
-      load_tile(ring[d], t + kReindexWaves * kRing);
-      f32x4 acc[HT];
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) acc[ht] = KT::mma(qa[ht][k], kb[k], acc[ht]);
-      const float sc = wave_sum_rows(weighted_relu_share<HT>(acc, wv));
-      const int pos = 16 * t + n;
-      if (g == 0 && pos < n_pool) {
-        const int row = s_row[pos];
-        s_key[pos] = row >= 0 ? compose_key(f32_order_key(sc), (uint32_t)row) : 0ull;
-      }
-    }
-  }
-  lds_barrier();
-
-  // The non-empty keys, compacted in pool order.
+// One workgroup per query: the query's nonzero keys, compacted in pool order, and the
+// top_k of them written in that order.
+__global__ __launch_bounds__(kReindexThreads) void reindex_select_kernel(
+    const uint64_t* __restrict__ keys, int n_pool, int top_k, int32_t* __restrict__ topk) {
+  constexpr int NT = kReindexThreads;
   constexpr int kPer = kMaxPool / NT;
-  const int q0 = threadIdx.x * kPer;
+  __shared__ uint64_t s_val[kMaxPool];
+  __shared__ uint64_t s_list[kMergeListCap];
+  __shared__ SelectSmem sm;
+  const int b = blockIdx.x;
+  const uint64_t* kq = keys + (int64_t)b * n_pool;
+  const int q0 = threadIdx.x * kPer;  // a contiguous run of slots keeps pool order
+  uint64_t kr[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) kr[j] = q0 + j < n_pool ? kq[q0 + j] : 0ull;
   uint32_t c = 0;
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) c += (q0 + j < n_pool && s_key[q0 + j] != 0ull);
+  for (int j = 0; j < kPer; ++j) c += kr[j] != 0ull;
   uint32_t n_valid;
   uint32_t wpos = block_exclusive_scan<NT>(c, sm.wsum, &n_valid);
 #pragma unroll
   for (int j = 0; j < kPer; ++j)
-    if (q0 + j < n_pool && s_key[q0 + j] != 0ull) s_val[wpos++] = s_key[q0 + j];
+    if (kr[j] != 0ull) s_val[wpos++] = kr[j];
   lds_barrier();
 
   int32_t* out = topk + (int64_t)b * top_k;
@@ -1147,11 +1131,13 @@ template <class KT, bool QH>
 void launch_reindex_ht(int ht, hipStream_t stream, const uint8_t* codes, const uint8_t* scales,
                        int64_t seq_stride, const Paging& pg, int64_t n_c, const int32_t* seq_rows,
                        const uint16_t* q_idx, const float* w_idx, int batch, int n_heads,
-                       const int32_t* pool, int n_pool, int top_k, int32_t* topk) {
-#define CSAKV_REINDEX(H)                                                                      \
-  hipLaunchKernelGGL((reindex_kernel<KT, H, QH>), dim3(batch), dim3(kReindexThreads), 0, stream, \
-                     codes, scales, seq_stride, pg, n_c, seq_rows, q_idx, w_idx, n_heads, pool,  \
-                     n_pool, top_k, topk)
+                       const int32_t* pool, int n_pool, uint64_t* keys) {
+  const int n_parts = (n_pool + kReindexPartRows - 1) / kReindexPartRows;
+  const dim3 grid((unsigned)(batch * n_parts));
+#define CSAKV_REINDEX(H)                                                                        \
+  hipLaunchKernelGGL((reindex_score_kernel<KT, H, QH>), grid, dim3(kReindexScoreThreads), 0,     \
+                     stream, codes, scales, seq_stride, pg, n_c, seq_rows, q_idx, w_idx, n_heads, \
+                     pool, n_pool, n_parts, keys)
   switch (ht) {
     case 1: CSAKV_REINDEX(1); break;
     case 2: CSAKV_REINDEX(2); break;
@@ -1282,21 +1268,28 @@ bool reindex_supported(int key_fmt, int64_t n_c) {
   return n_c >= 0 && n_c * row_bytes <= (int64_t)kReindexMaxSeqBytes;
 }
 
+size_t reindex_workspace_bytes(int batch, int n_pool) {
+  return (size_t)batch * (size_t)n_pool * sizeof(uint64_t);
+}
+
 hipError_t launch_reindex(int key_fmt, const uint8_t* codes, const uint8_t* scales,
                           int64_t seq_stride, const Paging& pg, int64_t n_c,
                           const int32_t* seq_rows, const uint16_t* q_idx, const float* w_idx,
                           int batch, int n_heads, const int32_t* pool, int n_pool, int top_k,
-                          int32_t* topk, hipStream_t stream) {
+                          int32_t* topk, void* workspace, hipStream_t stream) {
   const int ht = (n_heads + 15) / 16;
+  uint64_t* keys = static_cast<uint64_t*>(workspace);
   if (key_fmt == 0)
-    launch_reindex_ht<KeyTileBf16, false>(ht, stream, codes, scales, seq_stride, pg, n_c, seq_rows, q_idx, w_idx,
-                                          batch, n_heads, pool, n_pool, top_k, topk);
+    launch_reindex_ht<KeyTileBf16, false>(ht, stream, codes, scales, seq_stride, pg, n_c, seq_rows,
+                                          q_idx, w_idx, batch, n_heads, pool, n_pool, keys);
   else if (key_fmt == 1)
-    launch_reindex_ht<KeyTileFp4, false>(ht, stream, codes, scales, seq_stride, pg, n_c, seq_rows, q_idx, w_idx,
-                                         batch, n_heads, pool, n_pool, top_k, topk);
+    launch_reindex_ht<KeyTileFp4, false>(ht, stream, codes, scales, seq_stride, pg, n_c, seq_rows,
+                                         q_idx, w_idx, batch, n_heads, pool, n_pool, keys);
   else
-    launch_reindex_ht<KeyTileFp4, true>(ht, stream, codes, scales, seq_stride, pg, n_c, seq_rows, q_idx, w_idx,
-                                        batch, n_heads, pool, n_pool, top_k, topk);
+    launch_reindex_ht<KeyTileFp4, true>(ht, stream, codes, scales, seq_stride, pg, n_c, seq_rows,
+                                        q_idx, w_idx, batch, n_heads, pool, n_pool, keys);
+  hipLaunchKernelGGL(reindex_select_kernel, dim3(batch), dim3(kReindexThreads), 0, stream, keys,
+                     n_pool, top_k, topk);
   return hipGetLastError();
 }
 

@@ -174,10 +174,18 @@ csakv_status csa_select_topk(const csakv_csa_params* p, const csakv_cache* idx_k
  *   topk      [B][top_k] int32: the set of the top_k pool rows (ties in score go to
  *             the lower row index) in pool order; -1 pads when the pool holds fewer
  *             rows.  Must not overlap pool.
- * No workspace: one workgroup per query keeps the pool in LDS. */
+ *   workspace device memory of csa_reindex_topk_workspace_bytes(p, n_pool) bytes,
+ *             256-byte aligned, overlapping no argument; it holds every pool slot's
+ *             score between the call's two launches and may be reused once the call's
+ *             work on `stream` has finished. */
 csakv_status csa_reindex_topk(const csakv_csa_params* p, const csakv_cache* idx_keys,
                               const uint16_t* q_idx, const float* w_idx, const int32_t* pool,
-                              int32_t n_pool, int32_t* topk, void* stream);
+                              int32_t n_pool, int32_t* topk, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace csa_reindex_topk needs for p->batch queries of n_pool slots
+ * (8 per slot, rounded up to 256); 0 when p or n_pool is invalid. */
+size_t csa_reindex_topk_workspace_bytes(const csakv_csa_params* p, int32_t n_pool);
 
 /* Bytes of workspace hca_decode needs for B sequences of n_rows rows each. */
 size_t hca_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int64_t n_rows);

@@ -157,8 +157,12 @@ def test_hca_and_codecs_reject_bad_arguments():
 def test_reindex_rejects_bad_arguments():
     p = _params(mode=ck.MODE_REINDEX)
 
-    def call(p=p, idx=IDX, qi=FAKE, w=FAKE, pool=FAKE, n_pool=1024, topk=FAKE + 65536):
-        return ck.csa_reindex_topk(p, idx, qi, w, pool, n_pool, topk, stream=0, check=False)
+    def call(p=p, idx=IDX, qi=FAKE, w=FAKE, pool=FAKE, n_pool=1024, topk=FAKE + 65536,
+             ws=FAKE + (1 << 20), ws_bytes=None):
+        if ws_bytes is None:
+            ws_bytes = ck.csa_reindex_topk_workspace_bytes(p, n_pool)
+        return ck.csa_reindex_topk(p, idx, qi, w, pool, n_pool, topk, ws, ws_bytes, stream=0,
+                                   check=False)
 
     assert call(p=_params(mode=ck.MODE_FULL)) == ck.ERR_INVALID            # wrong mode
     assert ck.csa_decode_workspace_bytes(p, 1024) == 0                    # csa_decode has no REINDEX
@@ -173,6 +177,13 @@ def test_reindex_rejects_bad_arguments():
     assert call(topk=FAKE + 1024) == ck.ERR_INVALID                       # output overlaps the pool
     huge = ck.Cache(ck.IDX_BF16, 0, 1 << 24, 1 << 24, FAKE, None)         # 4 GiB of keys
     assert call(idx=huge) == ck.ERR_UNSUPPORTED
+    need = ck.csa_reindex_topk_workspace_bytes(p, 1024)
+    assert need == 1024 * 8                                               # one key per slot
+    assert ck.csa_reindex_topk_workspace_bytes(p, 0) == 0
+    assert ck.csa_reindex_topk_workspace_bytes(_params(mode=ck.MODE_FULL), 1024) == 0
+    assert call(ws_bytes=need - 1) == ck.ERR_WORKSPACE
+    assert call(ws=0) == ck.ERR_INVALID                                   # null workspace
+    assert call(ws=FAKE + 8) == ck.ERR_INVALID                            # misaligned workspace
 
 
 def test_cache_write_rejects_bad_arguments():

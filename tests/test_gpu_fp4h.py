@@ -91,6 +91,7 @@ def test_fp4h_reindex_parity():
     p = ck.CsaParams(B, 0, hi, k, 0, ck.MODE_REINDEX, 1.0, 0)
     out = torch.empty((B, k), dtype=torch.int32, device="cuda")
     ck.csa_reindex_topk(p, idx, to_dev(c["qb"].view(np.int16)), to_dev(c["w"]),
-                        to_dev(pool.astype(np.int32)), n_pool, out)
+                        to_dev(pool.astype(np.int32)), n_pool, out,
+                        workspace(ck.csa_reindex_topk_workspace_bytes(p, n_pool)))
     torch.cuda.synchronize()
     assert topk_sets_equal(out.cpu().numpy(), expect)

@@ -99,7 +99,8 @@ def test_csa2_reindex_fp4_1m():
     print("case: csa2 reindex layer 1 select", flush=True)
     pr = ck.CsaParams(B, 0, hi, k, 0, ck.MODE_REINDEX, 1.0, 0)
     tk = torch.empty((B, k), dtype=torch.int32, device=DEV)
-    ck.csa_reindex_topk(pr, ix.cache, qi1, w1, pool, P, tk)
+    rws = torch.empty(ck.csa_reindex_topk_workspace_bytes(pr, P), dtype=torch.uint8, device=DEV)
+    ck.csa_reindex_topk(pr, ix.cache, qi1, w1, pool, P, tk, rws)
     torch.cuda.synchronize()
     tkn = tk.cpu().numpy()
     sel = {}

@@ -140,7 +140,7 @@ def test_reindex_paged():
         idxc = _idx_cache(case.idx, pr, 507)
         topk = torch.empty((2, 128), dtype=torch.int32, device="cuda")
         ck.csa_reindex_topk(p, idxc, to_dev(case.q_idx_bits.view(np.int16)), to_dev(case.w), pool,
-                            1024, topk)
+                            1024, topk, workspace(ck.csa_reindex_topk_workspace_bytes(p, 1024)))
         torch.cuda.synchronize()
         got.append(topk.cpu().numpy())
     assert (got[0] == got[1]).all()

@@ -55,7 +55,7 @@ def run_reindex(c, stride_pad=0):
     pool = to_dev(c["pool"].astype(np.int32))
     out = Guarded((c["B"], c["top_k"]), torch.int32)
     ck.csa_reindex_topk(p, idx, to_dev(c["q_bits"].view(np.int16)), to_dev(c["w"]), pool,
-                        c["n_pool"], out.t)
+                        c["n_pool"], out.t, workspace(ck.csa_reindex_topk_workspace_bytes(p, c["n_pool"])))
     torch.cuda.synchronize()
     assert out.intact(), "write outside the output buffer"
     return out.t.cpu().numpy()
@@ -107,6 +107,7 @@ def test_reindex_of_the_full_pool_with_its_own_query_is_the_full_selection():
     ck.csa_select_topk(p, idx, qi, w, pool, workspace(ck.csa_select_topk_workspace_bytes(p, case.n_c)))
     pr = ck.CsaParams(case.B, 0, case.hi, 512, 0, ck.MODE_REINDEX, 1.0, 0)
     out = torch.empty((case.B, 512), dtype=torch.int32, device="cuda")
-    ck.csa_reindex_topk(pr, idx, qi, w, pool, 1024, out)
+    ck.csa_reindex_topk(pr, idx, qi, w, pool, 1024, out,
+                        workspace(ck.csa_reindex_topk_workspace_bytes(pr, 1024)))
     torch.cuda.synchronize()
     assert topk_sets_equal(out.cpu().numpy(), case.expect_topk)

@@ -187,7 +187,7 @@ def test_reindex_varlen():
     p = ck.CsaParams(B, 0, hi, top_k, 0, ck.MODE_REINDEX, 1.0, 0)
     topk = torch.empty((B, top_k), dtype=torch.int32, device="cuda")
     ck.csa_reindex_topk(p, idxc, to_dev(c["qi"].view(np.int16)), to_dev(c["w"]), to_dev(pool),
-                        cap, topk)
+                        cap, topk, workspace(ck.csa_reindex_topk_workspace_bytes(p, cap)))
     torch.cuda.synchronize()
     got = topk.cpu().numpy()
     qiv = OF.bf16_bits_to_f64(c["qi"])
