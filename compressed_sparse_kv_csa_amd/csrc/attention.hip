@@ -331,7 +331,10 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
   f32x4 o[kDimsPerWave / 16];
 #pragma unroll
   for (int i = 0; i < kDimsPerWave / 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.0f;
+  // m_run starts at a finite floor instead of -inf: the first step with a present row
+  // always moves it (grow), so no probability is ever taken against the floor, and no
+  // exponential sees -inf - -inf.  A chunk without present rows records -inf.
+  float m_run = -__FLT_MAX__, l_run = 0.0f;
 
   // Two steps are fetched ahead (raw0 / raw1 alternate), so both steps of a 64-row chunk
   // are in flight as soon as the row indices are known.  Rows are read through buffer
@@ -380,9 +383,11 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
       for (int i = 0; i < 4; ++i)
         sacc[rt][i] = s_logit[0][16 * rt + 4 * g + i][n] + s_logit[1][16 * rt + 4 * g + i][n];
     // ---- online softmax (log2 domain).  Row r of the step is present when bit r of
-    // `present` is set; a step whose rows are all present skips the masking.
-    const uint64_t present =
-        __ballot(s_rows[step * kStepRows + (lane & (kStepRows - 1))] >= 0) & 0xFFFFFFFFull;
+    // `present` is set.  Exponentials are the hardware's base-2 exponential: a
+    // probability below 2^-126 of the reference maximum flushes to 0, far below what
+    // its fp16 or bf16 operand resolves next to the maximum's 1.
+    const uint32_t present =
+        (uint32_t)__ballot(s_rows[step * kStepRows + (lane & (kStepRows - 1))] >= 0);
     float x[8];
     float mloc = -INFINITY;
 #pragma unroll
@@ -391,7 +396,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * g + i;
         float v = sacc[rt][i] * scale_log2;
-        if (present != 0xFFFFFFFFull && !((present >> r) & 1ull)) v = -INFINITY;
+        if (!((present >> r) & 1u)) v = -INFINITY;
         x[4 * rt + i] = v;
         mloc = fmaxf(mloc, v);
       }
@@ -401,17 +406,17 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
     // than 2^kLazyLog2: the probabilities then stay below 2^kLazyLog2 (within fp16's
     // range, rounded with its full precision), and the accumulators are rescaled only on
     // those rare steps instead of whenever a head's maximum grows.
-    const bool grow = mloc > m_run + kLazyLog2;  // m_run = -inf: any present row
+    const bool grow = mloc > m_run + kLazyLog2;  // m_run at its floor: any present row
     float alpha = 1.0f;
     if (grow) {
-      alpha = m_run == -INFINITY ? 0.0f : exp2f(m_run - mloc);
+      alpha = __builtin_amdgcn_exp2f(m_run - mloc);  // 0 from the floor
       m_run = mloc;
     }
     float psum = 0.0f;
     float pv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      pv[i] = m_run == -INFINITY ? 0.0f : exp2f(x[i] - m_run);
+      pv[i] = __builtin_amdgcn_exp2f(x[i] - m_run);  // absent rows: exp2(-inf) = 0
       psum += pv[i];
     }
     psum += __shfl_xor(psum, 16);
@@ -445,7 +450,8 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
   // (max, sum) pairs go to their own array.
   const int64_t rec0 = ((int64_t)b * n_chunks + chunk) * n_heads + 16 * hg;
   lds_barrier();  // every wave is done with the tiles and the query rows
-  if (wave == 0 && g == 0) *reinterpret_cast<f32x2*>(part_ml + (rec0 + n) * 2) = f32x2{m_run, l_run};
+  if (wave == 0 && g == 0)
+    *reinterpret_cast<f32x2*>(part_ml + (rec0 + n) * 2) = f32x2{l_run > 0.0f ? m_run : -INFINITY, l_run};
   {
     float* orow = s_out + n * kOutPitch + kDimsPerWave * wave + 4 * g;
 #pragma unroll
