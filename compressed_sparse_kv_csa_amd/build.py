@@ -26,6 +26,14 @@ CFLAGS = [
 ]
 
 
+# Per-source extra flags.  attention.hip: MFMA accumulators in VGPRs (the default keeps the
+# output accumulators in AGPRs and copies all 32 of them to VGPRs on every iteration of the
+# step loop, around the rare rescale).
+FILE_FLAGS = {
+    "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _hipcc() -> str:
     p = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(p):
@@ -39,7 +47,7 @@ def _sources():
 
 def _compile(src: str, resource_usage: bool) -> tuple[str, str]:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *CFLAGS, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     if resource_usage:

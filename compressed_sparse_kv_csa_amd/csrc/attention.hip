@@ -383,23 +383,27 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
       for (int i = 0; i < 4; ++i)
         sacc[rt][i] = s_logit[0][16 * rt + 4 * g + i][n] + s_logit[1][16 * rt + 4 * g + i][n];
     // ---- online softmax (log2 domain).  Row r of the step is present when bit r of
-    // `present` is set.  Exponentials are the hardware's base-2 exponential: a
+    // `present` is set; only a step with absent rows runs the masking (a uniform
+    // branch: the row list is full except at its end).  Exponentials are the hardware's base-2 exponential: a
     // probability below 2^-126 of the reference maximum flushes to 0, far below what
     // its fp16 or bf16 operand resolves next to the maximum's 1.
     const uint32_t present =
         (uint32_t)__ballot(s_rows[step * kStepRows + (lane & (kStepRows - 1))] >= 0);
     float x[8];
-    float mloc = -INFINITY;
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * g + i;
-        float v = sacc[rt][i] * scale_log2;
-        if (!((present >> r) & 1u)) v = -INFINITY;
-        x[4 * rt + i] = v;
-        mloc = fmaxf(mloc, v);
-      }
+      for (int i = 0; i < 4; ++i) x[4 * rt + i] = sacc[rt][i] * scale_log2;
+    if (__builtin_expect(present != 0xFFFFFFFFu, 0)) {  // a step with absent rows
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!((present >> (16 * rt + 4 * g + i)) & 1u)) x[4 * rt + i] = -INFINITY;
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mloc = fmaxf(mloc, x[i]);
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
     // The reference maximum m_run moves only when a step's maximum exceeds it by more
