@@ -38,6 +38,7 @@ struct IndexerPlan {
   int wg_per_query;   // scan workgroups per query
   int cap;            // candidate slots per slice
   int prefix;         // P: a slice sends at least its top-P keys
+  int first;          // slots per slice the merge reads with the counts (a power of two)
 };
 
 constexpr int kSliceRows = 4096;

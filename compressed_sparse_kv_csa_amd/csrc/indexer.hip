@@ -917,7 +917,7 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
 
 __global__ __launch_bounds__(kMergeThreads) void indexer_merge_kernel(
     IndexerWs ws, int64_t n_c, const int32_t* __restrict__ seq_rows, int top_k, int n_slices,
-    int cap, int32_t* __restrict__ topk) {
+    int cap, int first, int32_t* __restrict__ topk) {
   __shared__ uint64_t s_buf[kMergeCap];
   __shared__ uint64_t s_list[kMergeListCap];
   __shared__ uint64_t s_bound[kMaxMergeSlices];
@@ -935,6 +935,18 @@ __global__ __launch_bounds__(kMergeThreads) void indexer_merge_kernel(
   if (k1 == 0) return;
   const int64_t s0 = (int64_t)b * n_slices;
 
+  // Slots j < first of every slice (first a power of two, n_slices * first <= 4 * NT)
+  // are read in the same round of loads as the counts; slots past a slice's count are
+  // dropped once the counts are known.
+  constexpr int kFirstPerThread = 4;
+  const int f_shift = __builtin_ctz((unsigned)first);
+  const int n_first = n_slices << f_shift;
+  uint64_t slot[kFirstPerThread];
+#pragma unroll
+  for (int r = 0; r < kFirstPerThread; ++r) {
+    const int i = (int)threadIdx.x + NT * r;
+    slot[r] = i < n_first ? ws.cand[(s0 + (i >> f_shift)) * cap + (i & (first - 1))] : 0ull;
+  }
   // Candidate counts -> offsets in the buffer (n_slices <= NT).
   const uint32_t c = threadIdx.x < n_slices ? ws.count[s0 + threadIdx.x] : 0u;
   if (threadIdx.x < n_slices) s_bound[threadIdx.x] = ws.bound[s0 + threadIdx.x];
@@ -943,10 +955,21 @@ __global__ __launch_bounds__(kMergeThreads) void indexer_merge_kernel(
   if (threadIdx.x < n_slices) s_off[threadIdx.x] = off;
   if (threadIdx.x == 0) s_off[n_slices] = n_buf;
   lds_barrier();
-  for (int s = wave; s < n_slices; s += NT / kWave) {  // one wave per slice at a time
+#pragma unroll
+  for (int r = 0; r < kFirstPerThread; ++r) {
+    const int i = (int)threadIdx.x + NT * r;
+    if (i < n_first) {
+      const int s = i >> f_shift, j = i & (first - 1);
+      const uint32_t o = s_off[s];
+      if ((uint32_t)j < s_off[s + 1] - o) s_buf[o + j] = slot[r];
+    }
+  }
+  // The rest of the slices that sent more than `first` keys, one wave per slice.
+  for (int s = wave; s < n_slices; s += NT / kWave) {
     const uint32_t o = s_off[s], m = s_off[s + 1] - o;
+    if (m <= (uint32_t)first) continue;
     const uint64_t* src = ws.cand + (s0 + s) * cap;
-    for (uint32_t j = lane; j < m; j += kWave) s_buf[o + j] = src[j];
+    for (uint32_t j = (uint32_t)first + lane; j < m; j += kWave) s_buf[o + j] = src[j];
   }
   lds_barrier();
 
@@ -1224,6 +1247,11 @@ IndexerPlan plan_indexer(int batch, int64_t n_c, int top_k) {
       if (want < 16) want = 16;
       p.prefix = (int)std::min<int64_t>(want, p.cap / 2);
     }
+    // The merge reads the first `first` slots of every slice (4 per thread) in the same
+    // round as the counts; a slice that sent more has the rest read afterwards.
+    const int64_t room = std::min<int64_t>(p.cap, 4 * kMergeThreads / p.n_slices);
+    p.first = 1;
+    while (2 * (int64_t)p.first <= room) p.first *= 2;
   }
   return p;
 }
@@ -1259,7 +1287,7 @@ hipError_t launch_indexer(int key_fmt, const uint8_t* codes, const uint8_t* scal
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(indexer_merge_kernel, dim3(batch), dim3(kMergeThreads), 0, stream, ws, n_c, seq_rows,
-                     top_k, plan.n_slices, plan.cap, topk);
+                     top_k, plan.n_slices, plan.cap, plan.first, topk);
   return hipGetLastError();
 }
 
