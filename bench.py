@@ -14,10 +14,13 @@ keys, B = 4 query tokens.  Inputs are synthetic and seed-generated, and resident
 before timing starts; R replicas of every cache (>= 1 GiB in all) rotate across steps so
 that the 256 MB Infinity Cache cannot serve a step from the previous one.
 
-Output: one JSON line (rank 0).  `roofline` reports the dominant stage (the indexer scan
-+ top-k, csa_select_topk; for HCA the whole hca_decode) timed with HIP events on the
-stream it runs on; `cpu_baseline` times the CPU oracle on a bounded sample of the same
-workload.
+Timing: every step is captured once per replica as a hipGraph (torch.cuda.CUDAGraph over
+the library's own launches); the K timed steps replay step i's graph on the current
+stream, bracketed by HIP events.  `protocol` adds the R-step graph (all replicas)
+replayed at least 50 times.  Output: one JSON line.  `roofline` reports the dominant
+kernel (the indexer scan, csa_select_scan; for HCA the whole hca_decode) timed with one
+HIP event pair per launch on the stream it runs on; `cpu_baseline` times the CPU oracle
+on a bounded sample of the same workload, on one thread and on every host core.
 """
 from __future__ import annotations
 
@@ -60,7 +63,6 @@ WORKLOADS = {
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_stage_csa_mixed_1m_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "compressed_sparse_kv_csa_amd", "csrc", f)
                   for f in ("indexer.hip", "csakv_device.h", "csakv_launch.h")]
-COPY_PROBE_ELEMS = 1 << 28  # float32 elements: 1 GiB read + 1 GiB written
 
 KV_ROW_BYTES = {"bf16": 1024, "mixed": 576, "fp4": 256 + 32}
 IDX_ROW_BYTES = {"bf16": 256, "fp4": 64 + 8, "fp4h": 64 + 8}
@@ -71,19 +73,21 @@ def algorithmic_bytes(w: dict) -> dict:
     B, n_c, k = w["B"], w["n_c"], w["top_k"]
     if w["kind"] == "hca":
         attn = B * ((n_c + w["window"]) * KV_ROW_BYTES[w["kv"]] + 2 * w["hq"] * 512 * 2)
-        return {"indexer": 0, "attention": attn, "step": attn}
+        return {"scan": 0, "indexer": 0, "attention": attn, "step": attn}
     rows = min(k, n_c) + w["window"]
     q_i = w["hi"] * 128 * 2 + w["hi"] * 4
     attn = B * (rows * KV_ROW_BYTES[w["kv"]] + 2 * w["hq"] * 512 * 2)
     if w["kind"] == "csa2r":  # pool select, then per layer: re-rank the pool and attend
         P = w["pool"]
+        scan = B * (n_c * IDX_ROW_BYTES[w["idx"]] + q_i)
         idx = B * (n_c * IDX_ROW_BYTES[w["idx"]] + q_i + P * 4)
         reindex = B * (P * IDX_ROW_BYTES[w["idx"]] + q_i + P * 4 + k * 4)
-        return {"indexer": idx, "attention": attn,
+        return {"scan": scan, "indexer": idx, "attention": attn,
                 "step": idx + w["layers"] * (reindex + attn + B * k * 4)}
-    idx = B * (n_c * IDX_ROW_BYTES[w["idx"]] + q_i + k * 4)
+    scan = B * (n_c * IDX_ROW_BYTES[w["idx"]] + q_i)      # the scan reads keys, q_I and w
+    idx = scan + B * k * 4                                  # the merge writes topk
     reuse = (w["layers"] - 1) * (attn + B * k * 4)
-    return {"indexer": idx, "attention": attn, "step": idx + attn + reuse}
+    return {"scan": scan, "indexer": idx, "attention": attn, "step": idx + attn + reuse}
 
 
 def build_inputs(w: dict, replicas: int):
@@ -168,18 +172,17 @@ def run_gpu(w: dict, steps: int, warmup: int, replicas: int | None):
     R = replicas or max(2, math.ceil(MALL_BYTES / nbytes["step"]))
     reps = build_inputs(w, R)
     B, scale = w["B"], 1.0 / math.sqrt(512)
-    stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream
     if w["kind"] == "hca":
         rows = w["n_c"] + w["window"]
         ws_bytes = ck.hca_decode_workspace_bytes(B, w["hq"], rows)
         ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
 
-        def step(i):
+        def step(i, sh):
             r = reps[i % R]
             ck.hca_decode(B, w["hq"], scale, r["kv"][0], r["q"][0], r["out"][0], ws, ws_bytes, stream=sh)
 
         stage, stage_bytes, stage_name = step, nbytes["attention"], "hca_decode (attention + combine)"
+        whole, whole_bytes, whole_name = None, None, None
     elif w["kind"] == "csa2r":
         P = w["pool"]
         p_pool = ck.CsaParams(B, w["hq"], w["hi"], P, w["window"], ck.MODE_FULL, scale, 0)
@@ -191,7 +194,7 @@ def run_gpu(w: dict, steps: int, warmup: int, replicas: int | None):
         rx_bytes = ck.csa_reindex_topk_workspace_bytes(p_rx, P)
         rx_ws = torch.empty(rx_bytes, dtype=torch.uint8, device="cuda")
 
-        def step(i):
+        def step(i, sh):
             r = reps[i % R]
             ck.csa_select_topk(p_pool, r["idx"], r["qi"][0], r["w"][0], r["pool"], ws, ws_bytes,
                                stream=sh)
@@ -201,19 +204,24 @@ def run_gpu(w: dict, steps: int, warmup: int, replicas: int | None):
                 ck.csa_decode(p_reuse, r["kv"][layer], None, r["q"][layer], None, None, r["topk"],
                               r["out"][layer], ws, ws_bytes, stream=sh)
 
-        def stage(i):
+        def stage(i, sh):
+            r = reps[i % R]
+            ck.csa_select_scan(p_pool, r["idx"], r["qi"][0], r["w"][0], ws, ws_bytes, stream=sh)
+
+        def whole(i, sh):
             r = reps[i % R]
             ck.csa_select_topk(p_pool, r["idx"], r["qi"][0], r["w"][0], r["pool"], ws, ws_bytes,
                                stream=sh)
 
-        stage_bytes, stage_name = nbytes["indexer"], "indexer stage (csa_select_topk, 1024-row pool)"
+        stage_bytes, stage_name = nbytes["scan"], "indexer_scan_kernel (csa_select_scan, 1024-row pool)"
+        whole_bytes, whole_name = nbytes["indexer"], "indexer stage: scan + merge (csa_select_topk)"
     else:
         p = ck.CsaParams(B, w["hq"], w["hi"], w["top_k"], w["window"], ck.MODE_FULL, scale, 0)
         p_reuse = ck.CsaParams(B, w["hq"], 0, w["top_k"], w["window"], ck.MODE_REUSE, scale, 0)
         ws_bytes = ck.csa_decode_workspace_bytes(p, w["n_c"])
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
 
-        def step(i):
+        def step(i, sh):
             r = reps[i % R]
             ck.csa_decode(p, r["kv"][0], r["idx"], r["q"][0], r["qi"], r["w"], r["topk"], r["out"][0],
                           ws, ws_bytes, stream=sh)
@@ -221,40 +229,77 @@ def run_gpu(w: dict, steps: int, warmup: int, replicas: int | None):
                 ck.csa_decode(p_reuse, r["kv"][layer], None, r["q"][layer], None, None, r["topk"],
                               r["out"][layer], ws, ws_bytes, stream=sh)
 
-        def stage(i):
+        def stage(i, sh):
+            r = reps[i % R]
+            ck.csa_select_scan(p, r["idx"], r["qi"], r["w"], ws, ws_bytes, stream=sh)
+
+        def whole(i, sh):
             r = reps[i % R]
             ck.csa_select_topk(p, r["idx"], r["qi"], r["w"], r["topk"], ws, ws_bytes, stream=sh)
 
-        stage_bytes, stage_name = nbytes["indexer"], "indexer stage (csa_select_topk)"
+        stage_bytes, stage_name = nbytes["scan"], "indexer_scan_kernel (csa_select_scan)"
+        whole_bytes, whole_name = nbytes["indexer"], "indexer stage: scan + merge (csa_select_topk)"
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t0.record(stream)
-    for i in range(steps):
-        step(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms = t0.elapsed_time(t1) / steps
+    cur = torch.cuda.current_stream
 
-    # Dominant stage, one event pair per launch on its stream.
+    def timed(fn, n):
+        """HIP-event time of fn(i) for i < n on the current stream, ms per call."""
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(cur())
+        for i in range(n):
+            fn(i)
+        t1.record(cur())
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / n
+
+    # Eager warmup (every replica once), then one graph per replica's step.
+    for i in range(max(warmup, R)):
+        step(i, cur().cuda_stream)
+    torch.cuda.synchronize()
+    eager_ms = timed(lambda i: step(i, cur().cuda_stream), steps)
+    graphs = []
+    side = torch.cuda.Stream()
+    for r in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            step(r, cur().cuda_stream)
+        graphs.append(g)
     for i in range(warmup):
-        stage(i)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    for i in range(steps):
-        ev[i][0].record(stream)
-        stage(i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    stage_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
-    return dict(ms=ms, wall=wall, stage_ms=stage_ms, stage_bytes=stage_bytes, stage_name=stage_name,
-                replicas=R, bytes=nbytes)
+        graphs[i % R].replay()
+    ms = timed(lambda i: graphs[i % R].replay(), steps)
+
+    # Protocol: one graph of all R replicas' steps, replayed M >= 50 times.
+    g_all = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_all, stream=side):
+        for r in range(R):
+            step(r, cur().cuda_stream)
+    g_all.replay()
+    M = 50
+    proto_ms = timed(lambda i: g_all.replay(), M) / R
+
+    def per_launch(fn):
+        """Average HIP-event time of one fn(i) launch, each bracketed by its own events."""
+        for i in range(warmup):
+            fn(i, cur().cuda_stream)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record(cur())
+            fn(i, cur().cuda_stream)
+            ev[i][1].record(cur())
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / steps
+
+    # The dominant kernel, and the whole indexer stage it belongs to.
+    stage_ms = per_launch(stage)
+    whole_ms = per_launch(whole) if whole is not None else None
+    return dict(ms=ms, eager_ms=eager_ms, stage_ms=stage_ms, stage_bytes=stage_bytes,
+                stage_name=stage_name, whole_ms=whole_ms, whole_bytes=whole_bytes,
+                whole_name=whole_name, replicas=R, bytes=nbytes, proto_ms=proto_ms,
+                proto_replays=M)
 
 
 def kernel_sources_sha256() -> str:
@@ -283,18 +328,7 @@ def measured_traffic(workload: str):
         return None
 
 
-def copy_probe():
-    """One plain elementwise copy of known size (1 GiB in, 1 GiB out) for counter scaling."""
-    import torch
-    src = torch.ones(COPY_PROBE_ELEMS, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
-    torch.cuda.synchronize()
-    torch.neg(src, out=dst)
-    torch.cuda.synchronize()
-    del src, dst
-
-
-CPU_SAMPLE_SECONDS = 10.0  # the oracle's sample is repeated until it has run this long
+CPU_SAMPLE_SECONDS = 8.0  # each leg of the oracle's sample repeats until it has run this long
 
 
 def timed_passes(one_pass):
@@ -308,17 +342,43 @@ def timed_passes(one_pass):
             return n, dt
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def two_legs(one_pass, queries):
+    """The oracle's sample timed on one thread, then on every host core (numpy's BLAS
+    threads): (rates, passes, seconds, threads of the second leg)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    with threadpool_limits(limits=1):
+        p1, d1 = timed_passes(one_pass)
+    pn, dn = timed_passes(one_pass)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return (queries * pn / dn, queries * p1 / d1), (pn, p1), (dn, d1), threads
+
+
+def cpu_record(rates, passes, secs, threads, sample):
+    return {"value": round(rates[0], 4), "unit": "query-tokens/s", "cores": int(threads),
+            "kind": "oracle", "single_thread_value": round(rates[1], 4),
+            "nproc": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": cpu_model(),
+            "sample": f"{sample}; {passes[1]} pass(es) in {secs[1]:.1f} s on 1 thread, {passes[0]} in "
+                      f"{secs[0]:.1f} s on {threads} threads; numpy fp64"}
+
+
 def run_cpu_baseline(w: dict, queries: int):
     """The oracle, untuned, on `queries` query tokens of the same workload (seed, shapes)."""
     import numpy as np
     import torch
     import seedgen
     from oracle import decode as OD, formats as OF
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
     T = seedgen.TID
     n_c, W, k, B = w["n_c"], w["window"], w["top_k"], w["B"]
     dev = "cuda" if torch.cuda.is_available() else "cpu"
@@ -354,15 +414,12 @@ def run_cpu_baseline(w: dict, queries: int):
         def one_pass():
             for b in range(queries):
                 OD.hca_decode_one(qs[0][b], decode(encs[b]), scale)
-        passes, dt = timed_passes(one_pass)
         sample = (f"{queries} of the {B} query tokens of one step (same seeds and shapes): dense "
-                  f"attention over {W + n_c} {w['kv']} rows each, {passes} pass(es); numpy fp64, "
-                  f"{dt:.1f} s")
-        return {"value": round(queries * passes / dt, 4), "unit": "query-tokens/s",
-                "cores": int(cores), "kind": "oracle", "sample": sample}
+                  f"attention over {W + n_c} {w['kv']} rows each")
+        return cpu_record(*two_legs(one_pass, queries), sample)
 
     if w["kind"] == "csa2r":
-        return cpu_baseline_reindex(w, queries, qs, bits, encode, decode, cores)
+        return cpu_baseline_reindex(w, queries, qs, bits, encode, decode)
 
     qi = seedgen.bf16_normal(s, seedgen.tid(T.Q_IDX), (B, w["hi"], 128), dev)[:queries]
     wv = seedgen.uniform01(s, seedgen.tid(T.W_IDX), (B, w["hi"]), dev)[:queries]
@@ -399,16 +456,13 @@ def run_cpu_baseline(w: dict, queries: int):
             OD.topk_indices(OD.indexer_scores(qi[b], wv[b], kd), k)
             for layer in range(w["layers"]):
                 OD.attention(qs[layer][b], decode(rows_enc[layer][b]), scale)
-    passes, dt = timed_passes(one_pass)
     layers = f" in each of {w['layers']} layers" if w["layers"] > 1 else ""
-    return {"value": round(queries * passes / dt, 4), "unit": "query-tokens/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{queries} of the {B} query tokens of one step (same seeds and shapes): "
-                      f"{n_c} {w['idx']} indexer keys each, then {W}+{k} {w['kv']} rows{layers}, "
-                      f"{passes} pass(es); numpy fp64, {dt:.1f} s"}
+    sample = (f"{queries} of the {B} query tokens of one step (same seeds and shapes): "
+              f"{n_c} {w['idx']} indexer keys each, then {W}+{k} {w['kv']} rows{layers}")
+    return cpu_record(*two_legs(one_pass, queries), sample)
 
 
-def cpu_baseline_reindex(w, queries, qs, bits, encode, decode, cores):
+def cpu_baseline_reindex(w, queries, qs, bits, encode, decode):
     """The oracle on the CSA2 Reindex stack: the Full layer's pool, then per layer the
     re-ranked top-k and the attention over it (same seeds and shapes as the GPU run)."""
     import numpy as np
@@ -442,13 +496,10 @@ def cpu_baseline_reindex(w, queries, qs, bits, encode, decode, cores):
             for layer in range(w["layers"]):
                 OD.reindex_topk(qi[layer][b], wv[layer][b], kds[b], pool, k)
                 OD.attention(qs[layer][b], decode(rows_enc[layer][b]), scale)
-    passes, dt = timed_passes(one_pass)
-    return {"value": round(queries * passes / dt, 4), "unit": "query-tokens/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{queries} of the {B} query tokens of one step (same seeds and shapes): "
-                      f"{n_c} {w['idx']} indexer keys -> a {P}-row pool, then in each of "
-                      f"{w['layers']} layers the pool re-ranked to {k} and {W}+{k} {w['kv']} rows, "
-                      f"{passes} pass(es); numpy fp64, {dt:.1f} s"}
+    sample = (f"{queries} of the {B} query tokens of one step (same seeds and shapes): "
+              f"{n_c} {w['idx']} indexer keys -> a {P}-row pool, then in each of "
+              f"{w['layers']} layers the pool re-ranked to {k} and {W}+{k} {w['kv']} rows")
+    return cpu_record(*two_legs(one_pass, queries), sample)
 
 
 def main():
@@ -461,8 +512,6 @@ def main():
     ap.add_argument("--cpu-queries", type=int, default=None,
                     help="query tokens in the oracle sample (default: one step's batch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="first run one 1 GiB elementwise copy (scales HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -474,13 +523,12 @@ def main():
         print("bench.py needs a GPU (HIP device) to run.", file=sys.stderr)
         sys.exit(1)
     w = WORKLOADS[args.workload]
-    if args.copy_probe:
-        copy_probe()
     g = run_gpu(w, args.steps, args.warmup, args.replicas)
     B = w["B"]
     tok_s = B / (g["ms"] * 1e-3)
     step_gbps = g["bytes"]["step"] / (g["ms"] * 1e-3) / 1e9
     stage_gbps = g["stage_bytes"] / (g["stage_ms"] * 1e-3) / 1e9
+    whole_gbps = (g["whole_bytes"] / (g["whole_ms"] * 1e-3) / 1e9) if g["whole_ms"] else None
     cpu = None
     if not args.no_cpu_baseline:
         cpu = run_cpu_baseline(w, args.cpu_queries or B)
@@ -504,12 +552,22 @@ def main():
                    **({"pool": w["pool"]} if "pool" in w else {})},
         "hbm_gbps": round(step_gbps, 1),
         "algorithmic_bytes_per_step": g["bytes"]["step"],
+        "timing": {"graph_per_step": True, "eager_ms_per_step": round(g["eager_ms"], 5)},
+        "protocol": {"replicas": g["replicas"], "replays": g["proto_replays"],
+                     "ms_per_step": round(g["proto_ms"], 5),
+                     "query_tokens_per_s": round(B / (g["proto_ms"] * 1e-3), 1)},
         "roofline": {"bound": "hbm", "achieved": round(stage_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(stage_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(args.workload),
                      "kernel": g["stage_name"],
                      "avg_launch_us": round(g["stage_ms"] * 1e3, 2),
-                     "algorithmic_bytes_per_launch": g["stage_bytes"]},
+                     "algorithmic_bytes_per_launch": g["stage_bytes"],
+                     **({"stage": {"kernels": g["whole_name"],
+                                   "avg_launch_us": round(g["whole_ms"] * 1e3, 2),
+                                   "algorithmic_bytes_per_launch": g["whole_bytes"],
+                                   "achieved": round(whole_gbps, 1),
+                                   "frac": round(whole_gbps / HBM_PEAK_GBPS, 4)}}
+                        if g["whole_ms"] is not None else {})},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

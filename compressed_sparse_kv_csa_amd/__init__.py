@@ -16,8 +16,8 @@ __all__ = [
     "MODE_FULL",
     "MODE_REUSE", "MODE_REINDEX", "CsaParams", "Cache", "KvCacheSpec", "KvCacheBreakdown", "lib", "lib_path",
     "cache", "csa_decode_workspace_bytes", "csa_decode", "csa_select_topk_workspace_bytes",
-    "csa_select_topk", "csa_reindex_topk", "csa_reindex_topk_workspace_bytes",
-    "hca_decode_workspace_bytes",
+    "csa_select_topk", "csa_select_scan", "csa_select_merge", "csa_reindex_topk",
+    "csa_reindex_topk_workspace_bytes", "hca_decode_workspace_bytes",
     "hca_decode", "rope_output", "kv_quantize_fp4", "kv_quantize_fp8", "idx_quantize_fp4_hadamard",
     "kv_cache_write", "kv_dequantize",
     "kv_cache_bytes", "csakv_status_string", "EXPORTED_SYMBOLS",
@@ -31,7 +31,8 @@ OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 
 EXPORTED_SYMBOLS = (
     "csa_decode_workspace_bytes", "csa_decode", "csa_select_topk_workspace_bytes",
-    "csa_select_topk", "csa_reindex_topk", "csa_reindex_topk_workspace_bytes",
+    "csa_select_topk", "csa_select_scan", "csa_select_merge", "csa_reindex_topk",
+    "csa_reindex_topk_workspace_bytes",
     "hca_decode_workspace_bytes", "hca_decode", "rope_output", "kv_quantize_fp4", "kv_quantize_fp8", "idx_quantize_fp4_hadamard", "kv_cache_write",
     "kv_dequantize", "kv_cache_bytes", "csakv_status_string",
 )
@@ -73,7 +74,7 @@ class KvCacheSpec(ctypes.Structure):
 
 class KvCacheBreakdown(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
-        "csa_shared_kv", "csa_indexer", "hca_shared_kv", "windows", "swa_layers",
+        "csa_shared_kv", "csa_indexer", "hca_shared_kv", "windows", "swa_layers", "scales",
         "csa_per_layer", "hca_per_layer", "total")]
 
 
@@ -99,6 +100,10 @@ def lib() -> ctypes.CDLL:
         L.csa_select_topk_workspace_bytes.restype = SZ
         L.csa_select_topk.argtypes = [P(CsaParams), P(Cache), VP, VP, VP, VP, SZ, VP]
         L.csa_select_topk.restype = I32
+        L.csa_select_scan.argtypes = [P(CsaParams), P(Cache), VP, VP, VP, SZ, VP]
+        L.csa_select_scan.restype = I32
+        L.csa_select_merge.argtypes = [P(CsaParams), P(Cache), VP, VP, SZ, VP]
+        L.csa_select_merge.restype = I32
         L.csa_reindex_topk.argtypes = [P(CsaParams), P(Cache), VP, VP, VP, I32, VP, VP, SZ, VP]
         L.csa_reindex_topk.restype = I32
         L.csa_reindex_topk_workspace_bytes.argtypes = [P(CsaParams), I32]
@@ -202,6 +207,28 @@ def csa_select_topk(params: CsaParams, idx_keys: Cache, q_idx, w_idx, topk, work
                                _stream(stream))
     if check:
         _check(st, "csa_select_topk")
+    return st
+
+
+def csa_select_scan(params: CsaParams, idx_keys: Cache, q_idx, w_idx, workspace,
+                    workspace_bytes: int | None = None, stream=None, check: bool = True) -> int:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().csa_select_scan(ctypes.byref(params), ctypes.byref(idx_keys), _ptr(q_idx),
+                               _ptr(w_idx), _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if check:
+        _check(st, "csa_select_scan")
+    return st
+
+
+def csa_select_merge(params: CsaParams, idx_keys: Cache, topk, workspace,
+                     workspace_bytes: int | None = None, stream=None, check: bool = True) -> int:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().csa_select_merge(ctypes.byref(params), ctypes.byref(idx_keys), _ptr(topk),
+                                _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if check:
+        _check(st, "csa_select_merge")
     return st
 
 

@@ -78,7 +78,7 @@ CsaLayout csa_layout(const csakv_csa_params* p, int64_t n_c) {
 csakv_status check_select_params(const csakv_csa_params* p) {
   if (p->reserved != 0 || p->batch < 1 || p->top_k < 1 || p->n_idx_heads < 1)
     return CSAKV_ERR_INVALID;
-  if (p->top_k > csakv::kMaxTopK || p->n_idx_heads > 64) return CSAKV_ERR_UNSUPPORTED;
+  if (p->top_k > csakv::kMaxTopK || p->n_idx_heads > csakv::kMaxHeads) return CSAKV_ERR_UNSUPPORTED;
   return CSAKV_OK;
 }
 
@@ -88,7 +88,7 @@ csakv_status check_csa_params(const csakv_csa_params* p) {
   if (p->mode != CSAKV_MODE_FULL && p->mode != CSAKV_MODE_REUSE) return CSAKV_ERR_INVALID;
   if (p->top_k < 1 || p->n_q_heads < 1) return CSAKV_ERR_INVALID;
   if (p->top_k > csakv::kMaxTopK) return CSAKV_ERR_UNSUPPORTED;
-  if (p->n_q_heads % 16 != 0 || p->n_q_heads > 64) return CSAKV_ERR_UNSUPPORTED;
+  if (p->n_q_heads % 16 != 0 || p->n_q_heads > csakv::kMaxHeads) return CSAKV_ERR_UNSUPPORTED;
   if (p->mode == CSAKV_MODE_FULL) return check_select_params(p);
   return CSAKV_OK;
 }
@@ -163,16 +163,21 @@ size_t csa_select_topk_workspace_bytes(const csakv_csa_params* p, int64_t n_comp
   return round_up(csakv::indexer_workspace_bytes(p->batch, plan), kWsAlign);
 }
 
-csakv_status csa_select_topk(const csakv_csa_params* p, const csakv_cache* idx_keys,
-                             const uint16_t* q_idx, const float* w_idx, int32_t* topk,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// csa_select_topk and its two stages: validation, then the stages asked for.
+csakv_status select_stages(const csakv_csa_params* p, const csakv_cache* idx_keys,
+                           const uint16_t* q_idx, const float* w_idx, int32_t* topk,
+                           void* workspace, size_t workspace_bytes, void* stream, int stages) {
   if (!p || p->mode != CSAKV_MODE_FULL) return CSAKV_ERR_INVALID;
   csakv_status st = check_select_params(p);
   if (st != CSAKV_OK) return st;
   if ((st = check_cache(idx_keys, false)) != CSAKV_OK) return st;
   if (idx_keys->n_rows > INT32_MAX) return CSAKV_ERR_UNSUPPORTED;
-  if (!q_idx || !w_idx || !topk || !aligned(q_idx, 16) || !aligned(w_idx, 4) || !aligned(topk, 4))
+  const bool scan = stages & csakv::kStageScan, merge = stages & csakv::kStageMerge;
+  if (scan && (!q_idx || !w_idx || !aligned(q_idx, 16) || !aligned(w_idx, 4)))
     return CSAKV_ERR_INVALID;
+  if (merge && (!topk || !aligned(topk, 4))) return CSAKV_ERR_INVALID;
   const int64_t n_c = idx_keys->n_rows;
   const csakv::IndexerPlan plan = csakv::plan_indexer(p->batch, n_c, p->top_k);
   if (!csakv::indexer_supported(plan)) return CSAKV_ERR_UNSUPPORTED;
@@ -182,8 +187,30 @@ csakv_status csa_select_topk(const csakv_csa_params* p, const csakv_cache* idx_k
   return hip_status(csakv::launch_indexer(
       idx_keys->fmt, static_cast<const uint8_t*>(idx_keys->codes), idx_keys->scales,
       idx_keys->seq_stride_rows, paging(idx_keys), n_c, idx_keys->seq_rows, q_idx, w_idx, p->batch,
-      p->n_idx_heads, p->top_k, plan,
-      workspace, topk, static_cast<hipStream_t>(stream)));
+      p->n_idx_heads, p->top_k, plan, workspace, topk, static_cast<hipStream_t>(stream), stages));
+}
+
+}  // namespace
+
+csakv_status csa_select_topk(const csakv_csa_params* p, const csakv_cache* idx_keys,
+                             const uint16_t* q_idx, const float* w_idx, int32_t* topk,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return select_stages(p, idx_keys, q_idx, w_idx, topk, workspace, workspace_bytes, stream,
+                       csakv::kStageScan | csakv::kStageMerge);
+}
+
+csakv_status csa_select_scan(const csakv_csa_params* p, const csakv_cache* idx_keys,
+                             const uint16_t* q_idx, const float* w_idx, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return select_stages(p, idx_keys, q_idx, w_idx, nullptr, workspace, workspace_bytes, stream,
+                       csakv::kStageScan);
+}
+
+csakv_status csa_select_merge(const csakv_csa_params* p, const csakv_cache* idx_keys,
+                              int32_t* topk, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return select_stages(p, idx_keys, nullptr, nullptr, topk, workspace, workspace_bytes, stream,
+                       csakv::kStageMerge);
 }
 
 size_t csa_reindex_topk_workspace_bytes(const csakv_csa_params* p, int32_t n_pool) {
@@ -233,7 +260,7 @@ csakv_status hca_decode(int32_t batch, int32_t n_q_heads, float softmax_scale,
                         const csakv_cache* kv, const uint16_t* q, uint16_t* out, void* workspace,
                         size_t workspace_bytes, void* stream) {
   if (batch < 1 || n_q_heads < 1 || !std::isfinite(softmax_scale)) return CSAKV_ERR_INVALID;
-  if (n_q_heads % 16 != 0 || n_q_heads > 64) return CSAKV_ERR_UNSUPPORTED;
+  if (n_q_heads % 16 != 0 || n_q_heads > csakv::kMaxHeads) return CSAKV_ERR_UNSUPPORTED;
   csakv_status st = check_cache(kv, true);
   if (st != CSAKV_OK) return st;
   if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return CSAKV_ERR_INVALID;
@@ -333,23 +360,27 @@ uint64_t kv_cache_bytes(const kv_cache_spec* sp, int64_t seq_len, kv_cache_break
       sp->idx_dim < 0 || sp->count_window < 0 || sp->count_window > 2 || sp->count_scales < 0 ||
       sp->count_scales > 1 || sp->swa_layer_bytes < 0)
     return 0;
-  uint64_t s_kv;
+  // Code bytes per row, and FP4 scale bytes per row (added to the row when count_scales).
+  uint64_t s_kv, sc_kv = 0;
   switch (sp->kv_fmt) {
     case CSAKV_KV_BF16: s_kv = 2ull * sp->kv_dim; break;
     case CSAKV_KV_FP8_MIXED: s_kv = (uint64_t)(sp->kv_dim - sp->rope_dim) + 2ull * sp->rope_dim; break;
     case CSAKV_KV_FP4:
       if (sp->kv_dim % 16) return 0;
-      s_kv = sp->kv_dim / 2 + (sp->count_scales ? sp->kv_dim / 16 : 0);
+      s_kv = sp->kv_dim / 2;
+      sc_kv = sp->kv_dim / 16;
       break;
     default: return 0;
   }
-  uint64_t s_idx = 0;
+  uint64_t s_idx = 0, sc_idx = 0;
   if (sp->idx_dim > 0) {
     switch (sp->idx_fmt) {
       case CSAKV_IDX_BF16: s_idx = 2ull * sp->idx_dim; break;
       case CSAKV_IDX_FP4:
+      case CSAKV_IDX_FP4_HADAMARD:  // the same bytes: codes of the rotated row, and scales
         if (sp->idx_dim % 16) return 0;
-        s_idx = sp->idx_dim / 2 + (sp->count_scales ? sp->idx_dim / 16 : 0);
+        s_idx = sp->idx_dim / 2;
+        sc_idx = sp->idx_dim / 16;
         break;
       default: return 0;
     }
@@ -357,8 +388,15 @@ uint64_t kv_cache_bytes(const kv_cache_spec* sp, int64_t seq_len, kv_cache_break
   const uint64_t n = (uint64_t)seq_len;
   const uint64_t n_c = sp->n_csa ? n / sp->csa_ratio : 0;
   const uint64_t n_h = sp->n_hca ? n / sp->hca_ratio : 0;
-  const uint64_t win = (uint64_t)sp->count_window * sp->window * s_kv;
+  const uint64_t cw = (uint64_t)sp->count_window;
   kv_cache_breakdown r{};
+  r.scales = sp->n_csa * (n_c * (sc_kv + sc_idx) + cw * sp->window * sc_kv) +
+             sp->n_hca * (n_h + cw * sp->window) * sc_kv;
+  if (sp->count_scales) {
+    s_kv += sc_kv;
+    s_idx += sc_idx;
+  }
+  const uint64_t win = cw * sp->window * s_kv;
   r.csa_per_layer = n_c * s_kv + n_c * s_idx + win;
   r.hca_per_layer = n_h * s_kv + win;
   r.csa_shared_kv = sp->n_csa * n_c * s_kv;

@@ -125,37 +125,47 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const uint16_t* __rest
   }
 }
 
-// Hadamard-rotated FP4 indexer keys: one thread per 128-wide bf16 row, rotated in
-// registers, then the FP4 block codec on the rotated values.
+// Hadamard-rotated FP4 indexer keys: 16 lanes per 128-wide bf16 row, lane j holding
+// channels 8j .. 8j + 7 in fp64.  Butterflies h = 1, 2, 4 run in registers and h = 8 .. 64
+// across lanes j ^ 1 .. j ^ 8; every sum is exact, so the fp32 value of each channel is the
+// exact H x rounded once, then scaled once.  The 16-channel FP4 blocks span lane pairs
+// (2k, 2k + 1): their amax is exchanged, each lane encodes its 8 codes (one dword) and
+// the even lane stores the block's scale byte.
 __global__ __launch_bounds__(256) void quantize_fp4h_kernel(const uint16_t* __restrict__ x,
                                                             int64_t rows,
                                                             uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales) {
-#pragma clang fp contract(off)
-  for (int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; r < rows;
-       r += (int64_t)gridDim.x * blockDim.x) {
-    float y[128];
-    const u32x4* src = reinterpret_cast<const u32x4*>(x + r * 128);
+  const int j = threadIdx.x & 15;  // lane of the row's 16
+  const int64_t groups = (int64_t)gridDim.x * (blockDim.x / 16);
+  for (int64_t r = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / 16; r < rows; r += groups) {
+    // (r is uniform over the 16 lanes of a row, so all of them take part in every shuffle)
+    const u32x4 w = reinterpret_cast<const u32x4*>(x + r * 128)[j];
+    double y[8];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const u32x4 w = src[k];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        y[8 * k + 2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
-        y[8 * k + 2 * j + 1] = bf16_to_f32(w[j] >> 16);
-      }
+    for (int i = 0; i < 4; ++i) {
+      y[2 * i] = (double)bf16_to_f32(w[i] & 0xFFFFu);
+      y[2 * i + 1] = (double)bf16_to_f32(w[i] >> 16);
     }
-    hadamard_stages<128>(y);
+    hadamard_stages<8>(y);
 #pragma unroll
-    for (int i = 0; i < 128; ++i) y[i] *= kHadamardScale;
+    for (int m = 1; m < 16; m *= 2) hadamard_lane_stage<8>(y, m, (j & m) != 0);
+    float v[8];
+    float amax = 0.0f;
 #pragma unroll
-    for (int blk = 0; blk < 8; ++blk) {
-      u32x2 c;
-      uint32_t sc;
-      fp4_block_f32(y + 16 * blk, &c, &sc);
-      reinterpret_cast<u32x2*>(codes + r * 64)[blk] = c;
-      scales[r * 8 + blk] = (uint8_t)sc;
+    for (int i = 0; i < 8; ++i) {
+      v[i] = hadamard_round_scale(y[i]);
+      amax = fmaxf(amax, fabsf(v[i]));
     }
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    const uint32_t sc = f32_to_e4m3(amax / 6.0f);
+    const float s = e4m3_to_f32(sc);
+    uint32_t packed = 0u;
+    if (s != 0.0f) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) packed |= f32_to_e2m1(v[i] / s) << (4 * i);
+    }
+    reinterpret_cast<uint32_t*>(codes + r * 64)[j] = packed;
+    if ((j & 1) == 0) scales[r * 8 + (j >> 1)] = (uint8_t)sc;
   }
 }
 
@@ -235,8 +245,8 @@ hipError_t launch_quantize_fp8_mixed(const uint16_t* x, int64_t rows, int dim, i
 hipError_t launch_quantize_fp4h(const uint16_t* x, int64_t rows, uint8_t* codes, uint8_t* scales,
                                 hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(quantize_fp4h_kernel, dim3(grid_for(rows, 256)), dim3(256), 0, stream, x, rows,
-                     codes, scales);
+  hipLaunchKernelGGL(quantize_fp4h_kernel, dim3(grid_for(rows * 16, 256)), dim3(256), 0, stream, x,
+                     rows, codes, scales);
   return hipGetLastError();
 }
 

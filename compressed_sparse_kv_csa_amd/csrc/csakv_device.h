@@ -101,25 +101,41 @@ __device__ __forceinline__ void fp4_block_f32(const float* v, u32x2* codes, uint
 
 // ---------------------------------------------------------------- Hadamard rotation
 
-// The indexer's 128-wide Hadamard rotation, H x / sqrt(128) with H the Sylvester matrix,
-// computed as the fast transform in one fixed order (each step one fp32 rounding): for
-// h = 1, 2, ..., 64 every pair (i, i + h) with bit h of i clear becomes
-// (x[i] + x[i+h], x[i] - x[i+h]); then every element is scaled by fp32(1/sqrt(128)).
+// The indexer's 128-wide Hadamard rotation, H x / sqrt(128) with H the Sylvester matrix:
+// the product H x is formed exactly (fast-transform butterflies in fp64: for bf16 rows whose
+// nonzero magnitudes span at most 38 binades every sum is exact, so the butterfly order
+// does not matter), rounded once to fp32, then multiplied once by fp32(1/sqrt(128)).
 constexpr float kHadamardScale = 0x1.6a09e6p-4f;  // fp32(1 / sqrt(128))
 
-// The in-register stages h = 1 .. N/2 of N consecutive channels.
-template <int N>
-__device__ __forceinline__ void hadamard_stages(float* y) {
-#pragma clang fp contract(off)
+// The in-register butterfly stages h = 1 .. N/2 of N consecutive channels.
+template <int N, class T>
+__device__ __forceinline__ void hadamard_stages(T* y) {
 #pragma unroll
   for (int h = 1; h < N; h *= 2)
 #pragma unroll
     for (int i = 0; i < N; ++i)
       if ((i & h) == 0) {
-        const float a = y[i], b = y[i + h];
+        const T a = y[i], b = y[i + h];
         y[i] = a + b;
         y[i + h] = a - b;
       }
+}
+
+// One butterfly stage across lanes: the lane holding the upper half of each pair (`upper`)
+// takes partner - own, the lower one own + partner; `mask` selects the partner lane.
+template <int N>
+__device__ __forceinline__ void hadamard_lane_stage(double* y, int mask, bool upper) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const double p = __shfl_xor(y[i], mask);
+    y[i] = upper ? p - y[i] : y[i] + p;
+  }
+}
+
+// An exact H x value, rounded once to fp32 and scaled once (both round to nearest even).
+__device__ __forceinline__ float hadamard_round_scale(double v) {
+#pragma clang fp contract(off)
+  return (float)v * kHadamardScale;
 }
 
 // ---------------------------------------------------------------- FP4 block decode

@@ -42,7 +42,8 @@ struct IndexerPlan {
 };
 
 constexpr int kSliceRows = 4096;
-constexpr int kMaxTopK = 1024;
+constexpr int kMaxTopK = 2048;
+constexpr int kMaxHeads = 128;  // query heads (a multiple of 16) and indexer heads
 constexpr int kMergeCap = 8192;
 constexpr int kMaxMergeSlices = 512;
 
@@ -67,12 +68,17 @@ IndexerPlan plan_indexer(int batch, int64_t n_c, int top_k);
 bool indexer_supported(const IndexerPlan& plan);
 size_t indexer_workspace_bytes(int batch, const IndexerPlan& plan);
 
+// The two stages of the indexer: the scan leaves each slice's candidates, bound and
+// scores in the workspace; the merge reads them and writes topk.
+constexpr int kStageScan = 1;
+constexpr int kStageMerge = 2;
+
 hipError_t launch_indexer(int key_fmt, const uint8_t* codes, const uint8_t* scales,
                           int64_t seq_stride, const Paging& pg, int64_t n_c, const int32_t* seq_rows,
                           const uint16_t* q_idx,
                           const float* w_idx, int batch, int n_heads, int top_k,
                           const IndexerPlan& plan, void* workspace, int32_t* topk,
-                          hipStream_t stream);
+                          hipStream_t stream, int stages = kStageScan | kStageMerge);
 
 // ------------------------------------------------------------------ attention
 struct AttnPlan {

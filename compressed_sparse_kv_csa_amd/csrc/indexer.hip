@@ -530,22 +530,22 @@ __device__ __forceinline__ f16x8 fp4x8_to_f16(uint32_t cw, uint32_t scale_code) 
   return as_f16x8(r);
 }
 
-// Hadamard-rotated FP4 indexer queries (keys stored in the same form).  Wave ht of the
-// workgroup prepares head tile ht: the 4 lanes g of head n's row hold its channels
-// 32g .. 32g+31 and rotate the row together (stages h = 1..16 in registers, h = 32 and 64
-// across lanes g ^ 1 and g ^ 2, in that order, as the codec does), quantise their two
-// 16-channel blocks with the FP4 codec, and leave the decoded values (exact in fp16, in
-// the FP4 key tile's channel order) in LDS, from where every wave takes its A operands.
-// `stage` holds HT * 4 * 64 fragments; it is free again when this returns.
-template <int HT>
+// Hadamard-rotated FP4 indexer queries (keys stored in the same form).  Wave w of the NW
+// waves prepares head tiles w, w + NW, ...; for head tile ht the 4 lanes g of head n's row hold its channels
+// 32g .. 32g+31 in fp64 and rotate the row together (stages h = 1..16 in registers, h = 32
+// and 64 across lanes g ^ 1 and g ^ 2; every sum is exact), round each value once to fp32
+// and scale it once, quantise their two 16-channel blocks with the FP4 codec, and leave the
+// decoded values (exact in fp16, in the FP4 key tile's channel order) in LDS, from where
+// every wave takes its A operands.  `stage` holds HT * 4 * 64 fragments; it is free again
+// when this returns.
+template <int HT, int NW>
 __device__ __forceinline__ void query_frags_fp4h(const uint16_t* __restrict__ q_idx, int b,
                                                  int n_heads, int wave, int g, int n,
                                                  f16x8 (&qa)[HT][4], f16x8* stage) {
-#pragma clang fp contract(off)
   const int lane = threadIdx.x & (kWave - 1);
-  if (wave < HT) {
-    const int head = 16 * wave + n;
-    float y[32];
+  for (int ht = wave; ht < HT; ht += NW) {  // wave-uniform
+    const int head = 16 * ht + n;
+    double y[32];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       u32x4 v = {0u, 0u, 0u, 0u};
@@ -553,28 +553,21 @@ __device__ __forceinline__ void query_frags_fp4h(const uint16_t* __restrict__ q_
         v = *reinterpret_cast<const u32x4*>(q_idx + ((int64_t)b * n_heads + head) * kIdxDim + 32 * g + 8 * k);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        y[8 * k + 2 * j] = bf16_to_f32(v[j] & 0xFFFFu);
-        y[8 * k + 2 * j + 1] = bf16_to_f32(v[j] >> 16);
+        y[8 * k + 2 * j] = (double)bf16_to_f32(v[j] & 0xFFFFu);
+        y[8 * k + 2 * j + 1] = (double)bf16_to_f32(v[j] >> 16);
       }
     }
     hadamard_stages<32>(y);
+    hadamard_lane_stage<32>(y, 16, (g & 1) != 0);  // h = 32: lanes g, g ^ 1
+    hadamard_lane_stage<32>(y, 32, (g & 2) != 0);  // h = 64: lanes g, g ^ 2
+    float yf[32];
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {  // h = 32: channel pairs (i, i + 32) live in lanes g, g ^ 1
-      const float p = __shfl_xor(y[j], 16);
-      y[j] = (g & 1) ? p - y[j] : y[j] + p;
-    }
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {  // h = 64: lanes g, g ^ 2
-      const float p = __shfl_xor(y[j], 32);
-      y[j] = (g & 2) ? p - y[j] : y[j] + p;
-    }
-#pragma unroll
-    for (int j = 0; j < 32; ++j) y[j] *= kHadamardScale;
+    for (int j = 0; j < 32; ++j) yf[j] = hadamard_round_scale(y[j]);
     u32x2 c0, c1;
     uint32_t s0, s1;
-    fp4_block_f32(y, &c0, &s0);
-    fp4_block_f32(y + 16, &c1, &s1);
-    f16x8* out = stage + wave * 4 * kWave + lane;
+    fp4_block_f32(yf, &c0, &s0);
+    fp4_block_f32(yf + 16, &c1, &s1);
+    f16x8* out = stage + ht * 4 * kWave + lane;
     out[0 * kWave] = fp4x8_to_f16(c0[0], s0);
     out[1 * kWave] = fp4x8_to_f16(c0[1], s0);
     out[2 * kWave] = fp4x8_to_f16(c1[0], s1);
@@ -600,35 +593,41 @@ __device__ __forceinline__ float query_weight_load(const float* __restrict__ w_i
 }
 
 // The query fragments and head weights of query b; QH: Hadamard-rotated FP4 queries.
-// bf16 indexer queries, prepared once per workgroup: wave ht loads head tile ht and its
-// largest magnitude; all waves then agree on the query's power-of-two scale (fp16 path),
-// wave ht converts its fragments into LDS, and every wave takes all of them.  `red` holds
-// HT floats, `stage` HT * 256 fragments; both are free again when this returns.
-template <class KT, int HT>
+// bf16 indexer queries, prepared once per workgroup: wave w of the NW waves loads head
+// tiles w, w + NW, ... and their largest magnitudes; all waves then agree on the query's
+// power-of-two scale (fp16 path), each wave converts its tiles' fragments into LDS, and
+// every wave takes all of them.  `red` holds HT floats, `stage` HT * 256 fragments; both
+// are free again when this returns.
+template <class KT, int HT, int NW>
 __device__ __forceinline__ void query_frags_staged(const uint16_t* __restrict__ q_idx, int b,
                                                    int n_heads, int wave, int g, int n,
                                                    typename KT::Op (&qa)[HT][4], u32x4* stage,
                                                    float* red) {
   typedef typename KT::Op Op;
   const int lane = threadIdx.x & (kWave - 1);
-  u32x4 raw[4];
-  if (wave < HT) {
-    const int head = 16 * wave + n;
-    float qmax = 0.0f;
+  constexpr int kPer = (HT + NW - 1) / NW;  // head tiles per wave
+  u32x4 raw[kPer][4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (head < n_heads)
-        v = *reinterpret_cast<const u32x4*>(q_idx + ((int64_t)b * n_heads + head) * kIdxDim +
-                                            KT::q_channel(g, t));
-      raw[t] = v;
+  for (int i = 0; i < kPer; ++i) {
+    const int ht = wave + NW * i;
+    if (ht < HT) {  // wave-uniform
+      const int head = 16 * ht + n;
+      float qmax = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        qmax = fmaxf(qmax, fmaxf(fabsf(bf16_to_f32(v[i] & 0xFFFFu)), fabsf(bf16_to_f32(v[i] >> 16))));
+      for (int t = 0; t < 4; ++t) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (head < n_heads)
+          v = *reinterpret_cast<const u32x4*>(q_idx + ((int64_t)b * n_heads + head) * kIdxDim +
+                                              KT::q_channel(g, t));
+        raw[i][t] = v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          qmax = fmaxf(qmax, fmaxf(fabsf(bf16_to_f32(v[j] & 0xFFFFu)), fabsf(bf16_to_f32(v[j] >> 16))));
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, off));
+      if (lane == 0) red[ht] = qmax;
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, off));
-    if (lane == 0) red[wave] = qmax;
   }
   lds_barrier();
   float qmax = red[0];
@@ -639,10 +638,14 @@ __device__ __forceinline__ void query_frags_staged(const uint16_t* __restrict__ 
   if (qmax > 0.0f) p = 14 - ((int)((__float_as_uint(qmax) >> 23) & 0xFF) - 127);
   p = max(-100, min(p, 100));
   const float qscale = __builtin_ldexpf(1.0f, p);
-  if (wave < HT) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      stage[(wave * 4 + t) * kWave + lane] = __builtin_bit_cast(u32x4, q_operand(raw[t], qscale, (Op*)nullptr));
+  for (int i = 0; i < kPer; ++i) {
+    const int ht = wave + NW * i;
+    if (ht < HT) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        stage[(ht * 4 + t) * kWave + lane] = __builtin_bit_cast(u32x4, q_operand(raw[i][t], qscale, (Op*)nullptr));
+    }
   }
   lds_barrier();
 #pragma unroll
@@ -658,7 +661,7 @@ __device__ __forceinline__ void query_frags_staged(const uint16_t* __restrict__ 
 // which the caller keeps until every wave has left this function.  `w_pre`: this
 // thread's query_weight_load.  wv gets the weights of the accumulator rows lane (g, n)
 // holds (heads 16*ht + 4g + i).
-template <class KT, int HT, bool QH>
+template <class KT, int HT, bool QH, int NW>
 __device__ __forceinline__ void query_setup(const uint16_t* __restrict__ q_idx, float w_pre,
                                             int b, int n_heads, int wave, int g, int n,
                                             typename KT::Op (&qa)[HT][4], float (&wv)[HT][4],
@@ -666,9 +669,9 @@ __device__ __forceinline__ void query_setup(const uint16_t* __restrict__ q_idx, 
   if (threadIdx.x < 16 * HT) s_w[threadIdx.x] = w_pre;  // ordered by the barriers below
   if constexpr (QH) {
     static_assert(KT::kScales, "rotated FP4 queries meet rotated FP4 keys");
-    query_frags_fp4h<HT>(q_idx, b, n_heads, wave, g, n, qa, static_cast<f16x8*>(stage));
+    query_frags_fp4h<HT, NW>(q_idx, b, n_heads, wave, g, n, qa, static_cast<f16x8*>(stage));
   } else {
-    query_frags_staged<KT, HT>(q_idx, b, n_heads, wave, g, n, qa, static_cast<u32x4*>(stage), red);
+    query_frags_staged<KT, HT, NW>(q_idx, b, n_heads, wave, g, n, qa, static_cast<u32x4*>(stage), red);
   }
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht)
@@ -679,13 +682,35 @@ __device__ __forceinline__ void query_setup(const uint16_t* __restrict__ q_idx, 
 // Lane (g, n)'s share of the score of its tile row n: the sum over the heads it holds
 // (16 * ht + 4g + i) of w_h * ReLU(acc).  The four lane groups' shares add up to the
 // score.  ReLU is a signed-integer max: negative floats (and -0) have the sign bit set.
-template <int HT>
-__device__ __forceinline__ float weighted_relu_share(const f32x4 (&acc)[HT], const float (&wv)[HT][4]) {
+template <int N, int HT>
+__device__ __forceinline__ float weighted_relu_share(const f32x4 (&acc)[N], const float (&wv)[HT][4],
+                                                     int hg, float sc = 0.0f) {
+#pragma unroll
+  for (int ht = 0; ht < N; ++ht)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc += wv[hg + ht][i] * __int_as_float(max(__float_as_int(acc[ht][i]), 0));
+  return sc;
+}
+
+// Lane (g, n)'s share of the score of key-tile row n for all HT head tiles: the MFMAs of
+// up to 4 head tiles at a time (so that at most 4 accumulators are live), each group's
+// ReLU-weighted heads added to the share.
+template <class KT, int HT>
+__device__ __forceinline__ float tile_share(const typename KT::Op (&qa)[HT][4],
+                                            const typename KT::Op (&kb)[4], const float (&wv)[HT][4]) {
+  constexpr int G = HT < 4 ? HT : 4;
   float sc = 0.0f;
 #pragma unroll
-  for (int ht = 0; ht < HT; ++ht)
+  for (int hg = 0; hg < HT; hg += G) {
+    f32x4 acc[G];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc += wv[ht][i] * __int_as_float(max(__float_as_int(acc[ht][i]), 0));
+    for (int i = 0; i < G; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < G; ++i) acc[i] = KT::mma(qa[hg + i][t], kb[t], acc[i]);
+    sc = weighted_relu_share<G, HT>(acc, wv, hg, sc);
+  }
   return sc;
 }
 
@@ -776,10 +801,12 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
   };
 
   const float w_pre = query_weight_load<HT>(w_idx, b, n_heads);
-  // The ring's first loads go out before the query setup, which they overlap.
-  KT ring[kRing];
+  // The ring's first loads go out before the query setup, which they overlap.  With more
+  // than 64 heads the bf16 ring is halved: 128 heads' query fragments take 128 registers.
+  constexpr int RING = (HT > 4 && !KT::kScales) ? 2 : kRing;
+  KT ring[RING];
 #pragma unroll
-  for (int d = 0; d < kRing; ++d) {
+  for (int d = 0; d < RING; ++d) {
     ring[d].set_lane(g);
     load_slot(ring[d], d);
   }
@@ -787,10 +814,11 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
   // Indexer query fragments and head weights.
   Op qa[HT][4];
   float wv[HT][4];
-  static_assert(sizeof(s_part) >= sizeof(f16x8) * 4 * 4 * kWave, "query stage");
+  static_assert(sizeof(s_part) >= sizeof(f16x8) * HT * 4 * kWave, "query stage");
   static_assert(sizeof(sm.hist) >= sizeof(float) * 16 * HT, "weight stage");
-  query_setup<KT, HT, QH>(q_idx, w_pre, b, n_heads, wave, g, n, qa, wv, s_part,
-                          reinterpret_cast<float*>(sm.red32), reinterpret_cast<float*>(sm.hist));
+  static_assert(sizeof(sm.red32) >= sizeof(float) * HT, "query maxima");
+  query_setup<KT, HT, QH, kScanWaves>(q_idx, w_pre, b, n_heads, wave, g, n, qa, wv, s_part,
+                                      reinterpret_cast<float*>(sm.red32), reinterpret_cast<float*>(sm.hist));
 
   // Lane (g, n)'s share of tile row r of a pass goes to s_part[4 * r + g]: the slot of
   // tile wave + 8m of pass ps is row (ps % kPassesPerSlice) * kSubRows + 16 * (wave + 8m)
@@ -800,23 +828,16 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
     float* const pass_part = s_part + 4 * (ps % kPassesPerSlice) * kSubRows + lane_part;
 #pragma unroll
     for (int m = 0; m < kSubTiles; ++m) {
-      const int d = m % kRing;
+      const int d = m % RING;
       const int k = ps * kSubTiles + m;
       // Keep each tile's instructions together: hoisting a later tile's decode above
       // this point would wait on that tile's key load, which is still in flight.
       __builtin_amdgcn_sched_barrier(0);
       Op kb[4];
       ring[d].decode(kb);
-      load_slot(ring[d], k + kRing);  // past the end: reads zeros
-      f32x4 acc[HT];
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) acc[ht] = KT::mma(qa[ht][t], kb[t], acc[ht]);
+      load_slot(ring[d], k + RING);  // past the end: reads zeros
       // Each lane stores its share; the shares are added when the slice is complete.
-      pass_part[4 * 16 * kScanWaves * m] = weighted_relu_share<HT>(acc, wv);
+      pass_part[4 * 16 * kScanWaves * m] = tile_share<KT, HT>(qa, kb, wv);
     }
     if ((ps + 1) % kPassesPerSlice != 0 && ps + 1 < n_pass) continue;  // more passes in this slice
 
@@ -919,7 +940,8 @@ __global__ __launch_bounds__(kMergeThreads) void indexer_merge_kernel(
     IndexerWs ws, int64_t n_c, const int32_t* __restrict__ seq_rows, int top_k, int n_slices,
     int cap, int first, int32_t* __restrict__ topk) {
   __shared__ uint64_t s_buf[kMergeCap];
-  __shared__ uint64_t s_list[kMergeListCap];
+  // The boundary bin's keys (block_kth_exact), and the current winners (up to top_k).
+  __shared__ uint64_t s_list[kMaxTopK > kMergeListCap ? kMaxTopK : kMergeListCap];
   __shared__ uint64_t s_bound[kMaxMergeSlices];
   __shared__ uint32_t s_off[kMaxMergeSlices + 1];
   __shared__ int s_sat[kMaxMergeSlices];
@@ -1061,9 +1083,9 @@ __global__ __launch_bounds__(kReindexScoreThreads) void reindex_score_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx, int n_heads,
     const int32_t* __restrict__ pool, int n_pool, int n_parts, uint64_t* __restrict__ keys) {
   typedef typename KT::Op Op;
-  __shared__ u32x4 s_stage[4 * 4 * kWave];  // query fragments of up to 4 head tiles
-  __shared__ float s_red[4];
-  __shared__ float s_w[64];
+  __shared__ u32x4 s_stage[HT * 4 * kWave];  // query fragments of the HT head tiles
+  __shared__ float s_red[HT];
+  __shared__ float s_w[16 * HT];
   const int b = blockIdx.x / n_parts;
   const int part = blockIdx.x - b * n_parts;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -1076,7 +1098,8 @@ __global__ __launch_bounds__(kReindexScoreThreads) void reindex_score_kernel(
   const float w_pre = query_weight_load<HT>(w_idx, b, n_heads);
   Op qa[HT][4];
   float wv[HT][4];
-  query_setup<KT, HT, QH>(q_idx, w_pre, b, n_heads, wave, g, n, qa, wv, s_stage, s_red, s_w);
+  query_setup<KT, HT, QH, kReindexScoreWaves>(q_idx, w_pre, b, n_heads, wave, g, n, qa, wv, s_stage,
+                                              s_red, s_w);
 
   const int row = (r >= 0 && r < n_c) ? r : -1;
   const int at = row < 0 || !pg.table
@@ -1098,14 +1121,7 @@ __global__ __launch_bounds__(kReindexScoreThreads) void reindex_score_kernel(
           at >= 0 ? (uint32_t)at * (kIdxDim / 16) + KT::scale_offset(0, g) : kAbsentKeyOffset);
   Op kb[4];
   kt.decode(kb);
-  f32x4 acc[HT];
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) acc[ht] = KT::mma(qa[ht][k], kb[k], acc[ht]);
-  const float sc = wave_sum_rows(weighted_relu_share<HT>(acc, wv));
+  const float sc = wave_sum_rows(tile_share<KT, HT>(qa, kb, wv));
   if (g == 0 && pos < n_pool)
     keys[(int64_t)b * n_pool + pos] = row >= 0 ? compose_key(f32_order_key(sc), (uint32_t)row) : 0ull;
 }
@@ -1165,7 +1181,8 @@ void launch_reindex_ht(int ht, hipStream_t stream, const uint8_t* codes, const u
     case 1: CSAKV_REINDEX(1); break;
     case 2: CSAKV_REINDEX(2); break;
     case 3: CSAKV_REINDEX(3); break;
-    default: CSAKV_REINDEX(4); break;
+    case 4: CSAKV_REINDEX(4); break;
+    default: CSAKV_REINDEX(8); break;  // 65..128 heads (heads past n_heads are zero)
   }
 #undef CSAKV_REINDEX
 }
@@ -1203,7 +1220,8 @@ void launch_scan_ht(int ht, hipStream_t stream, const uint8_t* codes, const uint
     case 1: CSAKV_SCAN(1); break;
     case 2: CSAKV_SCAN(2); break;
     case 3: CSAKV_SCAN(3); break;
-    default: CSAKV_SCAN(4); break;
+    case 4: CSAKV_SCAN(4); break;
+    default: CSAKV_SCAN(8); break;  // 65..128 heads (heads past n_heads are zero)
   }
 #undef CSAKV_SCAN
 }
@@ -1270,9 +1288,9 @@ hipError_t launch_indexer(int key_fmt, const uint8_t* codes, const uint8_t* scal
                           int64_t seq_stride, const Paging& pg, int64_t n_c,
                           const int32_t* seq_rows, const uint16_t* q_idx, const float* w_idx,
                           int batch, int n_heads, int top_k, const IndexerPlan& plan,
-                          void* workspace, int32_t* topk, hipStream_t stream) {
+                          void* workspace, int32_t* topk, hipStream_t stream, int stages) {
   const IndexerWs ws = carve_indexer_ws(workspace, batch, plan);
-  if (plan.n_slices > 0) {
+  if (plan.n_slices > 0 && (stages & kStageScan)) {
     const int ht = (n_heads + 15) / 16;
     if (key_fmt == 0)
       launch_scan_ht<KeyTileBf16>(ht, stream, codes, scales, seq_stride, pg, n_c, seq_rows, q_idx, w_idx, batch,
@@ -1286,8 +1304,9 @@ hipError_t launch_indexer(int key_fmt, const uint8_t* codes, const uint8_t* scal
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(indexer_merge_kernel, dim3(batch), dim3(kMergeThreads), 0, stream, ws, n_c, seq_rows,
-                     top_k, plan.n_slices, plan.cap, plan.first, topk);
+  if (stages & kStageMerge)
+    hipLaunchKernelGGL(indexer_merge_kernel, dim3(batch), dim3(kMergeThreads), 0, stream, ws, n_c, seq_rows,
+                       top_k, plan.n_slices, plan.cap, plan.first, topk);
   return hipGetLastError();
 }
 

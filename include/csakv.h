@@ -110,14 +110,20 @@ typedef struct {
 
 typedef struct {
   int32_t batch;            /* B >= 1 query tokens, one independent sequence each  */
-  int32_t n_q_heads;        /* H_q: 16, 32, 48 or 64                                 */
-  int32_t n_idx_heads;      /* H_I: 1..64 (FULL mode)                               */
-  int32_t top_k;            /* 1..1024                                              */
+  int32_t n_q_heads;        /* H_q: a multiple of 16, at most 128                    */
+  int32_t n_idx_heads;      /* H_I: 1..128 (FULL mode)                              */
+  int32_t top_k;            /* 1..2048                                              */
   int32_t window;           /* window rows at the start of each sequence, >= 0      */
   int32_t mode;             /* csakv_mode                                           */
   float softmax_scale;      /* logit scale, e.g. 1/sqrt(512)                        */
   int32_t reserved;         /* must be 0                                            */
 } csakv_csa_params;
+
+/* Head and selection limits follow the pages: V4-Pro's query projection yields 128 heads
+ * of 512 ("DeepSeek-V4 KV Cache 深度分析", section 十一 forward-flow diagram), and its
+ * indexer keeps the top 1024 (section 一 index_topk; 512 on the V4.1-Flash page); the
+ * library accepts up to 128 heads of either kind and top_k up to 2048.  Calls beyond
+ * them return CSAKV_ERR_UNSUPPORTED.  */
 
 /* Bytes of workspace csa_decode needs for these parameters and N_c compressed rows. */
 size_t csa_decode_workspace_bytes(const csakv_csa_params* p, int64_t n_compressed);
@@ -155,6 +161,21 @@ csakv_status csa_select_topk(const csakv_csa_params* p, const csakv_cache* idx_k
                              const uint16_t* q_idx, const float* w_idx, int32_t* topk,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* The two stages of csa_select_topk, for callers that schedule them apart (and to time
+ * the scoring pass on its own).  csa_select_scan scores every key row and leaves, in the
+ * workspace, each 4096-row slice's candidates (every key at or above a per-slice bound),
+ * the bound and every row's score; csa_select_merge then writes topk exactly as
+ * csa_select_topk does (it re-reads a slice's scores when its bound lies above the k-th
+ * score).  Both take the arguments csa_select_topk takes, the same workspace (of
+ * csa_select_topk_workspace_bytes bytes, unchanged between the two calls) and the same
+ * p and idx_keys; run in this order on one stream, they equal one csa_select_topk call. */
+csakv_status csa_select_scan(const csakv_csa_params* p, const csakv_cache* idx_keys,
+                             const uint16_t* q_idx, const float* w_idx, void* workspace,
+                             size_t workspace_bytes, void* stream);
+csakv_status csa_select_merge(const csakv_csa_params* p, const csakv_cache* idx_keys,
+                              int32_t* topk, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* CSA2 Reindex, the hierarchical sparse indexer ("DeepSeek, KV 캐시를 토큰당 890바이트로
  * 줄인 V4.1-Flash 공개", section 핵심 내용: a Reindex layer computes only a new query and
  * re-ranks; "KV cache 890 bajtów na token", section "Trzy mechanizmy zamiast jednej
@@ -162,8 +183,8 @@ csakv_status csa_select_topk(const csakv_csa_params* p, const csakv_cache* idx_k
  * so their indexing cost no longer grows with the context).  For each query b, the rows
  * of pool[b] are scored with this layer's indexer query as s_j = sum_h w_h *
  * ReLU(q_h . k_j) over the shared indexer keys, and the top_k of the pool are kept.
- *   p         mode CSAKV_MODE_REINDEX; batch, n_idx_heads (1..64) and top_k
- *             (1..1024) are used, n_q_heads, window and softmax_scale are not.
+ *   p         mode CSAKV_MODE_REINDEX; batch, n_idx_heads (1..128) and top_k
+ *             (1..2048) are used, n_q_heads, window and softmax_scale are not.
  *   idx_keys  the shared indexer keys, n_rows = N_c, any csakv_idx_fmt; one sequence's
  *             keys (codes, and FP4 scales) must span at most 4 GiB - 256 bytes.
  *   q_idx     [B][H_I][128] bf16, this layer's indexer queries.
@@ -209,25 +230,35 @@ csakv_status hca_decode(int32_t batch, int32_t n_q_heads, float softmax_scale,
 csakv_status rope_output(uint16_t* out, int32_t batch, int32_t n_heads, const int64_t* positions,
                          double base, void* stream);
 
-/* FP4 block quantisation of bf16 rows x [rows][dim] (dim % 16 == 0):
+/* FP4 block quantisation of bf16 rows x [rows][dim] (dim % 16 == 0), the cache-write side
+ * of the FP4 formats: FP4 E2M1 values with one E4M3 scale per 16 channels for the main KV
+ * ("DeepSeek, KV 캐시를 토큰당 890바이트로 줄인 V4.1-Flash 공개", section 핵심 내용; "KV cache
+ * 890 bajtów na token", section "Trzy mechanizmy zamiast jednej sztuczki") and FP4 indexer
+ * keys ("DeepSeek-V4 KV Cache 深度分析", sections 四 and 六).  The pages fix neither
+ * rounding; this library takes:
  * scale = E4M3FN(amax/6) per 16 channels (round to nearest even, saturating);
  * code  = E2M1(x / scale), or 0 for every element when the scale decodes to 0.
- * codes [rows][dim/2], scales [rows][dim/16]. */
+ * codes [rows][dim/2], scales [rows][dim/16].  x, codes and scales are device pointers
+ * (x 16-byte aligned, codes 8-byte aligned); a negative row count or a dim that is not a
+ * positive multiple of 16 returns CSAKV_ERR_INVALID. */
 csakv_status kv_quantize_fp4(const uint16_t* x, int64_t rows, int32_t dim,
                              uint8_t* codes, uint8_t* scales, void* stream);
 
-/* Mixed FP8/BF16 rows: out [rows][nope_dim + 2*(dim - nope_dim)] holds
- * E4M3FN(x[0..nope_dim)) (round to nearest even, saturating at 448) followed by the
- * bf16 bytes of x[nope_dim..dim).  nope_dim % 16 == 0, dim % 16 == 0. */
+/* Mixed FP8/BF16 rows, the 576-byte shared-KV entry of "DeepSeek-V4 KV Cache 深度分析"
+ * (section 二: the 448 no-RoPE dims are quantised to FP8 and the 64 RoPE dims kept in bf16
+ * on the way into the cache; section 六: 448 + 64 x 2 = 576 bytes, no scale bytes):
+ * out [rows][nope_dim + 2*(dim - nope_dim)] holds E4M3FN(x[0..nope_dim)) (round to nearest
+ * even, saturating at 448; the pages give no scaling, so the cast is unscaled) followed by
+ * the bf16 bytes of x[nope_dim..dim).  nope_dim % 16 == 0, dim % 16 == 0; x and out are
+ * 16-byte aligned device pointers; other shapes return CSAKV_ERR_INVALID. */
 csakv_status kv_quantize_fp8(const uint16_t* x, int64_t rows, int32_t dim,
                              int32_t nope_dim, uint8_t* out, void* stream);
 
 /* Hadamard-rotated FP4 indexer keys ("DeepSeek-V4 KV Cache 深度分析", section 四, 结构):
  * each bf16 row x [rows][128] is rotated to H x / sqrt(128), H the Sylvester Hadamard
- * matrix, computed in fp32 as the fast transform in a fixed order (for h = 1, 2, ...,
- * 64 each pair (i, i + h) with bit h of i clear becomes (y[i] + y[i+h], y[i] - y[i+h]),
- * then every element times fp32(1/sqrt(128))), and the rotated row is FP4-quantised as
- * kv_quantize_fp4 does: codes [rows][64], scales [rows][8].  The rows of a
+ * matrix: the product H x exactly (exact for rows whose nonzero magnitudes span at most 38
+ * binades), rounded once to fp32, then multiplied once by fp32(1/sqrt(128)); the rotated
+ * row is FP4-quantised as kv_quantize_fp4 does: codes [rows][64], scales [rows][8].  The rows of a
  * CSAKV_IDX_FP4_HADAMARD cache.  A decode-step write points codes / scales at the
  * destination row. */
 csakv_status idx_quantize_fp4_hadamard(const uint16_t* x, int64_t rows, uint8_t* codes,
@@ -251,8 +282,13 @@ csakv_status kv_cache_write(int32_t fmt, int32_t dim, void* codes, uint8_t* scal
                             int64_t seq_stride_rows, int64_t n_rows, int32_t batch, int32_t n,
                             const uint16_t* x, const int32_t* dst, void* stream);
 
-/* Decode rows of any KV format back to bf16 (exact for every format):
- * fmt is csakv_kv_fmt; dim 512 for FP8_MIXED (nope 448), dim % 16 == 0 otherwise. */
+/* Decode rows of any KV format back to bf16, the read side of the formats above (sections
+ * 二 and 六 of "DeepSeek-V4 KV Cache 深度分析" for the mixed row; the V4.1-Flash page, section
+ * 핵심 내용, for FP4: value = E2M1 code x E4M3 scale).  Exact for every format (an E4M3 or
+ * E2M1 x E4M3 value fits in bf16): fmt is csakv_kv_fmt; dim 512 for FP8_MIXED (nope 448),
+ * dim % 16 == 0 otherwise; codes (scales for FP4 only, else NULL) and out [rows][dim] are
+ * device pointers.  A mismatched scales pointer or shape returns CSAKV_ERR_INVALID, an
+ * FP8_MIXED dim other than 512 CSAKV_ERR_UNSUPPORTED. */
 csakv_status kv_dequantize(int32_t fmt, const void* codes, const uint8_t* scales,
                            int64_t rows, int32_t dim, uint16_t* out, void* stream);
 
@@ -275,8 +311,11 @@ typedef struct {
   int64_t swa_layer_bytes;
 } kv_cache_spec;
 
+/* `scales` holds the FP4 scale bytes of the whole cache (shared-KV, indexer and window
+ * rows of every layer; 0 for formats without scales) whether or not count_scales adds them
+ * to the row sizes: section 六 counts the FP4 indexer row as 64 bytes, which leaves them out. */
 typedef struct {
-  uint64_t csa_shared_kv, csa_indexer, hca_shared_kv, windows, swa_layers;
+  uint64_t csa_shared_kv, csa_indexer, hca_shared_kv, windows, swa_layers, scales;
   uint64_t csa_per_layer, hca_per_layer, total;
 } kv_cache_breakdown;
 

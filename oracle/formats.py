@@ -24,7 +24,10 @@ Rounding readings (the pages fix none of them)
 Parity pins (tests/test_oracle_formats.py): exhaustive round trips over all
 codes; brute-force nearest-value search over all 65,536 bf16 inputs; the FP4
 format maximum 6 x 448 = 2688 printed on the V4.1-Flash page; the per-element
-error bound |x - x_hat| <= scale.
+error bound |x - x_hat| <= scale.  The Hadamard rotation: bit-for-bit equal to the
+dense Sylvester-matrix product (scipy) rounded the same way, exact rational
+arithmetic on sample rows, a correctly rounded scale constant, norm preservation
+and the involution property.
 """
 from __future__ import annotations
 
@@ -168,27 +171,55 @@ def fp4_dequantize(codes, scales) -> np.ndarray:
 # ---------------------------------------------------------------- Hadamard-rotated FP4
 
 HADAMARD_DIM = 128
+# fp32(1 / sqrt(128)): the nearest fp32 value (pinned in tests/test_oracle_formats.py)
+HADAMARD_SCALE_F32 = np.float32(1.0 / np.sqrt(HADAMARD_DIM))
+# Largest spread, in binades, between the largest and the smallest nonzero magnitude of a
+# bf16 row for which every partial sum of H x is exact in fp64: the terms are multiples of
+# 2**(e_min - 7) and every sum stays below 128 * 2**(e_max + 1), so 38 + 7 + 1 + 7 = 53 bits.
+HADAMARD_EXACT_SPAN = 38
 
 
-def hadamard128_f32(x) -> np.ndarray:
-    """Rows x[..., 128] -> H x / sqrt(128) in fp32, H the Sylvester Hadamard matrix
-    ("DeepSeek-V4 KV Cache 深度分析", section 四, 结构: the indexer rotates its 128-wide
-    vectors with a Hadamard transform before FP4 quantisation).
+def hadamard128_exact(x) -> np.ndarray:
+    """H x for bf16 rows x[..., 128], H the 128 x 128 Sylvester Hadamard matrix, exactly.
 
-    Computed as the fast transform in a fixed order, every operation one fp32 rounding:
-    for h = 1, 2, 4, ..., 64, each pair (i, i + h) with bit h of i clear becomes
-    (x[i] + x[i+h], x[i] - x[i+h]); then every element is multiplied by fp32(1/sqrt(128)).
+    The fast Walsh-Hadamard transform in fp64: for h = 1, 2, ..., 64 every pair (i, i + h)
+    with bit h of i clear becomes (y[i] + y[i+h], y[i] - y[i+h]).  Each row must hold bf16
+    values whose nonzero magnitudes span at most HADAMARD_EXACT_SPAN binades; every sum is
+    then exact (so any evaluation order gives the same result), and a row outside that range
+    raises ValueError.
     """
-    y = np.asarray(x, dtype=np.float32).copy()
+    x = np.asarray(x, dtype=np.float64)
+    assert x.shape[-1] == HADAMARD_DIM
+    if not np.array_equal(bf16_bits_to_f64(f64_to_bf16_bits(x)), x):
+        raise ValueError("hadamard128_exact takes bf16 values")
+    a = np.abs(x)
+    _, e = np.frexp(np.where(a > 0, a, 1.0))
+    e_max = np.where(a > 0, e, np.iinfo(np.int64).min).max(axis=-1)
+    e_min = np.where(a > 0, e, np.iinfo(np.int64).max).min(axis=-1)
+    span = np.where(e_max >= e_min, e_max - e_min, 0)
+    if (span > HADAMARD_EXACT_SPAN).any():
+        raise ValueError("a row spans more binades than H x can hold exactly in fp64")
+    y = x.copy()
     lead = y.shape[:-1]
-    assert y.shape[-1] == HADAMARD_DIM
     h = 1
     while h < HADAMARD_DIM:
         v = y.reshape(*lead, HADAMARD_DIM // (2 * h), 2, h)
-        a, b = v[..., 0, :], v[..., 1, :]
-        y = np.stack([a + b, a - b], axis=-2).reshape(*lead, HADAMARD_DIM)
+        lo, hi = v[..., 0, :], v[..., 1, :]
+        y = np.stack([lo + hi, lo - hi], axis=-2).reshape(*lead, HADAMARD_DIM)
         h *= 2
-    return y * np.float32(1.0 / np.sqrt(HADAMARD_DIM))
+    return y
+
+
+def hadamard128_f32(x) -> np.ndarray:
+    """bf16 rows x[..., 128] -> the fp32 values of their rotation H x / sqrt(128)
+    ("DeepSeek-V4 KV Cache 深度分析", section 四, 结构: the indexer rotates its 128-wide vectors
+    with a Hadamard transform before FP4 quantisation).
+
+    The page names the rotation but not its arithmetic; the plain reading taken here is the
+    product H x computed exactly (hadamard128_exact), rounded once to fp32 (nearest even),
+    then one fp32 multiplication by fp32(1/sqrt(128)) (nearest even).
+    """
+    return hadamard128_exact(x).astype(np.float32) * HADAMARD_SCALE_F32
 
 
 def fp4h_quantize(x_bf16_bits) -> tuple[np.ndarray, np.ndarray]:

@@ -20,6 +20,11 @@ Pure sliding-window layers (V4-Flash's first two layers) add
 MLA (V3) and DSA (V3.2) caches are the special case ratio 1, no window: S_kv =
 (512 + 64) * 2 and, for V3.2, an extra 128 * 2 indexer bytes.
 
+FP4 rows carry one E4M3 scale byte per 16 channels besides their codes; section 六
+counts the FP4 indexer row as 64 bytes, without them.  ``s_kv_scales`` / ``s_idx_scales``
+are those scale bytes per row; ``count_scales=1`` adds them to every row (and so to
+``total``), and ``scales`` reports the cache's scale bytes either way.
+
 Parity pins (tests/test_oracle_kvbytes.py and tests/golden/kv_cache_bytes.json):
 every byte total the pages print that the closed form reproduces.
 """
@@ -29,9 +34,14 @@ from __future__ import annotations
 def kv_cache_bytes(seq_len: int, *, n_csa: int, n_hca: int, csa_ratio: int = 4,
                    hca_ratio: int = 128, window: int = 128, s_kv: int = 1024,
                    s_idx: int = 256, count_window: int = 1, n_swa: int = 0,
-                   swa_layer_bytes: int = 0) -> dict:
+                   swa_layer_bytes: int = 0, s_kv_scales: int = 0, s_idx_scales: int = 0,
+                   count_scales: int = 0) -> dict:
     n_c = seq_len // csa_ratio if n_csa else 0
     n_h = seq_len // hca_ratio if n_hca else 0
+    scales = (n_csa * (n_c * (s_kv_scales + s_idx_scales) + count_window * window * s_kv_scales)
+              + n_hca * (n_h + count_window * window) * s_kv_scales)
+    if count_scales:
+        s_kv, s_idx = s_kv + s_kv_scales, s_idx + s_idx_scales
     win = count_window * window * s_kv
     csa_shared = n_c * s_kv
     csa_index = n_c * s_idx
@@ -46,6 +56,7 @@ def kv_cache_bytes(seq_len: int, *, n_csa: int, n_hca: int, csa_ratio: int = 4,
         "hca_shared_kv": n_hca * n_h * s_kv,
         "windows": (n_csa + n_hca) * win,
         "swa_layers": n_swa * swa_layer_bytes,
+        "scales": scales,
         "total": total,
     }
 

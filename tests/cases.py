@@ -57,8 +57,19 @@ def encode_kv(bits: np.ndarray, fmt: str) -> KvCache:
 def encode_idx(bits: np.ndarray, fmt: str) -> IdxCache:
     if fmt == "bf16":
         return IdxCache(fmt, np.ascontiguousarray(bits).view(np.uint8), None, OF.bf16_bits_to_f64(bits))
-    c, s = OF.fp4_quantize(OF.bf16_bits_to_f64(bits))
+    if fmt == "fp4h":  # FP4 codes of each row's Hadamard rotation
+        c, s = OF.fp4h_quantize(bits)
+    else:
+        c, s = OF.fp4_quantize(OF.bf16_bits_to_f64(bits))
     return IdxCache(fmt, c, s, OF.fp4_dequantize(c, s))
+
+
+def indexer_query_values(q_idx_bits: np.ndarray, fmt: str) -> np.ndarray:
+    """The indexer queries as the scores use them: bf16 values, or for Hadamard-rotated FP4
+    keys the FP4-decoded rotation of each query row."""
+    if fmt == "fp4h":
+        return OF.fp4_dequantize(*OF.fp4h_quantize(q_idx_bits))
+    return OF.bf16_bits_to_f64(q_idx_bits)
 
 
 @dataclass
@@ -93,9 +104,9 @@ def make_csa_case(seed: int, B: int, n_c: int, window: int, hq: int, hi: int, to
         qi = seedgen.bf16_normal(seed, seedgen.tid(T.Q_IDX, layer), (B, hi, DI))
         w = seedgen.uniform01(seed, seedgen.tid(T.W_IDX, layer), (B, hi)).numpy()
         keys = bf16_bits(seedgen.bf16_normal(seed, seedgen.tid(T.IDX_KEYS, layer), (B, n_c, DI)))
-        qi_vals = qi.double().numpy()
-        keys, certs = tiefree.make_tie_free(keys, qi_vals, w.astype(np.float64), top_k, idx_fmt)
         case.q_idx_bits = bf16_bits(qi)
+        qi_vals = indexer_query_values(case.q_idx_bits, idx_fmt)
+        keys, certs = tiefree.make_tie_free(keys, qi_vals, w.astype(np.float64), top_k, idx_fmt)
         case.w = w.astype(np.float32)
         case.idx = encode_idx(keys, idx_fmt)
         case.certs = certs
@@ -106,7 +117,7 @@ def make_csa_case(seed: int, B: int, n_c: int, window: int, hq: int, hi: int, to
 
 def run_oracle_full(case: CsaCase):
     qv = OF.bf16_bits_to_f64(case.q_bits)
-    qiv = OF.bf16_bits_to_f64(case.q_idx_bits)
+    qiv = indexer_query_values(case.q_idx_bits, case.idx.fmt)
     outs, tks = [], []
     for b in range(case.B):
         o, sel = OD.csa_decode_one(qv[b], qiv[b], case.w[b].astype(np.float64), case.idx.values[b],

@@ -39,13 +39,21 @@ def _spec(**kw):
     return ck.KvCacheSpec(**base)
 
 
-# (library spec, oracle row bytes) pairs; row bytes follow from the format definitions.
+# (library spec, oracle row bytes) pairs; row bytes follow from the format definitions:
+# bf16 2 B per dim; mixed 448 E4M3 + 64 bf16 = 576 B; FP4 half a byte per dim in codes and
+# one scale byte per 16 dims (512 dims: 256 + 32; 128 dims: 64 + 8).
+FP4_KV = dict(s_kv=256, s_kv_scales=32)
+FP4_IDX = dict(s_idx=64, s_idx_scales=8)
 FORMATS = [
     (dict(kv_fmt=ck.KV_BF16, idx_fmt=ck.IDX_BF16), dict(s_kv=1024, s_idx=256)),
-    (dict(kv_fmt=ck.KV_FP8_MIXED, idx_fmt=ck.IDX_FP4), dict(s_kv=576, s_idx=64)),
-    (dict(kv_fmt=ck.KV_FP8_MIXED, idx_fmt=ck.IDX_FP4, count_scales=1), dict(s_kv=576, s_idx=72)),
-    (dict(kv_fmt=ck.KV_FP4, idx_fmt=ck.IDX_FP4, count_scales=1), dict(s_kv=288, s_idx=72)),
-    (dict(kv_fmt=ck.KV_FP4, idx_fmt=ck.IDX_FP4), dict(s_kv=256, s_idx=64)),
+    (dict(kv_fmt=ck.KV_FP8_MIXED, idx_fmt=ck.IDX_FP4), dict(s_kv=576, **FP4_IDX)),
+    (dict(kv_fmt=ck.KV_FP8_MIXED, idx_fmt=ck.IDX_FP4, count_scales=1),
+     dict(s_kv=576, **FP4_IDX, count_scales=1)),
+    (dict(kv_fmt=ck.KV_FP4, idx_fmt=ck.IDX_FP4, count_scales=1), dict(**FP4_KV, **FP4_IDX, count_scales=1)),
+    (dict(kv_fmt=ck.KV_FP4, idx_fmt=ck.IDX_FP4), dict(**FP4_KV, **FP4_IDX)),
+    (dict(kv_fmt=ck.KV_FP8_MIXED, idx_fmt=ck.IDX_FP4_HADAMARD), dict(s_kv=576, **FP4_IDX)),
+    (dict(kv_fmt=ck.KV_FP4, idx_fmt=ck.IDX_FP4_HADAMARD, count_scales=1),
+     dict(**FP4_KV, **FP4_IDX, count_scales=1)),
 ]
 
 
@@ -57,8 +65,21 @@ def test_kv_cache_bytes_matches_oracle(lib_kw, orc_kw, count_window, seq_len):
     ref = kvbytes.kv_cache_bytes(seq_len, n_csa=30, n_hca=31, count_window=count_window, **orc_kw)
     assert total == ref["total"]
     for f in ("csa_per_layer", "hca_per_layer", "csa_shared_kv", "csa_indexer", "hca_shared_kv",
-              "windows", "swa_layers"):
+              "windows", "swa_layers", "scales"):
         assert getattr(br, f) == ref[f], f
+
+
+def test_kv_cache_bytes_scales_are_what_counting_them_adds():
+    """The scales field is exactly the difference counting the scale bytes makes."""
+    for kw in (dict(kv_fmt=ck.KV_FP4, idx_fmt=ck.IDX_FP4), dict(kv_fmt=ck.KV_FP8_MIXED, idx_fmt=ck.IDX_FP4_HADAMARD),
+               dict(kv_fmt=ck.KV_BF16, idx_fmt=ck.IDX_BF16)):
+        for cw in (0, 1, 2):
+            t0, b0 = ck.kv_cache_bytes(_spec(count_window=cw, count_scales=0, **kw), 1 << 20)
+            t1, b1 = ck.kv_cache_bytes(_spec(count_window=cw, count_scales=1, **kw), 1 << 20)
+            assert t1 - t0 == b0.scales == b1.scales
+    # V4-Pro with FP4 indexer keys at 1M tokens: 30 CSA layers x 262,144 rows x 8 scale bytes
+    _, br = ck.kv_cache_bytes(_spec(kv_fmt=ck.KV_FP8_MIXED, idx_fmt=ck.IDX_FP4_HADAMARD), 1 << 20)
+    assert br.scales == 30 * 262144 * 8
 
 
 def test_kv_cache_bytes_presets_and_invalid():
@@ -95,10 +116,10 @@ IDX = ck.Cache(ck.IDX_BF16, 0, 1024, 1024, FAKE, None)
 @pytest.mark.parametrize("kw,status", [
     (dict(batch=0), ck.ERR_INVALID),
     (dict(top_k=0), ck.ERR_INVALID),
-    (dict(top_k=2048), ck.ERR_UNSUPPORTED),
+    (dict(top_k=2049), ck.ERR_UNSUPPORTED),
     (dict(n_q_heads=24), ck.ERR_UNSUPPORTED),
-    (dict(n_q_heads=128), ck.ERR_UNSUPPORTED),
-    (dict(n_idx_heads=65), ck.ERR_UNSUPPORTED),
+    (dict(n_q_heads=144), ck.ERR_UNSUPPORTED),
+    (dict(n_idx_heads=129), ck.ERR_UNSUPPORTED),
     (dict(n_idx_heads=0), ck.ERR_INVALID),
     (dict(mode=5), ck.ERR_INVALID),
     (dict(window=-1), ck.ERR_INVALID),
@@ -107,6 +128,16 @@ IDX = ck.Cache(ck.IDX_BF16, 0, 1024, 1024, FAKE, None)
 ])
 def test_csa_rejects_bad_params(kw, status):
     assert _call(_params(**kw), idx=IDX) == status
+
+
+@pytest.mark.parametrize("kw", [dict(n_q_heads=128), dict(n_idx_heads=128), dict(top_k=2048),
+                                dict(n_q_heads=128, n_idx_heads=65, top_k=1024)])
+def test_csa_accepts_the_largest_shapes(kw):
+    # accepted up to the workspace check: 128 heads of either kind, top_k 2048
+    assert _call(_params(**kw), idx=IDX, ws_bytes=0) == ck.ERR_WORKSPACE
+    assert ck.csa_decode_workspace_bytes(_params(**kw), 1024) > 0
+    kv = ck.Cache(ck.KV_BF16, 0, 1000, 1000, FAKE, None)
+    assert ck.hca_decode(1, 128, 0.04, kv, FAKE, FAKE, FAKE, 0, stream=0, check=False) == ck.ERR_WORKSPACE
 
 
 def test_csa_rejects_bad_pointers_and_shapes():
@@ -145,6 +176,7 @@ def test_hca_and_codecs_reject_bad_arguments():
     kv = ck.Cache(ck.KV_BF16, 0, 1000, 1000, FAKE, None)
     assert ck.hca_decode(0, 64, 0.04, kv, FAKE, FAKE, FAKE, 1 << 30, stream=0, check=False) == ck.ERR_INVALID
     assert ck.hca_decode(1, 40, 0.04, kv, FAKE, FAKE, FAKE, 1 << 30, stream=0, check=False) == ck.ERR_UNSUPPORTED
+    assert ck.hca_decode(1, 144, 0.04, kv, FAKE, FAKE, FAKE, 1 << 30, stream=0, check=False) == ck.ERR_UNSUPPORTED
     assert ck.hca_decode(1, 64, 0.04, kv, FAKE, FAKE, FAKE, 0, stream=0, check=False) == ck.ERR_WORKSPACE
     assert ck.kv_quantize_fp4(FAKE, 10, 100, FAKE, FAKE, stream=0, check=False) == ck.ERR_INVALID
     assert ck.kv_quantize_fp8(FAKE, 10, 512, 440, FAKE, stream=0, check=False) == ck.ERR_INVALID
@@ -169,7 +201,9 @@ def test_reindex_rejects_bad_arguments():
     assert _call(p, idx=IDX) == ck.ERR_INVALID
     assert call(n_pool=0) == ck.ERR_INVALID
     assert call(n_pool=4097) == ck.ERR_UNSUPPORTED
-    assert call(p=_params(mode=ck.MODE_REINDEX, top_k=2048)) == ck.ERR_UNSUPPORTED
+    assert call(p=_params(mode=ck.MODE_REINDEX, top_k=2049)) == ck.ERR_UNSUPPORTED
+    assert call(p=_params(mode=ck.MODE_REINDEX, n_idx_heads=129)) == ck.ERR_UNSUPPORTED
+    assert call(p=_params(mode=ck.MODE_REINDEX, top_k=2048, n_idx_heads=128), ws_bytes=0) == ck.ERR_WORKSPACE
     assert call(p=_params(mode=ck.MODE_REINDEX, n_idx_heads=0)) == ck.ERR_INVALID
     assert call(pool=0) == ck.ERR_INVALID                                 # null
     assert call(qi=FAKE + 2) == ck.ERR_INVALID                            # misaligned

@@ -39,6 +39,11 @@ CASES = [
     (112, 2, 1500, 0, 64, 64, 512, "bf16", "bf16"),
     # top_k 1024 (the V4-Pro configuration's value)
     (113, 1, 5000, 128, 64, 64, 1024, "fp4", "fp4"),
+    # 128 query heads (V4-Pro's query), 128 and 80 indexer heads, top_k up to 2048
+    (114, 2, 3001, 128, 128, 128, 512, "mixed", "fp4"),
+    (115, 2, 6000, 128, 128, 80, 2048, "fp4", "bf16"),
+    (116, 1, 9000, 128, 64, 64, 2048, "mixed", "fp4"),
+    (117, 2, 5000, 128, 128, 128, 1024, "bf16", "fp4h"),
 ]
 
 
@@ -110,3 +115,10 @@ def test_csa_select_topk_matches_full():
     ck.csa_select_topk(p, idx, to_dev(case.q_idx_bits.view(np.int16)), to_dev(case.w), tk, ws)
     torch.cuda.synchronize()
     assert np.array_equal(tk.cpu().numpy(), topk_full)
+    # the same through its two stages, scan then merge
+    tk2 = torch.full((case.B, case.top_k), -7, dtype=torch.int32, device="cuda")
+    ws.fill_(0x5A)
+    ck.csa_select_scan(p, idx, to_dev(case.q_idx_bits.view(np.int16)), to_dev(case.w), ws)
+    ck.csa_select_merge(p, idx, tk2, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(tk2.cpu().numpy(), topk_full)

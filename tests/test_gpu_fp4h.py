@@ -64,7 +64,8 @@ def _cache(c, n_c):
 
 
 @pytest.mark.parametrize("seed,B,n_c,hi,k", [(62, 2, 5000, 64, 512), (63, 3, 9000, 40, 100),
-                                              (64, 1, 4096 * 3 + 77, 16, 1024)])
+                                              (64, 1, 4096 * 3 + 77, 16, 1024),
+                                              (66, 2, 5000, 128, 2048)])
 def test_fp4h_select_parity(seed, B, n_c, hi, k):
     print(f"case: fp4h select seed={seed} B={B} N_c={n_c} H_I={hi} k={k}", flush=True)
     c = make_case(seed, B, n_c, hi, k)

@@ -19,6 +19,8 @@ pytestmark = pytest.mark.gpu
     (3, 128 + 777, 32, "fp4"),
     (2, 20, 64, "bf16"),
     (1, 5000, 48, "mixed"),
+    (2, 128 + 1000, 128, "mixed"),
+    (2, 128 + 700, 128, "fp4"),
 ])
 def test_hca_parity(B, rows, hq, fmt):
     print(f"case: hca B={B} rows={rows} Hq={hq} kv={fmt}", flush=True)

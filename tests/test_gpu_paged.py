@@ -1,6 +1,6 @@
 """Paged caches (a page pool plus a per-sequence block table) against the same caches
 laid out contiguously: the kernels compute on the same rows in the same order, so the
-selected indices and the outputs must agree bit for bit; one case is also checked
+selected indices and the outputs must agree bit for bit; every case is also checked
 against the oracle.  The pages are scattered over the pool in a seeded random order and
 the pool holds spare pages filled with other data."""
 import math
@@ -13,6 +13,7 @@ import compressed_sparse_kv_csa_amd as ck
 from cases import (IDX_FMTS, KV_FMTS, attention_error, make_csa_case, oracle_hca,
                    topk_sets_equal)
 import seedgen
+from oracle import decode as OD, formats as OF
 from cases import bf16_bits, encode_kv
 from gpu_helpers import to_dev, workspace
 
@@ -85,28 +86,47 @@ CASES = [
 def test_csa_paged_matches_contiguous(seed, B, n_c, kv_fmt, idx_fmt, kv_pr, idx_pr):
     print(f"case: csa paged seed={seed} B={B} n_c={n_c} {kv_fmt}/{idx_fmt} pages {kv_pr}/{idx_pr}",
           flush=True)
-    case = make_csa_case(seed, B, n_c, 128, 64, 64, 512, kv_fmt, idx_fmt,
-                         expect=(seed == CASES[0][0]))
+    case = make_csa_case(seed, B, n_c, 128, 64, 64, 512, kv_fmt, idx_fmt)
     flat = _csa(case, _kv_cache(case.kv, 0, seed), _idx_cache(case.idx, 0, seed))
     paged = _csa(case, _kv_cache(case.kv, kv_pr, seed), _idx_cache(case.idx, idx_pr, seed + 1))
     assert (flat[0] == paged[0]).all(), "selected indices differ"
     assert (flat[1] == paged[1]).all(), "outputs differ"
-    if case.expect_topk is not None:
-        assert topk_sets_equal(paged[0], case.expect_topk)
-        out = torch.from_numpy(paged[1]).view(torch.bfloat16).double().numpy()
-        err, ok = attention_error(out, case.expect_out)
-        assert ok, err
+    assert topk_sets_equal(paged[0], case.expect_topk)
+    out = torch.from_numpy(paged[1]).view(torch.bfloat16).double().numpy()
+    err, ok = attention_error(out, case.expect_out)
+    assert ok, err
 
 
 def test_csa_paged_varlen():
-    # Paged caches with per-sequence lengths: the same as contiguous ones with them.
-    case = make_csa_case(504, 3, 6000, 128, 64, 64, 512, "mixed", "fp4", expect=False)
-    lens = [6000, 2500, 100]
-    kv_len = torch.tensor([128 + n for n in lens], dtype=torch.int32, device="cuda")
+    # Paged caches with per-sequence lengths: the same as contiguous ones with them, and
+    # each sequence's selection and output those of the oracle over its own rows (each
+    # sequence's keys are tie-free over the rows it holds).
+    from test_gpu_varlen import _varlen_case
+    lens, cap, W = [6000, 2500, 100], 6000, 128
+    c = _varlen_case(504, lens, cap, W, 64, 64, 512, "mixed", "fp4")
+    kv_len = torch.tensor([W + n for n in lens], dtype=torch.int32, device="cuda")
     idx_len = torch.tensor(lens, dtype=torch.int32, device="cuda")
-    flat = _csa(case, _kv_cache(case.kv, 0, 504, kv_len), _idx_cache(case.idx, 0, 504, idx_len))
-    paged = _csa(case, _kv_cache(case.kv, 32, 504, kv_len), _idx_cache(case.idx, 64, 505, idx_len))
-    assert (flat[0] == paged[0]).all() and (flat[1] == paged[1]).all()
+    p = ck.CsaParams(3, 64, 64, 512, W, ck.MODE_FULL, 1.0 / math.sqrt(D), 0)
+    res = []
+    for kv_pr, idx_pr in ((0, 0), (32, 64)):
+        kvc = _kv_cache(c["kv"], kv_pr, 504, kv_len)
+        idxc = _idx_cache(c["idx"], idx_pr, 505, idx_len)
+        topk = torch.empty((3, 512), dtype=torch.int32, device="cuda")
+        out = torch.empty((3, 64, D), dtype=torch.bfloat16, device="cuda")
+        ck.csa_decode(p, kvc, idxc, to_dev(c["q"].view(np.int16)), to_dev(c["qi"].view(np.int16)),
+                      to_dev(c["w"]), topk, out, workspace(ck.csa_decode_workspace_bytes(p, cap)))
+        torch.cuda.synchronize()
+        res.append((topk.cpu().numpy(), out.view(torch.int16).cpu().numpy()))
+    assert (res[0][0] == res[1][0]).all() and (res[0][1] == res[1][1]).all()
+    qv, qiv = OF.bf16_bits_to_f64(c["q"]), OF.bf16_bits_to_f64(c["qi"])
+    out = torch.from_numpy(res[1][1]).view(torch.bfloat16).double().numpy()
+    for b, n in enumerate(lens):
+        sel = OD.topk_indices(OD.indexer_scores(qiv[b], c["w"][b].astype(np.float64),
+                                                c["idx"].values[b, :n]), 512)
+        assert topk_sets_equal(res[1][0][b:b + 1], sel[None]), b
+        ref = OD.attention(qv[b], OD.csa_rows(c["kv"].values[b, :W + n], W, sel), p.softmax_scale)
+        err, ok = attention_error(out[b], ref)
+        assert ok, (b, err)
 
 
 @pytest.mark.parametrize("kv_fmt,pr", [("bf16", 128), ("fp4", 16)])
@@ -131,16 +151,19 @@ def test_hca_paged(kv_fmt, pr):
 
 
 def test_reindex_paged():
-    case = make_csa_case(507, 2, 3000, 0, 16, 64, 128, "bf16", "fp4", expect=False)
-    rng = np.random.default_rng(507)
-    pool = to_dev(np.stack([rng.permutation(3000)[:1024] for _ in range(2)]).astype(np.int32))
+    # A paged key cache gives the same Reindex selection as the contiguous one, and both are
+    # the oracle's top-k of each query's pool (keys tie-free inside the pool).
+    from test_gpu_reindex import make_case
+    c = make_case(507, 2, 3000, 64, 1024, 128, "fp4", n_empty=5)
     p = ck.CsaParams(2, 0, 64, 128, 0, ck.MODE_REINDEX, 1.0, 0)
+    pool = to_dev(c["pool"].astype(np.int32))
     got = []
     for pr in (0, 32):
-        idxc = _idx_cache(case.idx, pr, 507)
+        idxc = _idx_cache(c["idx"], pr, 507)
         topk = torch.empty((2, 128), dtype=torch.int32, device="cuda")
-        ck.csa_reindex_topk(p, idxc, to_dev(case.q_idx_bits.view(np.int16)), to_dev(case.w), pool,
+        ck.csa_reindex_topk(p, idxc, to_dev(c["q_bits"].view(np.int16)), to_dev(c["w"]), pool,
                             1024, topk, workspace(ck.csa_reindex_topk_workspace_bytes(p, 1024)))
         torch.cuda.synchronize()
         got.append(topk.cpu().numpy())
     assert (got[0] == got[1]).all()
+    assert topk_sets_equal(got[1], c["expect"])

@@ -74,8 +74,10 @@ CASES = [
     (301, 2, 5000, 64, 1024, 512, "bf16", 0),
     (302, 3, 3000, 48, 777, 100, "fp4", 9),
     (303, 2, 2000, 4, 16, 20, "bf16", 3),       # fewer pool rows than k: -1 padding
-    (304, 1, 9000, 64, 4096, 1024, "fp4", 0),   # largest pool and k
+    (304, 1, 9000, 64, 4096, 1024, "fp4", 0),   # largest pool, k 1024
     (305, 2, 700, 20, 33, 1, "fp4", 1),
+    (306, 2, 9000, 128, 4096, 2048, "fp4", 5),  # 128 indexer heads, the largest k
+    (307, 1, 3000, 100, 2500, 2048, "bf16", 0),
 ]
 
 

@@ -1,6 +1,7 @@
 """Pins of the oracle's storage formats: OCP code points, exhaustive brute force, an
 independent library cast, hand-worked blocks, and the FP4 maximum the pages print."""
 import numpy as np
+import pytest
 import torch
 
 from oracle import formats as F
@@ -172,37 +173,94 @@ def test_bf16_rounding_matches_torch():
 
 # ------------------------------------------------------------------ Hadamard-rotated FP4
 
-def test_hadamard_matches_the_textbook_matrix():
-    """Integer rows: the fast transform is exact, so H x / sqrt(128) equals scipy's
-    Sylvester matrix product rounded once to fp32."""
+def _bf16_rows(rng, n, spread=1.0):
+    """n random bf16 rows of 128 values, magnitudes spread over about `spread` decades."""
+    x = rng.standard_normal((n, 128)) * 10.0 ** rng.uniform(-spread, spread, size=(n, 128))
+    return F.bf16_bits_to_f64(F.f64_to_bf16_bits(x))
+
+
+def test_hadamard_equals_the_sylvester_matrix_product_rounded_once():
+    """The rotation is scipy's dense Sylvester matrix times x (exact in fp64 for these
+    rows, whatever BLAS's summation order), rounded once to fp32, times fp32(1/sqrt(128))."""
     import scipy.linalg
     rng = np.random.default_rng(51)
-    x = rng.integers(-8, 9, size=(20, 128)).astype(np.float64)
     H = scipy.linalg.hadamard(128).astype(np.float64)
-    exact = (x @ H.T).astype(np.float32) * np.float32(1.0 / np.sqrt(128))
-    assert np.array_equal(F.hadamard128_f32(x), exact)
+    for spread in (0.0, 1.0, 2.0, 2.5):
+        x = _bf16_rows(rng, 64, spread)
+        want = (x @ H.T).astype(np.float32) * np.float32(1.0 / np.sqrt(128))
+        assert np.array_equal(F.hadamard128_f32(x).view(np.uint32), want.view(np.uint32))
+    ints = rng.integers(-8, 9, size=(20, 128)).astype(np.float64)
+    assert np.array_equal(F.hadamard128_exact(ints), ints @ H.T)
+
+
+def test_hadamard_exact_product_matches_rational_arithmetic():
+    """H x of sample rows summed in exact rationals: the fp64 transform loses nothing."""
+    from fractions import Fraction
+    import scipy.linalg
+    rng = np.random.default_rng(55)
+    H = scipy.linalg.hadamard(128)
+    x = _bf16_rows(rng, 4, 2.0)
+    x[0, :3] = [2.0 ** 20, 2.0 ** -17, -(2.0 ** -17)]   # a row near the exactness limit
+    got = F.hadamard128_exact(x)
+    for r in range(x.shape[0]):
+        fx = [Fraction(float(v)) for v in x[r]]
+        for i in (0, 1, 63, 64, 127):
+            exact = sum((fx[j] if H[i, j] > 0 else -fx[j]) for j in range(128))
+            assert Fraction(float(got[r, i])) == exact
+
+
+def test_hadamard_scale_constant_is_correctly_rounded():
+    """fp32(1/sqrt(128)) is the fp32 value nearest 1/sqrt(128): its half-ulp neighbours
+    bracket 1/sqrt(128), checked by squaring in exact rationals."""
+    from fractions import Fraction
+    f = Fraction(float(F.HADAMARD_SCALE_F32))
+    half_ulp = Fraction(1, 2 ** 28)          # values in [2^-4, 2^-3) have ulp 2^-27
+    assert (f - half_ulp) ** 2 * 128 < 1 < (f + half_ulp) ** 2 * 128
+
+
+def test_hadamard_rejects_rows_beyond_the_exact_range():
+    x = np.zeros((1, 128))
+    x[0, 0], x[0, 1] = 2.0 ** 30, 2.0 ** -10    # 40 binades apart
+    with pytest.raises(ValueError):
+        F.hadamard128_exact(x)
+    x[0, 1] = 2.0 ** -8                          # 38 binades: still exact
+    assert F.hadamard128_exact(x)[0, 0] == 2.0 ** 30 + 2.0 ** -8
+
+
+def test_hadamard_fp32_butterfly_is_not_the_rotation():
+    """An fp32 fast transform (one rounding per add) differs from the rotation on some of
+    these rows: the pins above tell the two apart."""
+    rng = np.random.default_rng(56)
+    x = _bf16_rows(rng, 200, 2.0)
+    y = x.astype(np.float32)
+    h = 1
+    while h < 128:
+        v = y.reshape(200, 128 // (2 * h), 2, h)
+        y = np.stack([v[..., 0, :] + v[..., 1, :], v[..., 0, :] - v[..., 1, :]], axis=-2).reshape(200, 128)
+        h *= 2
+    butterfly = y * np.float32(1.0 / np.sqrt(128))
+    assert (butterfly != F.hadamard128_f32(x)).any()
 
 
 def test_hadamard_is_orthonormal_and_an_involution():
     rng = np.random.default_rng(52)
-    x = rng.standard_normal((50, 128)).astype(np.float32)
+    x = _bf16_rows(rng, 50)
     y = F.hadamard128_f32(x).astype(np.float64)
-    xx = x.astype(np.float64)
-    assert np.allclose((y * y).sum(1), (xx * xx).sum(1), rtol=1e-5)          # norms kept
-    assert np.allclose(F.hadamard128_f32(y), xx, atol=1e-5)                   # R(R(x)) = x
-    # basis vectors map to the Sylvester columns / sqrt(128)
+    assert np.allclose((y * y).sum(1), (x * x).sum(1), rtol=1e-5)                      # norms kept
+    back = F.hadamard128_exact(F.bf16_bits_to_f64(F.f64_to_bf16_bits(y))) / np.sqrt(128)
+    assert np.allclose(back, x, atol=1e-2 * np.abs(x).max())                          # R(R(x)) ~ x
     e = np.zeros((1, 128)); e[0, 37] = 1.0
     col = F.hadamard128_f32(e)[0] * np.sqrt(128)
     assert set(np.round(col).tolist()) == {-1.0, 1.0} and np.round(col[0]) == 1.0
 
 
-def test_hadamard_butterfly_is_within_fp32_rounding_of_fp64():
+def test_hadamard_is_within_the_two_roundings_of_the_exact_rotation():
     import scipy.linalg
     rng = np.random.default_rng(53)
-    x = F.bf16_bits_to_f64(F.f64_to_bf16_bits(rng.standard_normal((40, 128)) * 5))
-    ref = x @ scipy.linalg.hadamard(128).T / np.sqrt(128)
-    bound = 9 * 2.0 ** -24 * (np.abs(x).sum(1, keepdims=True) / np.sqrt(128))  # 7 adds + scale
-    assert (np.abs(F.hadamard128_f32(x) - ref) <= bound).all()
+    x = _bf16_rows(rng, 40, 1.0)
+    exact = x @ scipy.linalg.hadamard(128).T / np.sqrt(128)
+    bound = 2.0 ** -23 * np.abs(exact) + 2.0 ** -149
+    assert (np.abs(F.hadamard128_f32(x) - exact) <= 1.5 * bound).all()
 
 
 def test_fp4h_is_the_fp4_codec_of_the_rotation():

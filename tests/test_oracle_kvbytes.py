@@ -86,3 +86,18 @@ def test_window_count_readings():
     base = dict(MODELS["v4_pro_bf16"])
     t = [kvbytes.kv_cache_bytes(n, **{**base, "count_window": c})["total"] for c in (0, 1, 2)]
     assert t[1] - t[0] == t[2] - t[1] == 61 * 128 * 1024
+
+
+def test_scale_bytes_reading():
+    """FP4 scale bytes (one per 16 dims) are not in the pages' 64-byte indexer row: counting
+    them adds exactly the `scales` figure, which is one byte per 16 dims of every FP4 row."""
+    n = 1 << 20
+    kw = dict(MODELS["v4_pro_mixed"], s_idx_scales=128 // 16)
+    t0 = kvbytes.kv_cache_bytes(n, **kw)
+    t1 = kvbytes.kv_cache_bytes(n, **kw, count_scales=1)
+    assert t0["total"] == 5_183_938_560                      # the 4.83 GiB figure is unchanged
+    assert t0["scales"] == t1["scales"] == 30 * (n // 4) * 8
+    assert t1["total"] - t0["total"] == t0["scales"]
+    fp4 = dict(n_csa=30, n_hca=31, s_kv=256, s_kv_scales=32, s_idx=64, s_idx_scales=8)
+    r = kvbytes.kv_cache_bytes(n, **fp4, count_window=1)
+    assert r["scales"] == 30 * ((n // 4) * 40 + 128 * 32) + 31 * ((n // 128) + 128) * 32
