@@ -15,7 +15,8 @@ __all__ = [
     "CsakvError", "KV_BF16", "KV_FP8_MIXED", "KV_FP4", "IDX_BF16", "IDX_FP4", "IDX_FP4_HADAMARD",
     "MODE_FULL",
     "MODE_REUSE", "MODE_REINDEX", "CsaParams", "Cache", "KvCacheSpec", "KvCacheBreakdown", "lib", "lib_path",
-    "cache", "csa_decode_workspace_bytes", "csa_decode", "csa_select_topk_workspace_bytes",
+    "cache", "csa_decode_workspace_bytes", "csa_decode", "csa_decode_noalloc",
+    "csa_decode_noalloc_scratch_bytes", "csa_select_topk_workspace_bytes",
     "csa_select_topk", "csa_select_scan", "csa_select_merge", "csa_reindex_topk",
     "csa_reindex_topk_workspace_bytes", "hca_decode_workspace_bytes",
     "hca_decode", "rope_output", "kv_quantize_fp4", "kv_quantize_fp8", "idx_quantize_fp4_hadamard",
@@ -30,7 +31,8 @@ MODE_FULL, MODE_REUSE, MODE_REINDEX = 0, 1, 2
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 
 EXPORTED_SYMBOLS = (
-    "csa_decode_workspace_bytes", "csa_decode", "csa_select_topk_workspace_bytes",
+    "csa_decode_workspace_bytes", "csa_decode", "csa_decode_noalloc",
+    "csa_decode_noalloc_scratch_bytes", "csa_select_topk_workspace_bytes",
     "csa_select_topk", "csa_select_scan", "csa_select_merge", "csa_reindex_topk",
     "csa_reindex_topk_workspace_bytes",
     "hca_decode_workspace_bytes", "hca_decode", "rope_output", "kv_quantize_fp4", "kv_quantize_fp8", "idx_quantize_fp4_hadamard", "kv_cache_write",
@@ -96,6 +98,10 @@ def lib() -> ctypes.CDLL:
         L.csa_decode_workspace_bytes.restype = SZ
         L.csa_decode.argtypes = [P(CsaParams), P(Cache), P(Cache), VP, VP, VP, VP, VP, VP, SZ, VP]
         L.csa_decode.restype = I32
+        L.csa_decode_noalloc.argtypes = [P(CsaParams), P(Cache), P(Cache), VP, VP, VP, VP, VP, VP]
+        L.csa_decode_noalloc.restype = I32
+        L.csa_decode_noalloc_scratch_bytes.argtypes = []
+        L.csa_decode_noalloc_scratch_bytes.restype = SZ
         L.csa_select_topk_workspace_bytes.argtypes = [P(CsaParams), I64]
         L.csa_select_topk_workspace_bytes.restype = SZ
         L.csa_select_topk.argtypes = [P(CsaParams), P(Cache), VP, VP, VP, VP, SZ, VP]
@@ -192,6 +198,21 @@ def csa_decode(params: CsaParams, kv: Cache, idx_keys: Cache | None, q, q_idx, w
     if check:
         _check(st, "csa_decode")
     return st
+
+
+def csa_decode_noalloc(params: CsaParams, kv: Cache, idx_keys: Cache | None, q, q_idx, w_idx,
+                       topk, out, stream=None, check: bool = True) -> int:
+    st = lib().csa_decode_noalloc(ctypes.byref(params), ctypes.byref(kv),
+                                  ctypes.byref(idx_keys) if idx_keys is not None else None,
+                                  _ptr(q), _ptr(q_idx), _ptr(w_idx), _ptr(topk), _ptr(out),
+                                  _stream(stream))
+    if check:
+        _check(st, "csa_decode_noalloc")
+    return st
+
+
+def csa_decode_noalloc_scratch_bytes() -> int:
+    return int(lib().csa_decode_noalloc_scratch_bytes())
 
 
 def csa_select_topk_workspace_bytes(params: CsaParams, n_compressed: int) -> int:

@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/csakv.h"
 #include "csakv_launch.h"
@@ -93,6 +94,30 @@ csakv_status check_csa_params(const csakv_csa_params* p) {
   return CSAKV_OK;
 }
 
+// ---- scratch of csa_decode_noalloc: one array in each GPU's memory, held until the process
+// ends.  Host code never uses the array's name as an address: the device address of each
+// GPU's copy comes from hipGetSymbolAddress on that GPU's first call and is kept per device.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up once per device, with it current).
+csakv_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return CSAKV_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return CSAKV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CSAKV_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return CSAKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -155,6 +180,23 @@ csakv_status csa_decode(const csakv_csa_params* p, const csakv_cache* kv,
       p->window, L.attn,
       ws + L.attn_offset, out, s));
 }
+
+csakv_status csa_decode_noalloc(const csakv_csa_params* p, const csakv_cache* kv,
+                                const csakv_cache* idx_keys, const uint16_t* q,
+                                const uint16_t* q_idx, const float* w_idx, int32_t* topk,
+                                uint16_t* out, void* stream) {
+  csakv_status st = check_csa_params(p);
+  if (st != CSAKV_OK) return st;
+  if ((st = check_cache(kv, true)) != CSAKV_OK) return st;
+  if (kv->n_rows < p->window) return CSAKV_ERR_INVALID;
+  const size_t need = csa_layout(p, kv->n_rows - p->window).total;
+  if (need > kNoAllocScratchBytes) return CSAKV_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != CSAKV_OK) return st;
+  return csa_decode(p, kv, idx_keys, q, q_idx, w_idx, topk, out, ws, kNoAllocScratchBytes, stream);
+}
+
+size_t csa_decode_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 size_t csa_select_topk_workspace_bytes(const csakv_csa_params* p, int64_t n_compressed) {
   if (!p || p->mode != CSAKV_MODE_FULL || check_select_params(p) != CSAKV_OK || n_compressed < 0)

@@ -149,6 +149,22 @@ csakv_status csa_decode(const csakv_csa_params* p, const csakv_cache* kv,
                         uint16_t* out, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): csa_decode with the library's own device
+ * scratch in place of a caller workspace, arguments otherwise as csa_decode.  The scratch is
+ * one array of csa_decode_noalloc_scratch_bytes() bytes (32 MiB) in the memory of each GPU
+ * the library runs on, held until the process ends; its address is looked up on the first
+ * call on each device.  The call allocates nothing: a request whose
+ * csa_decode_workspace_bytes exceeds the scratch returns CSAKV_ERR_WORKSPACE before any
+ * launch.  Every call on one GPU shares that GPU's scratch, which keeps the last call's
+ * contents (nothing in it needs to start at zero): calls that overlap on one GPU (other
+ * streams, other threads) race and must be serialised by the caller. */
+csakv_status csa_decode_noalloc(const csakv_csa_params* p, const csakv_cache* kv,
+                                const csakv_cache* idx_keys, const uint16_t* q,
+                                const uint16_t* q_idx, const float* w_idx, int32_t* topk,
+                                uint16_t* out, void* stream);
+size_t csa_decode_noalloc_scratch_bytes(void);
+
 /* Bytes of workspace csa_select_topk needs for these parameters and N_c rows. */
 size_t csa_select_topk_workspace_bytes(const csakv_csa_params* p, int64_t n_compressed);
 
