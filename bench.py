@@ -14,13 +14,14 @@ keys, B = 4 query tokens.  Inputs are synthetic and seed-generated, and resident
 before timing starts; R replicas of every cache (>= 1 GiB in all) rotate across steps so
 that the 256 MB Infinity Cache cannot serve a step from the previous one.
 
-Timing: every step is captured once per replica as a hipGraph (torch.cuda.CUDAGraph over
-the library's own launches); the K timed steps replay step i's graph on the current
-stream, bracketed by HIP events.  `protocol` adds the R-step graph (all replicas)
-replayed at least 50 times.  Output: one JSON line.  `roofline` reports the dominant
-kernel (the indexer scan, csa_select_scan; for HCA the whole hca_decode) timed with one
-HIP event pair per launch on the stream it runs on; `cpu_baseline` times the CPU oracle
-on a bounded sample of the same workload, on one thread and on every host core.
+Timing: the K timed steps are captured as one hipGraph (torch.cuda.CUDAGraph over the
+library's own launches; step i runs on replica i % R), replayed once untimed and once
+between HIP events on the current stream.  `protocol` adds the R-step graph (all
+replicas) replayed 50 times.  Output: one JSON line.  `roofline` reports the dominant
+kernel (the indexer scan, csa_select_scan; for HCA the whole hca_decode): K back-to-back
+launches captured and timed the same way, on the stream they run on.  `cpu_baseline`
+times the CPU oracle on a bounded sample of the same workload, on one thread and on
+every host core.
 """
 from __future__ import annotations
 
@@ -254,48 +255,38 @@ def run_gpu(w: dict, steps: int, warmup: int, replicas: int | None):
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / n
 
-    # Eager warmup (every replica once), then one graph per replica's step.
+    side = torch.cuda.Stream()
+
+    def capture(fn, n):
+        """One graph holding fn(0) .. fn(n - 1), launched on the capture stream."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for i in range(n):
+                fn(i, cur().cuda_stream)
+        return g
+
+    def graph_ms(fn, n):
+        """ms per call of fn over n calls captured in one graph: one untimed replay, then
+        one replay bracketed by HIP events on the current stream."""
+        g = capture(fn, n)
+        g.replay()
+        return timed(lambda i: g.replay(), 1) / n
+
+    # Eager warmup (every replica at least once) and an eager timing for reference.
     for i in range(max(warmup, R)):
         step(i, cur().cuda_stream)
     torch.cuda.synchronize()
     eager_ms = timed(lambda i: step(i, cur().cuda_stream), steps)
-    graphs = []
-    side = torch.cuda.Stream()
-    for r in range(R):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=side):
-            step(r, cur().cuda_stream)
-        graphs.append(g)
-    for i in range(warmup):
-        graphs[i % R].replay()
-    ms = timed(lambda i: graphs[i % R].replay(), steps)
-
+    # The K timed steps: one graph of steps 0 .. K-1 (step i on replica i % R).
+    ms = graph_ms(step, steps)
     # Protocol: one graph of all R replicas' steps, replayed M >= 50 times.
-    g_all = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_all, stream=side):
-        for r in range(R):
-            step(r, cur().cuda_stream)
+    g_all = capture(step, R)
     g_all.replay()
     M = 50
     proto_ms = timed(lambda i: g_all.replay(), M) / R
-
-    def per_launch(fn):
-        """Average HIP-event time of one fn(i) launch, each bracketed by its own events."""
-        for i in range(warmup):
-            fn(i, cur().cuda_stream)
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
-        for i in range(steps):
-            ev[i][0].record(cur())
-            fn(i, cur().cuda_stream)
-            ev[i][1].record(cur())
-        torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in ev) / steps
-
-    # The dominant kernel, and the whole indexer stage it belongs to.
-    stage_ms = per_launch(stage)
-    whole_ms = per_launch(whole) if whole is not None else None
+    # The dominant kernel (and its whole stage): K back-to-back launches in one graph.
+    stage_ms = graph_ms(stage, steps)
+    whole_ms = graph_ms(whole, steps) if whole is not None else None
     return dict(ms=ms, eager_ms=eager_ms, stage_ms=stage_ms, stage_bytes=stage_bytes,
                 stage_name=stage_name, whole_ms=whole_ms, whole_bytes=whole_bytes,
                 whole_name=whole_name, replicas=R, bytes=nbytes, proto_ms=proto_ms,
@@ -552,7 +543,7 @@ def main():
                    **({"pool": w["pool"]} if "pool" in w else {})},
         "hbm_gbps": round(step_gbps, 1),
         "algorithmic_bytes_per_step": g["bytes"]["step"],
-        "timing": {"graph_per_step": True, "eager_ms_per_step": round(g["eager_ms"], 5)},
+        "timing": {"k_steps_in_one_graph": True, "eager_ms_per_step": round(g["eager_ms"], 5)},
         "protocol": {"replicas": g["replicas"], "replays": g["proto_replays"],
                      "ms_per_step": round(g["proto_ms"], 5),
                      "query_tokens_per_s": round(B / (g["proto_ms"] * 1e-3), 1)},
