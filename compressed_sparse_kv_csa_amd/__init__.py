@@ -43,7 +43,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def lib_path() -> str:
-    return os.path.join(_HERE, "libcsakv.so")
+    """The in-tree libcsakv.so, or the library CSAKV_LIBRARY names (for example the
+    host-sanitized build that tests load)."""
+    return os.environ.get("CSAKV_LIBRARY") or os.path.join(_HERE, "libcsakv.so")
 
 
 class CsakvError(RuntimeError):

@@ -2,7 +2,13 @@
 
 Every source under ``csrc/`` is compiled by hipcc for gfx950 only, in parallel, and
 linked into one shared library with a C ABI (``include/csakv.h``).
-Usage: ``python -m compressed_sparse_kv_csa_amd.build [--resource-usage]``.
+Usage: ``python -m compressed_sparse_kv_csa_amd.build [--resource-usage] [--host-sanitize]``.
+
+``--host-sanitize`` (after a normal build) also links ``_build/libcsakv_hostsan.so``: the C
+ABI's host code (``capi.cpp``: validation, workspace layout, byte accounting) compiled with
+AddressSanitizer and UndefinedBehaviorSanitizer for the host only (``-Xarch_host``), linked
+with the unchanged GPU objects.  Load it with the sanitizer runtime preloaded
+(``host_sanitizer_runtime()``) and ``CSAKV_LIBRARY`` pointing at it.
 """
 from __future__ import annotations
 
@@ -32,6 +38,43 @@ CFLAGS = [
 FILE_FLAGS = {
     "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
+
+
+SAN_LIB = os.path.join(BUILD, "libcsakv_hostsan.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-g"]
+
+
+def host_sanitizer_runtime() -> str:
+    """Path of the AddressSanitizer runtime of the compiler that builds the library."""
+    import glob
+    llvm = os.path.join(os.path.dirname(os.path.realpath(_hipcc())), "..", "lib", "llvm")
+    hits = sorted(glob.glob(os.path.join(llvm, "lib", "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")))
+    if not hits:
+        raise RuntimeError("no clang AddressSanitizer runtime found next to hipcc")
+    return os.path.realpath(hits[-1])
+
+
+def build_host_sanitized() -> str:
+    """Link _build/libcsakv_hostsan.so: capi.cpp with host ASan + UBSan, the other objects as
+    built by build()."""
+    src = os.path.join(CSRC, "capi.cpp")
+    obj = os.path.join(BUILD, "capi.cpp.hostsan.o")
+    cmd = [_hipcc(), "-x", "hip", *CFLAGS, *SAN_FLAGS, "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on capi.cpp (host sanitizers):\n{r.stdout}{r.stderr}")
+    objs = [os.path.join(BUILD, os.path.basename(x) + ".o") for x in _sources()
+            if not x.endswith("capi.cpp")]
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-shared-libsan",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-o", SAN_LIB,
+           obj, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed (host sanitizers):\n{r.stdout}{r.stderr}")
+    return SAN_LIB
 
 
 def _hipcc() -> str:
@@ -81,3 +124,5 @@ def build(resource_usage: bool = False, verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     print(build(resource_usage="--resource-usage" in sys.argv, verbose="-v" in sys.argv))
+    if "--host-sanitize" in sys.argv:
+        print(build_host_sanitized())
