@@ -6,12 +6,12 @@
 // over the rows r of one query: CSA = the window rows plus the selected compressed
 // rows (one softmax over their union), HCA = every row of the sequence.
 //
-// Structure: one workgroup per (query, chunk of its row list, 16-head group); the head
-// groups of one chunk run on one XCD and share its L2 for the gathered rows.  A
+// Structure: one workgroup per (query, chunk of its row list, block of up to 64 heads);
+// the head blocks of one chunk run on one XCD and share its L2 for the gathered rows.  A
 // workgroup first resolves the chunk's row indices into LDS, then per 32-row step
-// gathers whole rows (coalesced 16-byte loads, two steps ahead of the one computing),
-// stores them into a row-major LDS tile (bf16 rows as they are, FP8 and FP4 rows
-// decoded exactly to fp16), and runs
+// gathers whole rows (coalesced 16-byte loads, several steps ahead of the one
+// computing), stores them into a row-major LDS tile (bf16 rows as they are, FP8 and FP4
+// rows decoded exactly to fp16) that all of its heads use, and runs, per 16-head group,
 //   S^T[32 rows x 16 heads] = K[32 x 512] . Q^T            (16x16x32 MFMA)
 //   O^T[512 x 16 heads]    += V^T[512 x 32] . P^T[32 x 16]  (16x16x32 MFMA)
 // with an online softmax in fp32 (exp2 domain) whose reference maximum moves only when
@@ -39,7 +39,6 @@ constexpr int kDim = 512;
 constexpr int kNope = 448;
 constexpr int kStepRows = 32;
 constexpr int kPitch = kDim + 16;     // fp16 elements per LDS row (32-byte pad)
-constexpr int kOutPitch = kDim + 4;   // floats per LDS row when staging the output
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyLog2 = 8.0f;  // rescale the accumulators once the maximum grows by 2^8
 // Buffer offset given to an absent row: at or past the end of every sequence the
@@ -76,17 +75,160 @@ __device__ __forceinline__ void load16(uint32_t* w, Rsrc rc, uint32_t off) {
 __device__ __forceinline__ void store16(uint16_t* dst, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   *reinterpret_cast<u32x4*>(dst) = u32x4{a, b, c, d};
 }
+// A workgroup-uniform 64-bit value, held in scalar registers (buffer resources built from
+// it then need no per-lane loop around each load).
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ uint32_t row_offset(int row, uint32_t row_bytes, uint32_t in_row) {
   return row >= 0 ? (uint32_t)row * row_bytes + in_row : kAbsentOffset;
 }
 
+constexpr int kAttnThreads = 512;                 // 8 waves
+constexpr int kAttnWaves = kAttnThreads / kWave;
+constexpr int kHeadGroups = 4;                    // 16-head groups per workgroup
+constexpr int kBlockHeads = 16 * kHeadGroups;     // heads per workgroup
+constexpr int kHalfDim = kDim / 2;                // dims of one wave's products
+constexpr int kAttnTargetBlocks = 256;            // workgroups a launch aims for (one per CU)
+constexpr int64_t kWideMinRows = 2048;            // lists at least this long run on wide workgroups
+
 template <int KVFMT>
 struct StepRaw;
 
-// bf16 rows (1 KB): load k of wave w reads step row 8w + k whole, lane l its bytes
+// bf16 rows (1 KB): load k of wave w reads step row 4w + k whole, lane l its bytes
 // 16l .. 16l + 15 (dims 8l .. 8l + 7).  The row is wave-uniform.
 template <>
 struct StepRaw<0> {
+  static constexpr uint32_t kRowBytes = kDim * 2;
+  static constexpr uint32_t kScaleRowBytes = 0;
+  static constexpr int kAhead = 2;  // steps fetched ahead of the one computing
+  static constexpr int kRowsPerWave = kStepRows / kAttnWaves;
+  uint32_t w[4 * kRowsPerWave];
+  __device__ __forceinline__ void load(Rsrc rc, Rsrc, const int* rows, int tid) {
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid & (kWave - 1);
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave; ++k) {
+      const int row = __builtin_amdgcn_readfirstlane(rows[kRowsPerWave * wave + k]);
+      load16(w + 4 * k, rc, row_offset(row, kRowBytes, 16 * lane));
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* tile, int tid) const {  // as bf16
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid & (kWave - 1);
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave; ++k)
+      store16(tile + (kRowsPerWave * wave + k) * kPitch + 8 * lane, w[4 * k], w[4 * k + 1],
+              w[4 * k + 2], w[4 * k + 3]);
+  }
+};
+
+// Mixed rows (576 B: 448 E4M3 codes, then 64 bf16).  The step's 32 x 28 E4M3 pieces
+// (16 dims each) are numbered row-major, piece p = 512k + tid: every thread takes one in
+// the first round, waves 0..5 one more in the second (896 pieces).  The 32 x 8 bf16
+// pieces (8 dims each) go to waves 4..7, one per thread.  Every thread issues the same
+// three loads (a thread without a piece reads at the absent offset, which returns zeros
+// and touches no memory), so the outstanding-load count is the same on every path; only
+// the LDS stores are skipped, on wave-uniform branches.
+template <>
+struct StepRaw<1> {
+  static constexpr uint32_t kRowBytes = kNope + 2 * (kDim - kNope);
+  static constexpr uint32_t kScaleRowBytes = 0;
+  static constexpr int kAhead = 3;
+  static constexpr int kFp8Pieces = kStepRows * (kNope / 16);  // 896
+  static constexpr int kSecondRoundWaves = (kFp8Pieces - kAttnThreads) / kWave;  // 6
+  static constexpr int kBf16Pieces = kStepRows * ((kDim - kNope) / 8);           // 256
+  static constexpr int kBf16Wave0 = kAttnWaves - kBf16Pieces / kWave;            // 4
+  uint32_t e[8];  // two E4M3 pieces
+  uint32_t r[4];  // one bf16 piece
+  __device__ __forceinline__ void load(Rsrc rc, Rsrc, const int* rows, int tid) {
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int p = kAttnThreads * k + tid;
+      const int rl = p / (kNope / 16), c = p - rl * (kNope / 16);
+      const bool has = k == 0 || wave < kSecondRoundWaves;
+      load16(e + 4 * k, rc, has ? row_offset(rows[rl], kRowBytes, 16 * c) : kAbsentOffset);
+    }
+    const int q = (tid - kBf16Wave0 * kWave) & (kBf16Pieces - 1);
+    load16(r, rc, wave >= kBf16Wave0 ? row_offset(rows[q >> 3], kRowBytes, kNope + 16 * (q & 7))
+                                     : kAbsentOffset);
+  }
+  __device__ __forceinline__ void store(uint16_t* tile, int tid) const {
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if (k == 1 && wave >= kSecondRoundWaves) break;
+      const int p = kAttnThreads * k + tid;
+      const int rl = p / (kNope / 16), c = p - rl * (kNope / 16);
+      uint16_t* dst = tile + rl * kPitch + 16 * c;
+      uint32_t h[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {  // 4 E4M3 codes -> 4 fp16 (exact)
+        h[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e[4 * k + i], 1.0f, false));
+        h[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(e[4 * k + i], 1.0f, true));
+      }
+      store16(dst, h[0], h[1], h[2], h[3]);
+      store16(dst + 8, h[4], h[5], h[6], h[7]);
+    }
+    if (wave >= kBf16Wave0) {
+      const int q = tid - kBf16Wave0 * kWave;
+      store16(tile + (q >> 3) * kPitch + kNope + 8 * (q & 7), bf16x2_to_f16x2(r[0]),
+              bf16x2_to_f16x2(r[1]), bf16x2_to_f16x2(r[2]), bf16x2_to_f16x2(r[3]));
+    }
+  }
+};
+
+// FP4 rows (256 code bytes, 32 E4M3 scale bytes, one per 16 dims): thread t takes row
+// t / 16, code bytes 16c .. 16c + 15 with c = t % 16 (dims 32c .. 32c + 31), and the two
+// scale bytes of those dims.
+template <>
+struct StepRaw<2> {
+  static constexpr uint32_t kRowBytes = kDim / 2;
+  static constexpr uint32_t kScaleRowBytes = kDim / 16;
+  static constexpr int kAhead = 4;
+  uint32_t c[4];
+  uint32_t s;  // the aligned dword holding the piece's two scale bytes
+  __device__ __forceinline__ void load(Rsrc rc, Rsrc rs, const int* rows, int tid) {
+    const int row = rows[tid >> 4];
+    load16(c, rc, row_offset(row, kRowBytes, 16 * (tid & 15)));
+    s = __builtin_amdgcn_raw_buffer_load_b32(rs, row_offset(row, kScaleRowBytes, 4 * ((tid & 15) >> 1)), 0, 0);
+  }
+  __device__ __forceinline__ void store(uint16_t* tile, int tid) const {
+    uint16_t* dst = tile + (tid >> 4) * kPitch + 32 * (tid & 15);
+    // Both scales as an fp16 pair (exact), each broadcast to both halves of a pair.
+    const uint32_t s2 = s >> (16 * (tid & 1));
+    const uint32_t sp = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s2, 1.0f, false));
+    const f16x2 s0 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(sp, sp, 0x01000100u));
+    const f16x2 s1 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(sp, sp, 0x03020302u));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // code dword j holds dims 8j .. 8j + 7 (scale j / 2)
+      const uint32_t cw = c[j];
+      const f16x2 sc = j < 2 ? s0 : s1;
+      store16(dst + 8 * j,
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 0) * sc),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1) * sc),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2) * sc),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 3) * sc));
+    }
+  }
+};
+
+// ---------------------------------------------------------------- narrow workgroups
+// Short row lists (CSA: window + top-k rows) run on narrow workgroups of 16 heads and 4
+// waves, which spread one query's list over more compute units; long lists (HCA) run on
+// wide workgroups of 64 heads and 8 waves, which decode each row once for all heads.
+constexpr int kNarrowThreads = 256;  // 4 waves
+constexpr int kNarrowDims = kDim / 4;  // output dims per wave
+constexpr int kOutPitch = kDim + 4;    // floats per LDS row when staging the output
+
+template <int KVFMT>
+struct NarrowRaw;
+
+// Narrow workgroups (256 threads).  bf16 rows (1 KB): load k of wave w reads step row 8w + k whole, lane l its bytes
+// 16l .. 16l + 15 (dims 8l .. 8l + 7).  The row is wave-uniform.
+template <>
+struct NarrowRaw<0> {
   static constexpr uint32_t kRowBytes = kDim * 2;
   static constexpr uint32_t kScaleRowBytes = 0;
   uint32_t w[32];
@@ -113,7 +255,7 @@ struct StepRaw<0> {
 // threads of the last E4M3 round that have no piece read nothing and write their 32
 // bytes into the tile's row padding (dims 512 .. 527, which no product reads).
 template <>
-struct StepRaw<1> {
+struct NarrowRaw<1> {
   static constexpr uint32_t kRowBytes = kNope + 2 * (kDim - kNope);
   static constexpr uint32_t kScaleRowBytes = 0;
   static constexpr int kFp8Pieces = kStepRows * (kNope / 16);  // 896
@@ -153,7 +295,7 @@ struct StepRaw<1> {
 // (k < 2) is row p / 16, code bytes 16c .. 16c + 15 with c = p % 16 (dims 32c .. 32c + 31),
 // and the two scale bytes of those dims.
 template <>
-struct StepRaw<2> {
+struct NarrowRaw<2> {
   static constexpr uint32_t kRowBytes = kDim / 2;
   static constexpr uint32_t kScaleRowBytes = kDim / 16;
   uint32_t c[8];
@@ -242,17 +384,14 @@ struct TileMath<0> {
   }
 };
 
-constexpr int kAttnThreads = 256;  // 4 waves
-constexpr int kDimsPerWave = kDim / 4;
-
-// Workgroup -> (query b, chunk, head group).  Workgroups are dispatched round-robin over
-// the 8 XCDs by index, so the head groups of one (query, chunk) pair are given indices
+// Workgroup -> (query b, chunk, head block).  Workgroups are dispatched round-robin over
+// the 8 XCDs by index, so the head blocks of one (query, chunk) pair are given indices
 // that are equal modulo 8: they run on one XCD and share its L2 for the gathered rows.
-__device__ __forceinline__ bool attn_block(int n_pairs, int n_groups, int n_chunks, int* b,
-                                           int* chunk, int* hg) {
+__device__ __forceinline__ bool attn_block(int n_pairs, int n_blocks, int n_chunks, int* b,
+                                           int* chunk, int* blk) {
   const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
-  *hg = k % n_groups;
-  const int pair = x + 8 * (k / n_groups);
+  *blk = k % n_blocks;
+  const int pair = x + 8 * (k / n_blocks);
   if (pair >= n_pairs) return false;
   *b = pair / n_chunks;
   *chunk = pair - *b * n_chunks;
@@ -261,10 +400,10 @@ __device__ __forceinline__ bool attn_block(int n_pairs, int n_groups, int n_chun
 
 // One workgroup: 16 heads, one chunk of a query's row list.  All 4 waves gather and
 // decode; each wave then computes the logits of all 16 heads (the K tile and the query
-// rows are shared in LDS) and the output for its own 128 dims.  NB = decode tiles (2
-// when the chunk has several steps, so that one barrier per step suffices).
-template <int KVFMT, bool CSA, int NB, bool PG>
-__global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
+// rows are shared in LDS) and the output for its own 128 dims.  One decode tile: a step
+// takes three barriers (previous tile consumed; tile complete; logit halves written).
+template <int KVFMT, bool CSA, bool PG>
+__global__ __launch_bounds__(kNarrowThreads) void attention_narrow_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t seq_stride,
     Paging pg, int64_t n_rows_max, const int32_t* __restrict__ seq_rows,
     const uint16_t* __restrict__ q,
@@ -272,7 +411,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
     const int32_t* __restrict__ topk, int top_k, int window, int64_t n_list, int rows_per_chunk,
     int n_chunks, int n_pairs, float* __restrict__ part_o, float* __restrict__ part_ml) {
   constexpr int kTileElems = kStepRows * kPitch;
-  constexpr int kTileBytes = NB * kTileElems * 2;
+  constexpr int kTileBytes = kTileElems * 2;
   constexpr int kOutBytes = 16 * kOutPitch * 4;
   constexpr int kSmem = kTileBytes > kOutBytes ? kTileBytes : kOutBytes;
   __shared__ __attribute__((aligned(16))) uint8_t s_mem[kSmem];
@@ -283,6 +422,9 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
 
   int b, chunk, hg;
   if (!attn_block(n_pairs, n_heads / 16, n_chunks, &b, &chunk, &hg)) return;
+  b = __builtin_amdgcn_readfirstlane(b);
+  chunk = __builtin_amdgcn_readfirstlane(chunk);
+  hg = __builtin_amdgcn_readfirstlane(hg);
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int g = lane >> 4;
@@ -291,13 +433,13 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
   const int64_t p_begin = (int64_t)chunk * rows_per_chunk;
   const int64_t p_end = min(p_begin + rows_per_chunk, n_list);
   const int n_steps = (int)((p_end - p_begin + kStepRows - 1) / kStepRows);
-  const int64_t n_rows = seq_len(seq_rows, b, n_rows_max);  // this sequence's rows
+  const int64_t n_rows = uniform64(seq_len(seq_rows, b, n_rows_max));  // this sequence's rows
   const int64_t n_c = n_rows - window;
 
   // Sequence row of every list position of the chunk (-1: absent or out of range), and
   // two steps of -1 past the end for the fetches that run ahead of the last step; for a
   // paged cache, the row's place in the page pool instead.
-  for (int i = threadIdx.x; i < (n_steps + 2) * kStepRows; i += kAttnThreads) {
+  for (int i = threadIdx.x; i < (n_steps + 2) * kStepRows; i += kNarrowThreads) {
     const int64_t p = p_begin + i;
     int row = -1;
     if (p < p_end) {
@@ -328,9 +470,9 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
   }
   lds_barrier();
 
-  f32x4 o[kDimsPerWave / 16];
+  f32x4 o[kNarrowDims / 16];
 #pragma unroll
-  for (int i = 0; i < kDimsPerWave / 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < kNarrowDims / 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   // m_run starts at a finite floor instead of -inf: the first step with a present row
   // always moves it (grow), so no probability is ever taken against the floor, and no
   // exponential sees -inf - -inf.  A chunk without present rows records -inf.
@@ -342,21 +484,22 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
   // steps past the end have only absent rows, which read nothing); an absent row's logit
   // is masked to -inf, so its probability is exactly 0.  With no branch around the
   // loads, both fetched steps stay in flight across the step being computed.
-  typedef StepRaw<KVFMT> Raw;
+  typedef NarrowRaw<KVFMT> Raw;
   Raw raw0, raw1;
   // Rows are addressed inside the sequence's rows, or inside the page pool when paged.
+  const int64_t seq0 = uniform64((int64_t)b * seq_stride);
   const Rsrc rc = PG ? make_rsrc(codes, kAttnMaxSeqBytes)
-                           : make_rsrc(codes + (int64_t)b * seq_stride * Raw::kRowBytes,
-                                       (uint32_t)(n_rows * Raw::kRowBytes));
+                     : make_rsrc(codes + uniform64(seq0 * Raw::kRowBytes),
+                                 __builtin_amdgcn_readfirstlane((uint32_t)(n_rows * Raw::kRowBytes)));
   const Rsrc rs = Raw::kScaleRowBytes == 0 ? rc
                   : PG ? make_rsrc(scales, kAttnMaxSeqBytes)
-                             : make_rsrc(scales + (int64_t)b * seq_stride * Raw::kScaleRowBytes,
-                                         (uint32_t)(n_rows * Raw::kScaleRowBytes));
+                       : make_rsrc(scales + uniform64(seq0 * Raw::kScaleRowBytes),
+                                   __builtin_amdgcn_readfirstlane((uint32_t)(n_rows * Raw::kScaleRowBytes)));
   auto fetch = [&](Raw& raw, int step) { raw.load(rc, rs, s_rows + step * kStepRows, threadIdx.x); };
 
   auto run_step = [&](Raw& raw, int step) {
-    uint16_t* tile = s_kv0 + (NB == 2 ? (step & 1) * kTileElems : 0);
-    if (NB == 1 && step > 0) lds_barrier();  // the previous step's tile is consumed
+    uint16_t* tile = s_kv0;
+    if (step > 0) lds_barrier();  // the previous step's tile is consumed
     // ---- decode the fetched rows into the tile (fp16, row-major)
     raw.store(tile, threadIdx.x);
     lds_barrier();
@@ -404,8 +547,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
     float mloc = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 8; ++i) mloc = fmaxf(mloc, x[i]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    mloc = wave_max_rows(mloc);
     // The reference maximum m_run moves only when a step's maximum exceeds it by more
     // than 2^kLazyLog2: the probabilities then stay below 2^kLazyLog2 (within fp16's
     // range, rounded with its full precision), and the accumulators are rescaled only on
@@ -423,25 +565,28 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
       pv[i] = __builtin_amdgcn_exp2f(x[i] - m_run);  // absent rows: exp2(-inf) = 0
       psum += pv[i];
     }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
+    psum = wave_sum_rows(psum);
     l_run = l_run * alpha + psum;
     if (__any(grow)) {
 #pragma unroll
-      for (int i = 0; i < kDimsPerWave / 16; ++i) o[i] *= alpha;
+      for (int i = 0; i < kNarrowDims / 16; ++i) o[i] *= alpha;
     }
     // ---- O^T += V^T P^T over this wave's dims (K-slots 8g+s <-> rows 4g+s, 16+4g+s-4)
 #pragma unroll
     for (int t = 0; t < TM::kPTerms; ++t) {
       const typename TM::Op pb = TM::p_term(pv, t);
 #pragma unroll
-      for (int i = 0; i < kDimsPerWave / 16; ++i)
-        o[i] = TM::mma(TM::op(v_fragment(tile, g, n, (kDimsPerWave / 16) * wave + i)), pb, o[i]);
+      for (int i = 0; i < kNarrowDims / 16; ++i)
+        o[i] = TM::mma(TM::op(v_fragment(tile, g, n, (kNarrowDims / 16) * wave + i)), pb, o[i]);
     }
   };
 
+  // The first fetches are issued in order (the scheduler may not interleave them), so
+  // that each step waits only for its own rows.
   fetch(raw0, 0);
+  __builtin_amdgcn_sched_barrier(0);
   fetch(raw1, 1);
+  __builtin_amdgcn_sched_barrier(0);
   int step = 0;
   for (; step + 1 < n_steps; step += 2) {
     run_step(raw0, step);
@@ -457,19 +602,237 @@ __global__ __launch_bounds__(kAttnThreads) void attention_chunk_kernel(
   if (wave == 0 && g == 0)
     *reinterpret_cast<f32x2*>(part_ml + (rec0 + n) * 2) = f32x2{l_run > 0.0f ? m_run : -INFINITY, l_run};
   {
-    float* orow = s_out + n * kOutPitch + kDimsPerWave * wave + 4 * g;
+    float* orow = s_out + n * kOutPitch + kNarrowDims * wave + 4 * g;
 #pragma unroll
-    for (int i = 0; i < kDimsPerWave / 16; ++i) *reinterpret_cast<f32x4*>(orow + 16 * i) = o[i];
+    for (int i = 0; i < kNarrowDims / 16; ++i) *reinterpret_cast<f32x4*>(orow + 16 * i) = o[i];
   }
   lds_barrier();
   constexpr int kVecPerHead = kDim / 4;
 #pragma unroll
-  for (int k = 0; k < 16 * kVecPerHead / kAttnThreads; ++k) {
-    const int i = threadIdx.x + k * kAttnThreads;
+  for (int k = 0; k < 16 * kVecPerHead / kNarrowThreads; ++k) {
+    const int i = threadIdx.x + k * kNarrowThreads;
     const int h = i / kVecPerHead, c4 = i - h * kVecPerHead;
     *reinterpret_cast<f32x4*>(part_o + (rec0 + h) * kDim + 4 * c4) =
         *reinterpret_cast<const f32x4*>(s_out + h * kOutPitch + 4 * c4);
   }
+}
+
+// One workgroup: up to 64 heads (four 16-head groups), one chunk of a query's row list.
+// All 8 waves gather and decode each 32-row step into one LDS tile that every head
+// uses.  Wave w serves head group w / 2 over dims 256 * (w % 2) .. +255: it computes the
+// logits' partial sums over those dims, the two halves of each logit meet in LDS, both
+// waves of the pair run the same softmax, and each accumulates the output of its own
+// dims.  Two tiles alternate, so a step takes two barriers (tile complete; logit halves
+// written).  Waves of a head group past the last head only gather and decode.
+template <int KVFMT, bool CSA, bool PG>
+__global__ __launch_bounds__(kAttnThreads) void attention_wide_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t seq_stride,
+    Paging pg, int64_t n_rows_max, const int32_t* __restrict__ seq_rows,
+    const uint16_t* __restrict__ q,
+    int n_heads, float scale_log2,
+    const int32_t* __restrict__ topk, int top_k, int window, int64_t n_list, int rows_per_chunk,
+    int n_chunks, int n_pairs, int n_blocks, float* __restrict__ part_o, float* __restrict__ part_ml) {
+  typedef StepRaw<KVFMT> Raw;
+  constexpr int kAhead = Raw::kAhead;
+  constexpr int kTileElems = kStepRows * kPitch;
+  __shared__ __attribute__((aligned(16))) uint16_t s_tile[2 * kTileElems];
+  __shared__ __attribute__((aligned(16))) int s_rows[kMaxChunkRows + kAhead * kStepRows];
+  // Partial logits: [dim half][head group][value j of the lane][lane].
+  __shared__ __attribute__((aligned(16))) float s_logit[2][kHeadGroups][8][kWave];
+
+  int b, chunk, blk;
+  if (!attn_block(n_pairs, n_blocks, n_chunks, &b, &chunk, &blk)) return;
+  b = __builtin_amdgcn_readfirstlane(b);
+  chunk = __builtin_amdgcn_readfirstlane(chunk);
+  blk = __builtin_amdgcn_readfirstlane(blk);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int hg = wave >> 1, kh = wave & 1;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int head0 = kBlockHeads * blk + 16 * hg;  // first head of the wave's group
+  const bool active = head0 < n_heads;
+
+  const int64_t p_begin = (int64_t)chunk * rows_per_chunk;
+  const int64_t p_end = min(p_begin + rows_per_chunk, n_list);
+  const int n_steps = (int)((p_end - p_begin + kStepRows - 1) / kStepRows);
+  const int64_t n_rows = uniform64(seq_len(seq_rows, b, n_rows_max));  // this sequence's rows
+  const int64_t n_c = n_rows - window;
+
+  // Sequence row of every list position of the chunk (-1: absent or out of range), and
+  // kAhead steps of -1 past the end for the fetches that run ahead of the last step; for
+  // a paged cache, the row's place in the page pool instead.
+  for (int i = threadIdx.x; i < (n_steps + kAhead) * kStepRows; i += kAttnThreads) {
+    const int64_t p = p_begin + i;
+    int row = -1;
+    if (p < p_end) {
+      if (!CSA || p < window) {
+        row = p < n_rows ? (int)p : -1;
+      } else {
+        const int32_t j = topk[(int64_t)b * top_k + (p - window)];
+        row = (j >= 0 && j < n_c) ? window + j : -1;
+      }
+    }
+    if (PG && row >= 0)
+      row = (pg.table[(int64_t)b * pg.table_stride + (row >> pg.page_shift)] << pg.page_shift) +
+            (row & ((1 << pg.page_shift) - 1));
+    s_rows[i] = row;
+  }
+  // The wave's logit B operands, kept in registers: lane (g, n) supplies head n of the
+  // group, dims 256 * kh + 32t + 8g .. +7 of K-step t, in the tile's operand type.
+  typedef TileMath<KVFMT> TM;
+  typename TM::Op qf[kHalfDim / 32];
+  if (active) {
+    const uint16_t* qr = q + ((int64_t)b * n_heads + head0 + n) * kDim + kHalfDim * kh + 8 * g;
+    u32x4 qv[kHalfDim / 32];
+#pragma unroll
+    for (int t = 0; t < kHalfDim / 32; ++t) qv[t] = *reinterpret_cast<const u32x4*>(qr + 32 * t);
+#pragma unroll
+    for (int t = 0; t < kHalfDim / 32; ++t) qf[t] = TM::q_op(qv[t]);
+  }
+  lds_barrier();
+
+  // O^T accumulators of the wave's dims: o[i] holds dims 256 * kh + 16i + 4g .. +3 of
+  // head n (lane (g, n)).
+  f32x4 o[kHalfDim / 16];
+#pragma unroll
+  for (int i = 0; i < kHalfDim / 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // m_run starts at a finite floor instead of -inf: the first step with a present row
+  // always moves it (grow), so no probability is ever taken against the floor, and no
+  // exponential sees -inf - -inf.  A chunk without present rows records -inf.
+  float m_run = -__FLT_MAX__, l_run = 0.0f;
+
+  // kAhead steps are fetched ahead (a ring of raw buffers), so a short chunk has all its
+  // steps in flight as soon as the row indices are known.  Rows are read through buffer
+  // resources over this query's sequence.  Every fetch is issued unconditionally (the
+  // steps past the end have only absent rows, which read nothing); an absent row's logit
+  // is masked to -inf, so its probability is exactly 0.
+  Raw raw[kAhead];
+  // Rows are addressed inside the sequence's rows, or inside the page pool when paged.
+  // Offsets and sizes are made explicitly uniform, so the resources sit in scalar registers.
+  const int64_t seq0 = uniform64((int64_t)b * seq_stride);
+  const Rsrc rc = PG ? make_rsrc(codes, kAttnMaxSeqBytes)
+                     : make_rsrc(codes + uniform64(seq0 * Raw::kRowBytes),
+                                 __builtin_amdgcn_readfirstlane((uint32_t)(n_rows * Raw::kRowBytes)));
+  const Rsrc rs = Raw::kScaleRowBytes == 0 ? rc
+                  : PG ? make_rsrc(scales, kAttnMaxSeqBytes)
+                       : make_rsrc(scales + uniform64(seq0 * Raw::kScaleRowBytes),
+                                   __builtin_amdgcn_readfirstlane((uint32_t)(n_rows * Raw::kScaleRowBytes)));
+  auto fetch = [&](Raw& r, int step) { r.load(rc, rs, s_rows + step * kStepRows, threadIdx.x); };
+
+  auto run_step = [&](Raw& r, int step) {
+    uint16_t* tile = s_tile + (step & 1) * kTileElems;
+    // ---- decode the fetched rows into the tile (fp16 or bf16, row-major).  The tile
+    // was last read two steps ago, before every wave passed the previous step's barriers.
+    r.store(tile, threadIdx.x);
+    lds_barrier();
+    fetch(r, step + kAhead);
+
+    // ---- logits S^T over the wave's dims: lane (g, n) gets rows 16rt + 4g + i of head n.
+    // Two accumulator chains per row tile (even and odd K-steps) halve the chain of
+    // dependent MFMAs; the halves add in the same order in both waves of the pair.
+    f32x4 part[2];
+    if (active) {
+      const uint16_t* kr = tile + n * kPitch + kHalfDim * kh + 8 * g;
+      f32x4 acc[2][2] = {};
+#pragma unroll
+      for (int t = 0; t < kHalfDim / 32; ++t)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+          acc[rt][t & 1] = TM::mma(TM::op(*reinterpret_cast<const u32x4*>(kr + 16 * rt * kPitch + 32 * t)),
+                                   qf[t], acc[rt][t & 1]);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) part[rt] = acc[rt][0] + acc[rt][1];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s_logit[kh][hg][j][lane] = part[j >> 2][j & 3];
+    }
+    lds_barrier();
+    if (!active) return;
+    // The two halves add in either order to the same fp32 logit, so both waves of the
+    // pair see identical logits and keep identical softmax states.
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = (part[j >> 2][j & 3] + s_logit[kh ^ 1][hg][j][lane]) * scale_log2;
+    // ---- online softmax (log2 domain).  Row r of the step is present when bit r of
+    // `present` is set; only a step with absent rows runs the masking (a uniform branch:
+    // the row list is full except at its end).  Exponentials are the hardware's base-2
+    // exponential: a probability below 2^-126 of the reference maximum flushes to 0, far
+    // below what its fp16 or bf16 operand resolves next to the maximum's 1.
+    const uint32_t present =
+        (uint32_t)__ballot(s_rows[step * kStepRows + (lane & (kStepRows - 1))] >= 0);
+    if (__builtin_expect(present != 0xFFFFFFFFu, 0)) {  // a step with absent rows
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!((present >> (16 * rt + 4 * g + i)) & 1u)) x[4 * rt + i] = -INFINITY;
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mloc = fmaxf(mloc, x[i]);
+    mloc = wave_max_rows(mloc);
+    // The reference maximum m_run moves only when a step's maximum exceeds it by more
+    // than 2^kLazyLog2: the probabilities then stay below 2^kLazyLog2 (within fp16's
+    // range, rounded with its full precision), and the accumulators are rescaled only on
+    // those rare steps instead of whenever a head's maximum grows.
+    const bool grow = mloc > m_run + kLazyLog2;  // m_run at its floor: any present row
+    float alpha = 1.0f;
+    if (grow) {
+      alpha = __builtin_amdgcn_exp2f(m_run - mloc);  // 0 from the floor
+      m_run = mloc;
+    }
+    float psum = 0.0f;
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pv[i] = __builtin_amdgcn_exp2f(x[i] - m_run);  // absent rows: exp2(-inf) = 0
+      psum += pv[i];
+    }
+    psum = wave_sum_rows(psum);
+    l_run = l_run * alpha + psum;
+    if (__any(grow)) {
+#pragma unroll
+      for (int i = 0; i < kHalfDim / 16; ++i) o[i] *= alpha;
+    }
+    // ---- O^T += V^T P^T over the wave's dims (K-slots 8g+s <-> rows 4g+s, 16+4g+s-4)
+#pragma unroll
+    for (int t = 0; t < TM::kPTerms; ++t) {
+      const typename TM::Op pb = TM::p_term(pv, t);
+#pragma unroll
+      for (int i = 0; i < kHalfDim / 16; ++i)
+        o[i] = TM::mma(TM::op(v_fragment(tile, g, n, (kHalfDim / 16) * kh + i)), pb, o[i]);
+    }
+  };
+
+  // The first fetches are issued in ring order (the scheduler may not interleave them),
+  // so that, as in the loop, the oldest outstanding loads are the next step's: each step
+  // then waits only for its own rows.
+#pragma unroll
+  for (int k = 0; k < kAhead; ++k) {
+    fetch(raw[k], k);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Whole rounds of kAhead steps run without a branch between them, so the loop carries
+  // the same outstanding loads around every iteration and each step waits only for its
+  // own; the last, partial round follows.
+  int step = 0;
+  for (; step + kAhead <= n_steps; step += kAhead) {
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k) run_step(raw[k], step + k);
+  }
+#pragma unroll
+  for (int k = 0; k < kAhead - 1; ++k)
+    if (step + k < n_steps) run_step(raw[k], step + k);
+  if (!active) return;
+
+  // ---- partial records: (max, sum) per head, and the wave's 256 dims of each head's
+  // unnormalised O (four lanes write 64 contiguous bytes of one head's record).
+  const int64_t rec = ((int64_t)b * n_chunks + chunk) * n_heads + head0 + n;
+  if (kh == 0 && g == 0)
+    *reinterpret_cast<f32x2*>(part_ml + rec * 2) = f32x2{l_run > 0.0f ? m_run : -INFINITY, l_run};
+  float* orow = part_o + rec * kDim + kHalfDim * kh + 4 * g;
+#pragma unroll
+  for (int i = 0; i < kHalfDim / 16; ++i) *reinterpret_cast<f32x4*>(orow + 16 * i) = o[i];
 }
 
 // One workgroup per (query, head): merges the chunks' (max, sum, O) records.  Up to
@@ -530,9 +893,17 @@ __global__ __launch_bounds__(kCombineThreads) void attention_combine_kernel(
   *reinterpret_cast<u32x2*>(out + (int64_t)bh * kDim + d0) = u32x2{lo, hi};
 }
 
+// Heads one workgroup serves: 64 (wide) or 16 (narrow).
+int attention_wg_heads(const AttnPlan& plan) { return plan.wide ? kBlockHeads : 16; }
+
+int attention_head_blocks(int n_heads, const AttnPlan& plan) {
+  const int h = attention_wg_heads(plan);
+  return (n_heads + h - 1) / h;
+}
+
 int attention_blocks(int batch, int n_heads, const AttnPlan& plan) {
   const int n_pairs = batch * plan.n_chunks;
-  return 8 * (n_heads / 16) * ((n_pairs + 7) / 8);
+  return 8 * attention_head_blocks(n_heads, plan) * ((n_pairs + 7) / 8);
 }
 
 template <int KVFMT, bool CSA>
@@ -543,19 +914,27 @@ void launch_chunks(hipStream_t stream, const uint8_t* codes, const uint8_t* scal
                    const AttnPlan& plan, float* part_o, float* part_ml) {
   const dim3 grid(attention_blocks(batch, n_heads, plan));
   const int n_pairs = batch * plan.n_chunks;
-#define CSAKV_CHUNK(NB, PG)                                                                     \
-  hipLaunchKernelGGL((attention_chunk_kernel<KVFMT, CSA, NB, PG>), grid, dim3(kAttnThreads), 0,  \
+  // A paged cache has its own kernels so that the contiguous ones carry no trace of the
+  // page lookup.
+#define CSAKV_WIDE(PG)                                                                          \
+  hipLaunchKernelGGL((attention_wide_kernel<KVFMT, CSA, PG>), grid, dim3(kAttnThreads), 0,        \
+                     stream, codes, scales, seq_stride, pg, n_rows, seq_rows, q, n_heads,         \
+                     scale_log2, topk, top_k, window, plan.n_list, plan.rows_per_chunk,           \
+                     plan.n_chunks, n_pairs, attention_head_blocks(n_heads, plan), part_o, part_ml)
+#define CSAKV_NARROW(PG)                                                                        \
+  hipLaunchKernelGGL((attention_narrow_kernel<KVFMT, CSA, PG>), grid, dim3(kNarrowThreads), 0,    \
                      stream, codes, scales, seq_stride, pg, n_rows, seq_rows, q, n_heads,         \
                      scale_log2, topk, top_k, window, plan.n_list, plan.rows_per_chunk,           \
                      plan.n_chunks, n_pairs, part_o, part_ml)
-  // One decode tile (42 KB of LDS); a second tile's one barrier per step saved less than
-  // the lower occupancy cost.  A paged cache has its own kernel so that the contiguous
-  // one carries no trace of the page lookup.
-  if (pg.table)
-    CSAKV_CHUNK(1, true);
-  else
-    CSAKV_CHUNK(1, false);
-#undef CSAKV_CHUNK
+  if (plan.wide) {
+    if (pg.table) CSAKV_WIDE(true);
+    else CSAKV_WIDE(false);
+  } else {
+    if (pg.table) CSAKV_NARROW(true);
+    else CSAKV_NARROW(false);
+  }
+#undef CSAKV_WIDE
+#undef CSAKV_NARROW
 }
 
 // Output RoPE with position -i on the 64 RoPE dims of every output row, in place: one
@@ -600,10 +979,11 @@ hipError_t launch_rope_output(uint16_t* out, int batch, int n_heads, const int64
 AttnPlan plan_attention(int batch, int64_t n_list, bool csa, int n_heads) {
   AttnPlan p{};
   p.n_list = n_list;
-  // Chunks of whole 32-row steps; about 256 workgroups in all, each one
-  // (query, chunk, 16-head group), never more than kMaxChunks chunks per query.
-  const int64_t groups = n_heads / 16 > 0 ? n_heads / 16 : 1;
-  const int64_t want = (256 + batch * groups - 1) / (batch * groups);
+  p.wide = n_list >= kWideMinRows;
+  // Chunks of whole 32-row steps; about one workgroup per compute unit in all, each one
+  // (query, chunk, head block), never more than kMaxChunks chunks per query.
+  const int64_t blocks = std::max(1, attention_head_blocks(n_heads, p));
+  const int64_t want = (kAttnTargetBlocks + batch * blocks - 1) / (batch * blocks);
   int64_t rpc = (n_list + want - 1) / want;
   const int64_t floor_rows = (n_list + kMaxChunks - 1) / kMaxChunks;
   if (rpc < floor_rows) rpc = floor_rows;

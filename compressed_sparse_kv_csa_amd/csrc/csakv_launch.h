@@ -85,6 +85,7 @@ struct AttnPlan {
   int64_t n_list;      // row positions per query (CSA: window + top_k; HCA: rows)
   int rows_per_chunk;  // multiple of 32
   int n_chunks;        // chunks per query
+  bool wide;           // 64-head workgroups (long lists) instead of 16-head ones
 };
 
 constexpr int kMaxChunkRows = 1024;  // rows one attention workgroup walks

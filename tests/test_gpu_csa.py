@@ -44,6 +44,8 @@ CASES = [
     (115, 2, 6000, 128, 128, 80, 2048, "fp4", "bf16"),
     (116, 1, 9000, 128, 64, 64, 2048, "mixed", "fp4"),
     (117, 2, 5000, 128, 128, 128, 1024, "bf16", "fp4h"),
+    # lists of 2048 rows and more run on the 64-head workgroups: bf16 rows there too
+    (118, 2, 5000, 128, 64, 64, 2048, "bf16", "bf16"),
 ]
 
 

@@ -74,19 +74,21 @@ def _csa(case, kvc, idxc):
     return topk.cpu().numpy(), out.view(torch.int16).cpu().numpy()
 
 
-# (seed, B, N_c, kv_fmt, idx_fmt, kv page rows, key page rows)
+# (seed, B, N_c, kv_fmt, idx_fmt, kv page rows, key page rows, top_k)
 CASES = [
-    (501, 3, 5000, "mixed", "fp4", 64, 16),
-    (502, 2, 9000, "bf16", "bf16", 256, 128),
-    (503, 2, 3001, "fp4", "fp4h", 16, 4096),
+    (501, 3, 5000, "mixed", "fp4", 64, 16, 512),
+    (502, 2, 9000, "bf16", "bf16", 256, 128, 512),
+    (503, 2, 3001, "fp4", "fp4h", 16, 4096, 512),
+    # a 2176-row list: the 64-head workgroups' paged kernel
+    (508, 2, 5000, "mixed", "fp4", 32, 64, 2048),
 ]
 
 
-@pytest.mark.parametrize("seed,B,n_c,kv_fmt,idx_fmt,kv_pr,idx_pr", CASES)
-def test_csa_paged_matches_contiguous(seed, B, n_c, kv_fmt, idx_fmt, kv_pr, idx_pr):
-    print(f"case: csa paged seed={seed} B={B} n_c={n_c} {kv_fmt}/{idx_fmt} pages {kv_pr}/{idx_pr}",
-          flush=True)
-    case = make_csa_case(seed, B, n_c, 128, 64, 64, 512, kv_fmt, idx_fmt)
+@pytest.mark.parametrize("seed,B,n_c,kv_fmt,idx_fmt,kv_pr,idx_pr,top_k", CASES)
+def test_csa_paged_matches_contiguous(seed, B, n_c, kv_fmt, idx_fmt, kv_pr, idx_pr, top_k):
+    print(f"case: csa paged seed={seed} B={B} n_c={n_c} {kv_fmt}/{idx_fmt} pages {kv_pr}/{idx_pr}"
+          f" k={top_k}", flush=True)
+    case = make_csa_case(seed, B, n_c, 128, 64, 64, top_k, kv_fmt, idx_fmt)
     flat = _csa(case, _kv_cache(case.kv, 0, seed), _idx_cache(case.idx, 0, seed))
     paged = _csa(case, _kv_cache(case.kv, kv_pr, seed), _idx_cache(case.idx, idx_pr, seed + 1))
     assert (flat[0] == paged[0]).all(), "selected indices differ"
@@ -129,7 +131,7 @@ def test_csa_paged_varlen():
         assert ok, (b, err)
 
 
-@pytest.mark.parametrize("kv_fmt,pr", [("bf16", 128), ("fp4", 16)])
+@pytest.mark.parametrize("kv_fmt,pr", [("bf16", 128), ("mixed", 32), ("fp4", 16)])
 def test_hca_paged(kv_fmt, pr):
     B, rows, hq = 3, 2500, 64
     T = seedgen.TID

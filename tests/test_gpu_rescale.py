@@ -19,8 +19,9 @@ CSA (REUSE mode, whose row order the caller controls) and HCA:
 
 The row values stay below 22.5 in magnitude, the bound of the other workloads' rows.
 The batch sizes are chosen so that each query's rows span several 32-row steps in one
-workgroup (B = 16 for the 640-row CSA lists, B = 8 for 960 HCA rows), with spikes inside
-those runs of steps.  The test first
+workgroup (B = 16 for the 640-row CSA lists, B = 4 for the 2240-row ones, B = 8 for 960
+and 2240 HCA rows), with spikes inside those runs of steps; the longer lists run on the
+64-head workgroups, the shorter ones on the 16-head ones.  The test first
 checks those properties on the oracle's logits, then compares the GPU output with the
 oracle (max-abs 1e-2; bf16's half-ulp added where |o| >= 4).
 """
@@ -80,10 +81,15 @@ def _assert_branch_taken(qv, rows, scale):
     return grows
 
 
+# (B, W, N_c, k): a 640-row list (16-head workgroups) and a 2240-row one (64-head ones)
+LISTS = [(16, 128, 1500, 512), (4, 192, 3000, 2048)]
+
+
+@pytest.mark.parametrize("B,W,n_c,k", LISTS)
 @pytest.mark.parametrize("kv_fmt", ["bf16", "mixed", "fp4"])
-def test_csa_reuse_rescale(kv_fmt):
-    seed, B, W, n_c, hq, k = 801, 16, 128, 1500, 64, 512
-    print(f"case: csa REUSE rescale kv={kv_fmt} B={B} Nc={n_c} Hq={hq} k={k}", flush=True)
+def test_csa_reuse_rescale(kv_fmt, B, W, n_c, k):
+    seed, hq = 801, 64
+    print(f"case: csa REUSE rescale kv={kv_fmt} B={B} W={W} Nc={n_c} Hq={hq} k={k}", flush=True)
     n_list = W + k
     # each query's selection: k distinct compressed rows in a seeded order
     sel = np.stack([seedgen.distinct_indices(seed, seedgen.tid(T.POOL, b), n_c, k) for b in range(B)])
@@ -114,9 +120,10 @@ def test_csa_reuse_rescale(kv_fmt):
     assert ok, err
 
 
+@pytest.mark.parametrize("rows", [960, 2240])
 @pytest.mark.parametrize("kv_fmt", ["bf16", "mixed", "fp4"])
-def test_hca_rescale(kv_fmt):
-    seed, B, rows, hq = 802, 8, 960, 64
+def test_hca_rescale(kv_fmt, rows):
+    seed, B, hq = 802, 8, 64
     print(f"case: hca rescale kv={kv_fmt} B={B} rows={rows} Hq={hq}", flush=True)
     q_bits = _queries(seed, B, hq)
     level = np.broadcast_to(_ladder(rows), (B, rows))
