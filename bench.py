@@ -63,7 +63,7 @@ WORKLOADS = {
 # kernel sources hash to the recorded value.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_stage_csa_mixed_1m_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "compressed_sparse_kv_csa_amd", "csrc", f)
-                  for f in ("indexer.hip", "csakv_device.h", "csakv_launch.h")]
+                  for f in ("indexer.hip", "topk_select.h", "csakv_device.h", "csakv_launch.h")]
 
 KV_ROW_BYTES = {"bf16": 1024, "mixed": 576, "fp4": 256 + 32}
 IDX_ROW_BYTES = {"bf16": 256, "fp4": 64 + 8, "fp4h": 64 + 8}

@@ -402,29 +402,34 @@ __device__ __forceinline__ bool attn_block(int n_pairs, int n_blocks, int n_chun
 // decode; each wave then computes the logits of all 16 heads (the K tile and the query
 // rows are shared in LDS) and the output for its own 128 dims.  One decode tile: a step
 // takes three barriers (previous tile consumed; tile complete; logit halves written).
+constexpr int kNarrowTileBytes = kStepRows * kPitch * 2;
+constexpr int kNarrowOutBytes = 16 * kOutPitch * 4;
+constexpr int kNarrowMemBytes = kNarrowTileBytes > kNarrowOutBytes ? kNarrowTileBytes : kNarrowOutBytes;
+
+// LDS of a narrow workgroup: the decode tile (later the output staging area), the
+// chunk's row indices, and the two halves of each step's logits.
+struct NarrowSmem {
+  __attribute__((aligned(16))) uint8_t mem[kNarrowMemBytes];
+  __attribute__((aligned(16))) int rows[kMaxChunkRows + 2 * kStepRows];
+  __attribute__((aligned(16))) float logit[2][kStepRows][16];  // per K half
+};
+
+// One chunk of query b's row list for head group hg.  For CSA, sel points at the query's
+// selected compressed-row indices (in the workspace, or in LDS when the selection was
+// just computed by the same workgroup).
 template <int KVFMT, bool CSA, bool PG>
-__global__ __launch_bounds__(kNarrowThreads) void attention_narrow_kernel(
-    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t seq_stride,
-    Paging pg, int64_t n_rows_max, const int32_t* __restrict__ seq_rows,
-    const uint16_t* __restrict__ q,
-    int n_heads, float scale_log2,
-    const int32_t* __restrict__ topk, int top_k, int window, int64_t n_list, int rows_per_chunk,
-    int n_chunks, int n_pairs, float* __restrict__ part_o, float* __restrict__ part_ml) {
+__device__ __forceinline__ void narrow_chunk(
+    NarrowSmem& sm, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    int64_t seq_stride, const Paging& pg, int64_t n_rows_max, const int32_t* __restrict__ seq_rows,
+    const uint16_t* __restrict__ q, int n_heads, float scale_log2, const int32_t* sel, int window,
+    int64_t n_list, int rows_per_chunk, int n_chunks, float* __restrict__ part_o,
+    float* __restrict__ part_ml, int b, int chunk, int hg) {
   constexpr int kTileElems = kStepRows * kPitch;
-  constexpr int kTileBytes = kTileElems * 2;
-  constexpr int kOutBytes = 16 * kOutPitch * 4;
-  constexpr int kSmem = kTileBytes > kOutBytes ? kTileBytes : kOutBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t s_mem[kSmem];
-  __shared__ __attribute__((aligned(16))) int s_rows[kMaxChunkRows + 2 * kStepRows];
-  __shared__ __attribute__((aligned(16))) float s_logit[2][kStepRows][16];  // per K half
+  uint8_t* const s_mem = sm.mem;
+  int* const s_rows = sm.rows;
+  auto& s_logit = sm.logit;
   uint16_t* const s_kv0 = reinterpret_cast<uint16_t*>(s_mem);
   float* const s_out = reinterpret_cast<float*>(s_mem);
-
-  int b, chunk, hg;
-  if (!attn_block(n_pairs, n_heads / 16, n_chunks, &b, &chunk, &hg)) return;
-  b = __builtin_amdgcn_readfirstlane(b);
-  chunk = __builtin_amdgcn_readfirstlane(chunk);
-  hg = __builtin_amdgcn_readfirstlane(hg);
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int g = lane >> 4;
@@ -446,7 +451,7 @@ __global__ __launch_bounds__(kNarrowThreads) void attention_narrow_kernel(
       if (!CSA || p < window) {
         row = p < n_rows ? (int)p : -1;
       } else {
-        const int32_t j = topk[(int64_t)b * top_k + (p - window)];
+        const int32_t j = sel[p - window];
         row = (j >= 0 && j < n_c) ? window + j : -1;
       }
     }
@@ -615,6 +620,25 @@ __global__ __launch_bounds__(kNarrowThreads) void attention_narrow_kernel(
     *reinterpret_cast<f32x4*>(part_o + (rec0 + h) * kDim + 4 * c4) =
         *reinterpret_cast<const f32x4*>(s_out + h * kOutPitch + 4 * c4);
   }
+}
+
+template <int KVFMT, bool CSA, bool PG>
+__global__ __launch_bounds__(kNarrowThreads) void attention_narrow_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t seq_stride,
+    Paging pg, int64_t n_rows_max, const int32_t* __restrict__ seq_rows,
+    const uint16_t* __restrict__ q,
+    int n_heads, float scale_log2,
+    const int32_t* __restrict__ topk, int top_k, int window, int64_t n_list, int rows_per_chunk,
+    int n_chunks, int n_pairs, float* __restrict__ part_o, float* __restrict__ part_ml) {
+  __shared__ NarrowSmem sm;
+  int b, chunk, hg;
+  if (!attn_block(n_pairs, n_heads / 16, n_chunks, &b, &chunk, &hg)) return;
+  b = __builtin_amdgcn_readfirstlane(b);
+  chunk = __builtin_amdgcn_readfirstlane(chunk);
+  hg = __builtin_amdgcn_readfirstlane(hg);
+  narrow_chunk<KVFMT, CSA, PG>(sm, codes, scales, seq_stride, pg, n_rows_max, seq_rows, q, n_heads,
+                               scale_log2, CSA ? topk + (int64_t)b * top_k : nullptr, window,
+                               n_list, rows_per_chunk, n_chunks, part_o, part_ml, b, chunk, hg);
 }
 
 // One workgroup: up to 64 heads (four 16-head groups), one chunk of a query's row list.

@@ -45,6 +45,7 @@ constexpr int kSliceRows = 4096;
 constexpr int kMaxTopK = 2048;
 constexpr int kMaxHeads = 128;  // query heads (a multiple of 16) and indexer heads
 constexpr int kMergeCap = 8192;
+constexpr int kMergeFirstSlots = 4096;  // candidate slots a merge reads with the slice counts
 constexpr int kMaxMergeSlices = 512;
 
 // CSA2 reindex: pool slots per query, and the largest indexer-key byte count of one
