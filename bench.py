@@ -58,10 +58,10 @@ WORKLOADS = {
     "hca_bf16_1m": dict(kind="hca", B=16, n_c=8192, window=128, hq=64, hi=0, top_k=0, kv="bf16",
                         idx=None, seed=3, context=1 << 20, layers=1),
 }
-# HBM traffic of the indexer stage, from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs scaled
-# by what the same counters read for a copy kernel of known size.  Valid only while the
-# kernel sources hash to the recorded value.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_stage_csa_mixed_1m_traffic.txt")
+# HBM traffic of the dominant kernel (the indexer scan) at the default workload, from
+# rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs scaled as the summary derives.  Valid only
+# while the kernel sources hash to the recorded value.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_scan_csa_mixed_1m_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "compressed_sparse_kv_csa_amd", "csrc", f)
                   for f in ("indexer.hip", "topk_select.h", "csakv_device.h", "csakv_launch.h")]
 
