@@ -21,6 +21,9 @@ pytestmark = pytest.mark.gpu
     (1, 5000, 48, "mixed"),
     (2, 128 + 1000, 128, "mixed"),
     (2, 128 + 700, 128, "fp4"),
+    # 2048 rows and more: 64-head workgroups, two blocks at 128 heads, one group of four at 16
+    (1, 2500, 128, "fp4"),
+    (2, 2100, 16, "bf16"),
 ])
 def test_hca_parity(B, rows, hq, fmt):
     print(f"case: hca B={B} rows={rows} Hq={hq} kv={fmt}", flush=True)
