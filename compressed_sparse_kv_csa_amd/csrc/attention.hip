@@ -86,8 +86,8 @@ __device__ __forceinline__ uint32_t row_offset(int row, uint32_t row_bytes, uint
   return row >= 0 ? (uint32_t)row * row_bytes + in_row : kAbsentOffset;
 }
 
-constexpr int kAttnThreads = 512;                 // 8 waves
-constexpr int kAttnWaves = kAttnThreads / kWave;
+constexpr int kWideThreads = 512;                 // 8 waves
+constexpr int kWideWaves = kWideThreads / kWave;
 constexpr int kHeadGroups = 4;                    // 16-head groups per workgroup
 constexpr int kBlockHeads = 16 * kHeadGroups;     // heads per workgroup
 constexpr int kHalfDim = kDim / 2;                // dims of one wave's products
@@ -104,7 +104,7 @@ struct StepRaw<0> {
   static constexpr uint32_t kRowBytes = kDim * 2;
   static constexpr uint32_t kScaleRowBytes = 0;
   static constexpr int kAhead = 2;  // steps fetched ahead of the one computing
-  static constexpr int kRowsPerWave = kStepRows / kAttnWaves;
+  static constexpr int kRowsPerWave = kStepRows / kWideWaves;
   uint32_t w[4 * kRowsPerWave];
   __device__ __forceinline__ void load(Rsrc rc, Rsrc, const int* rows, int tid) {
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid & (kWave - 1);
@@ -136,16 +136,16 @@ struct StepRaw<1> {
   static constexpr uint32_t kScaleRowBytes = 0;
   static constexpr int kAhead = 3;
   static constexpr int kFp8Pieces = kStepRows * (kNope / 16);  // 896
-  static constexpr int kSecondRoundWaves = (kFp8Pieces - kAttnThreads) / kWave;  // 6
+  static constexpr int kSecondRoundWaves = (kFp8Pieces - kWideThreads) / kWave;  // 6
   static constexpr int kBf16Pieces = kStepRows * ((kDim - kNope) / 8);           // 256
-  static constexpr int kBf16Wave0 = kAttnWaves - kBf16Pieces / kWave;            // 4
+  static constexpr int kBf16Wave0 = kWideWaves - kBf16Pieces / kWave;            // 4
   uint32_t e[8];  // two E4M3 pieces
   uint32_t r[4];  // one bf16 piece
   __device__ __forceinline__ void load(Rsrc rc, Rsrc, const int* rows, int tid) {
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int p = kAttnThreads * k + tid;
+      const int p = kWideThreads * k + tid;
       const int rl = p / (kNope / 16), c = p - rl * (kNope / 16);
       const bool has = k == 0 || wave < kSecondRoundWaves;
       load16(e + 4 * k, rc, has ? row_offset(rows[rl], kRowBytes, 16 * c) : kAbsentOffset);
@@ -159,7 +159,7 @@ struct StepRaw<1> {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       if (k == 1 && wave >= kSecondRoundWaves) break;
-      const int p = kAttnThreads * k + tid;
+      const int p = kWideThreads * k + tid;
       const int rl = p / (kNope / 16), c = p - rl * (kNope / 16);
       uint16_t* dst = tile + rl * kPitch + 16 * c;
       uint32_t h[8];
@@ -649,7 +649,7 @@ __global__ __launch_bounds__(kNarrowThreads) void attention_narrow_kernel(
 // dims.  Two tiles alternate, so a step takes two barriers (tile complete; logit halves
 // written).  Waves of a head group past the last head only gather and decode.
 template <int KVFMT, bool CSA, bool PG>
-__global__ __launch_bounds__(kAttnThreads) void attention_wide_kernel(
+__global__ __launch_bounds__(kWideThreads) void attention_wide_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t seq_stride,
     Paging pg, int64_t n_rows_max, const int32_t* __restrict__ seq_rows,
     const uint16_t* __restrict__ q,
@@ -686,7 +686,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_wide_kernel(
   // Sequence row of every list position of the chunk (-1: absent or out of range), and
   // kAhead steps of -1 past the end for the fetches that run ahead of the last step; for
   // a paged cache, the row's place in the page pool instead.
-  for (int i = threadIdx.x; i < (n_steps + kAhead) * kStepRows; i += kAttnThreads) {
+  for (int i = threadIdx.x; i < (n_steps + kAhead) * kStepRows; i += kWideThreads) {
     const int64_t p = p_begin + i;
     int row = -1;
     if (p < p_end) {
@@ -941,7 +941,7 @@ void launch_chunks(hipStream_t stream, const uint8_t* codes, const uint8_t* scal
   // A paged cache has its own kernels so that the contiguous ones carry no trace of the
   // page lookup.
 #define CSAKV_WIDE(PG)                                                                          \
-  hipLaunchKernelGGL((attention_wide_kernel<KVFMT, CSA, PG>), grid, dim3(kAttnThreads), 0,        \
+  hipLaunchKernelGGL((attention_wide_kernel<KVFMT, CSA, PG>), grid, dim3(kWideThreads), 0,        \
                      stream, codes, scales, seq_stride, pg, n_rows, seq_rows, q, n_heads,         \
                      scale_log2, topk, top_k, window, plan.n_list, plan.rows_per_chunk,           \
                      plan.n_chunks, n_pairs, attention_head_blocks(n_heads, plan), part_o, part_ml)
