@@ -631,6 +631,9 @@ __global__ __launch_bounds__(kNarrowThreads) void attention_narrow_kernel(
     const int32_t* __restrict__ topk, int top_k, int window, int64_t n_list, int rows_per_chunk,
     int n_chunks, int n_pairs, float* __restrict__ part_o, float* __restrict__ part_ml) {
   __shared__ NarrowSmem sm;
+  args_in_sgprs(codes, scales, seq_stride, pg.table, pg.page_shift, pg.table_stride, n_rows_max,
+                seq_rows, q, n_heads, scale_log2, topk, top_k, window, n_list, rows_per_chunk,
+                n_chunks, n_pairs, part_o, part_ml);
   int b, chunk, hg;
   if (!attn_block(n_pairs, n_heads / 16, n_chunks, &b, &chunk, &hg)) return;
   b = __builtin_amdgcn_readfirstlane(b);
@@ -664,6 +667,9 @@ __global__ __launch_bounds__(kWideThreads) void attention_wide_kernel(
   // Partial logits: [dim half][head group][value j of the lane][lane].
   __shared__ __attribute__((aligned(16))) float s_logit[2][kHeadGroups][8][kWave];
 
+  args_in_sgprs(codes, scales, seq_stride, pg.table, pg.page_shift, pg.table_stride, n_rows_max,
+                seq_rows, q, n_heads, scale_log2, topk, top_k, window, n_list, rows_per_chunk,
+                n_chunks, n_pairs, n_blocks, part_o, part_ml);
   int b, chunk, blk;
   if (!attn_block(n_pairs, n_blocks, n_chunks, &b, &chunk, &blk)) return;
   b = __builtin_amdgcn_readfirstlane(b);
@@ -870,20 +876,27 @@ __global__ __launch_bounds__(kCombineThreads) void attention_combine_kernel(
     int n_chunks, uint16_t* __restrict__ out) {
   __shared__ float s_m[kMaxChunks];
   __shared__ float s_l[kMaxChunks];
+  args_in_sgprs(part_o, part_ml, n_heads, n_chunks, out);
   const int bh = blockIdx.x;  // b * n_heads + h
   const int b = bh / n_heads, h = bh - b * n_heads;
-  const int64_t cstride = (int64_t)n_heads * kDim;
-  const float* base = part_o + ((int64_t)b * n_chunks * n_heads + h) * kDim;
-  const float* mlb = part_ml + ((int64_t)b * n_chunks * n_heads + h) * 2;
-  const int d0 = 4 * threadIdx.x;
+  // Chunk c's record of this head starts cstride bytes after chunk c - 1's.  The records
+  // are read through buffer resources that end with the last chunk's, so every load of a
+  // round is issued unconditionally (a chunk past the last one reads zeros) and the
+  // round's loads are in flight together.  The largest resource, 4096 chunks of 128
+  // heads, spans 1 GiB; with no chunks (an empty row list) both are empty.
+  const uint32_t cstride = (uint32_t)n_heads * kDim * 4;
+  const int64_t rec0 = (int64_t)b * n_chunks * n_heads + h;
+  const Rsrc ro = make_rsrc(part_o + rec0 * kDim, n_chunks > 0 ? (uint32_t)(n_chunks - 1) * cstride + kDim * 4 : 0u);
+  const Rsrc rm = make_rsrc(part_ml + rec0 * 2, n_chunks > 0 ? (uint32_t)(n_chunks - 1) * n_heads * 8 + 8 : 0u);
+  const uint32_t d0 = 4 * threadIdx.x;
 
   f32x4 v[kCombineBatch];
 #pragma unroll
   for (int i = 0; i < kCombineBatch; ++i)
-    v[i] = i < n_chunks ? *reinterpret_cast<const f32x4*>(base + i * cstride + d0)
-                        : f32x4{0.f, 0.f, 0.f, 0.f};
+    v[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, 4 * d0 + i * cstride, 0, 0));
   for (int c = threadIdx.x; c < n_chunks; c += kCombineThreads) {
-    const f32x2 ml = *reinterpret_cast<const f32x2*>(mlb + (int64_t)c * n_heads * 2);
+    const f32x2 ml =
+        __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rm, (uint32_t)c * n_heads * 8, 0, 0));
     s_m[c] = ml[0];
     s_l[c] = ml[1];
   }
@@ -898,8 +911,8 @@ __global__ __launch_bounds__(kCombineThreads) void attention_combine_kernel(
       if (c0 > 0) {
 #pragma unroll
         for (int i = 0; i < kCombineBatch; ++i)
-          v[i] = c0 + i < n_chunks ? *reinterpret_cast<const f32x4*>(base + (c0 + i) * cstride + d0)
-                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+          v[i] = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, 4 * d0 + (uint32_t)(c0 + i) * cstride, 0, 0));
       }
 #pragma unroll
       for (int i = 0; i < kCombineBatch; ++i) {

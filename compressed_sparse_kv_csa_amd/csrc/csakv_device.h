@@ -28,6 +28,21 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
 
+// ---------------------------------------------------------------- kernel arguments
+
+// Kernel arguments are read from the argument segment by scalar loads that the compiler
+// places at each argument's first use, so a prologue with branches pays one round trip
+// per group of first uses.  Naming every argument as a scalar-register input of an empty
+// asm statement at kernel entry issues all of those loads together, behind one wait.
+template <class T>
+__device__ __forceinline__ void arg_in_sgprs(T v) {
+  asm volatile("" ::"s"(v));
+}
+template <class... T>
+__device__ __forceinline__ void args_in_sgprs(T... v) {
+  (arg_in_sgprs(v), ...);
+}
+
 // ---------------------------------------------------------------- bf16 bits
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {

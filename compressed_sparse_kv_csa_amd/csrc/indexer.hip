@@ -346,6 +346,9 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
   __shared__ uint32_t s_score[kSliceRows];  // order keys of the slice's scores
   __shared__ SelectSmem sm;
 
+  args_in_sgprs(codes, scales, seq_stride, page_table, page_shift, table_stride, n_c, seq_rows, q_idx,
+                w_idx, n_heads, n_slices, slices_per_wg, wg_per_query, prefix, cap, ws.cand, ws.bound,
+                ws.count, ws.scores);
   const int b = blockIdx.x / wg_per_query;
   const int slice0 = (blockIdx.x - b * wg_per_query) * slices_per_wg;
   const int n_sl = min(slices_per_wg, n_slices - slice0);
@@ -544,6 +547,7 @@ __global__ __launch_bounds__(kMergeThreads) void indexer_merge_kernel(
     IndexerWs ws, int64_t n_c, const int32_t* __restrict__ seq_rows, int top_k, int n_slices,
     int cap, int first, int32_t* __restrict__ topk) {
   __shared__ MergeSmem ms;
+  args_in_sgprs(ws.cand, ws.bound, ws.count, ws.scores, n_c, seq_rows, top_k, n_slices, cap, first, topk);
   const int b = blockIdx.x;
   merge_query<kMergeThreads, kMergeFirstPerThread>(ws, n_c, seq_rows, top_k, n_slices, cap, first, b,
                                                    ms, topk + (int64_t)b * top_k, nullptr);
