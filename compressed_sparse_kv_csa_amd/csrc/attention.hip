@@ -865,17 +865,21 @@ __global__ __launch_bounds__(kWideThreads) void attention_wide_kernel(
   for (int i = 0; i < kHalfDim / 16; ++i) *reinterpret_cast<f32x4*>(orow + 16 * i) = o[i];
 }
 
-// One workgroup per (query, head): merges the chunks' (max, sum, O) records.  Up to
-// kCombineBatch chunks are read in a single round of independent loads (records, maxima
-// and sums together); more chunks take further rounds.
+// One workgroup per (query, head): merges the chunks' (max, sum, O) records.  NB chunks
+// (the launch picks the smallest power of two covering the chunk count, at most
+// kCombineMaxBatch) are read in a single round of independent loads; more chunks take
+// further rounds.
 constexpr int kCombineThreads = 128;   // 4 dims each
-constexpr int kCombineBatch = 32;
+constexpr int kCombineMaxBatch = 32;
 
+template <int NB>
 __global__ __launch_bounds__(kCombineThreads) void attention_combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml, int n_heads,
     int n_chunks, uint16_t* __restrict__ out) {
-  __shared__ float s_m[kMaxChunks];
-  __shared__ float s_l[kMaxChunks];
+  // With fewer than kCombineMaxBatch chunks there are at most NB maxima and sums.
+  constexpr int kSlots = NB < kCombineMaxBatch ? NB : kMaxChunks;
+  __shared__ float s_m[kSlots];
+  __shared__ float s_l[kSlots];
   args_in_sgprs(part_o, part_ml, n_heads, n_chunks, out);
   const int bh = blockIdx.x;  // b * n_heads + h
   const int b = bh / n_heads, h = bh - b * n_heads;
@@ -890,9 +894,9 @@ __global__ __launch_bounds__(kCombineThreads) void attention_combine_kernel(
   const Rsrc rm = make_rsrc(part_ml + rec0 * 2, n_chunks > 0 ? (uint32_t)(n_chunks - 1) * n_heads * 8 + 8 : 0u);
   const uint32_t d0 = 4 * threadIdx.x;
 
-  f32x4 v[kCombineBatch];
+  f32x4 v[NB];
 #pragma unroll
-  for (int i = 0; i < kCombineBatch; ++i)
+  for (int i = 0; i < NB; ++i)
     v[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, 4 * d0 + i * cstride, 0, 0));
   for (int c = threadIdx.x; c < n_chunks; c += kCombineThreads) {
     const f32x2 ml =
@@ -907,15 +911,15 @@ __global__ __launch_bounds__(kCombineThreads) void attention_combine_kernel(
   float den = 0.0f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (mmax != -INFINITY) {
-    for (int c0 = 0; c0 < n_chunks; c0 += kCombineBatch) {
+    for (int c0 = 0; c0 < n_chunks; c0 += NB) {
       if (c0 > 0) {
 #pragma unroll
-        for (int i = 0; i < kCombineBatch; ++i)
+        for (int i = 0; i < NB; ++i)
           v[i] = __builtin_bit_cast(
               f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, 4 * d0 + (uint32_t)(c0 + i) * cstride, 0, 0));
       }
 #pragma unroll
-      for (int i = 0; i < kCombineBatch; ++i) {
+      for (int i = 0; i < NB; ++i) {
         if (c0 + i < n_chunks) {
           const float wt = exp2f(s_m[c0 + i] - mmax);  // 0 for empty chunks (max -inf)
           den += s_l[c0 + i] * wt;
@@ -1071,8 +1075,17 @@ hipError_t launch_attention(int kv_fmt, bool csa, const uint8_t* codes, const ui
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(attention_combine_kernel, dim3(batch * n_heads), dim3(kCombineThreads), 0,
-                     stream, part_o, part_ml, n_heads, plan.n_chunks, out);
+  // A round's loads past the last chunk read nothing but still pass through the address
+  // unit, so the round is as short as the chunk count allows.
+#define CSAKV_COMBINE(NB)                                                                       \
+  hipLaunchKernelGGL((attention_combine_kernel<NB>), dim3(batch * n_heads), dim3(kCombineThreads), \
+                     0, stream, part_o, part_ml, n_heads, plan.n_chunks, out)
+  if (plan.n_chunks <= 2) CSAKV_COMBINE(2);
+  else if (plan.n_chunks <= 4) CSAKV_COMBINE(4);
+  else if (plan.n_chunks <= 8) CSAKV_COMBINE(8);
+  else if (plan.n_chunks <= 16) CSAKV_COMBINE(16);
+  else CSAKV_COMBINE(kCombineMaxBatch);
+#undef CSAKV_COMBINE
   return hipGetLastError();
 }
 
