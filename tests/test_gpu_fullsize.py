@@ -80,9 +80,9 @@ def test_csa2_stack_fp4_1m():
 def test_csa2_reindex_fp4_1m():
     # Hierarchical indexer at the CSA2 workload: the Full layer selects a 1024-row pool over
     # 262,144 FP4 keys; a Reindex layer re-ranks the pool with its own indexer query to 512
-    # rows and attends (REUSE) over its own FP4 cache.  8 tokens, queries 0 and 5 checked.
+    # rows and attends (REUSE) over its own FP4 cache.  8 tokens, every query checked.
     seed, B, n_c, W, hq, hi, P, k = 5, 8, 262144, 128, 64, 64, 1024, 512
-    check = [0, 5]
+    check = list(range(B))
     print(f"case: csa2 reindex seed={seed} B={B} Nc={n_c} pool={P} k={k} checked={check}", flush=True)
     ix = make_indexer(seed, 0, B, n_c, hi, P, "fp4", check)
     p = ck.CsaParams(B, 0, hi, P, 0, ck.MODE_FULL, 1.0, 0)
@@ -124,8 +124,8 @@ def test_csa2_reindex_fp4_1m():
 
 def test_csa_fp4h_mixed_1m():
     # The 1M mixed workload with Hadamard-rotated FP4 indexer keys (the indexer rotates and
-    # FP4-quantises the queries itself); queries 0 and 3 checked.
-    _csa_full_layer(7, 4, 262144, 128, 64, 64, 512, "mixed", "fp4h", [0, 3], "csa fp4h mixed 1M")
+    # FP4-quantises the queries itself); every query checked.
+    _csa_full_layer(7, 4, 262144, 128, 64, 64, 512, "mixed", "fp4h", [0, 1, 2, 3], "csa fp4h mixed 1M")
 
 
 def test_hca_1m():
