@@ -19,7 +19,10 @@ library's own launches; step i runs on replica i % R), replayed once untimed and
 between HIP events on the current stream.  `protocol` adds the R-step graph (all
 replicas) replayed 50 times.  Output: one JSON line.  `roofline` reports the dominant
 kernel (the indexer scan, csa_select_scan; for HCA the whole hca_decode): K back-to-back
-launches captured and timed the same way, on the stream they run on.  `cpu_baseline`
+launches captured and timed the same way, on the stream they run on, as algorithmic GB/s
+against 8 TB/s, as algorithmic TFLOP/s against the 2.5 PFLOP/s of dense fp16/bf16 MFMA
+(`mfma`), and against the rate a plain streaming read reaches on the same GPU
+(`read_probe`).  `cpu_baseline`
 times the CPU oracle on a bounded sample of the same workload, on one thread and on
 every host core.
 """
@@ -39,6 +42,7 @@ if ROOT not in sys.path:
 
 METRIC = "CSA decode query-tokens/s + achieved HBM GB/s, top-512 @1M ctx, 1 GPU"
 HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16 matrix cores (the scan's and attention's MFMA types)
 MALL_BYTES = 1 << 30
 
 WORKLOADS = {
@@ -89,6 +93,40 @@ def algorithmic_bytes(w: dict) -> dict:
     idx = scan + B * k * 4                                  # the merge writes topk
     reuse = (w["layers"] - 1) * (attn + B * k * 4)
     return {"scan": scan, "indexer": idx, "attention": attn, "step": idx + attn + reuse}
+
+
+def algorithmic_flops(w: dict) -> int:
+    """Flops of the dominant timed unit: the indexer scan's contraction 2·H_I·128·N_c per
+    query, or for HCA the whole attention, 4·H_q·512·rows per query."""
+    if w["kind"] == "hca":
+        return w["B"] * 4 * w["hq"] * 512 * (w["n_c"] + w["window"])
+    return w["B"] * 2 * w["hi"] * 128 * w["n_c"]
+
+
+READ_PROBE = "row sums of a 2 GiB float32 buffer (torch.sum over rows of 4096), best of 5"
+
+
+def read_probe_gbps(reps: int = 5, nbytes: int = 2 << 30) -> float:
+    """Achieved HBM read bandwidth of a plain streaming read (the row sums of a 2 GiB float32
+    buffer viewed as rows of 4096 values; 512 KB written), GB/s, best of `reps` timed
+    passes after one untimed pass: the rate a simple read-only kernel reaches on this GPU,
+    beside the 8 TB/s specification.  (A full reduction to one value reads more slowly.)"""
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda").view(-1, 4096)
+    x.sum(dim=1)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        x.sum(dim=1)
+        t1.record()
+        torch.cuda.synchronize()
+        best = max(best, nbytes / (t0.elapsed_time(t1) * 1e-3) / 1e9)
+    del x
+    torch.cuda.empty_cache()
+    return best
 
 
 def build_inputs(w: dict, replicas: int):
@@ -503,6 +541,8 @@ def main():
     ap.add_argument("--cpu-queries", type=int, default=None,
                     help="query tokens in the oracle sample (default: one step's batch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-probe", action="store_true",
+                    help="skip the streaming read-bandwidth probe (for counter-collection runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -520,6 +560,8 @@ def main():
     step_gbps = g["bytes"]["step"] / (g["ms"] * 1e-3) / 1e9
     stage_gbps = g["stage_bytes"] / (g["stage_ms"] * 1e-3) / 1e9
     whole_gbps = (g["whole_bytes"] / (g["whole_ms"] * 1e-3) / 1e9) if g["whole_ms"] else None
+    probe = None if args.no_read_probe else read_probe_gbps()
+    stage_tflops = algorithmic_flops(w) / (g["stage_ms"] * 1e-3) / 1e12
     cpu = None
     if not args.no_cpu_baseline:
         cpu = run_cpu_baseline(w, args.cpu_queries or B)
@@ -553,6 +595,13 @@ def main():
                      "kernel": g["stage_name"],
                      "avg_launch_us": round(g["stage_ms"] * 1e3, 2),
                      "algorithmic_bytes_per_launch": g["stage_bytes"],
+                     "mfma": {"achieved_tflops": round(stage_tflops, 1), "peak_tflops": MFMA_PEAK_TFLOPS,
+                              "frac": round(stage_tflops / MFMA_PEAK_TFLOPS, 4),
+                              "algorithmic_flops_per_launch": algorithmic_flops(w)},
+                     "read_probe": (None if probe is None else
+                                    {"gbps": round(probe, 1), "frac_of_peak": round(probe / HBM_PEAK_GBPS, 4),
+                                     "frac_achieved_of_probe": round(stage_gbps / probe, 4),
+                                     "kernel": READ_PROBE}),
                      **({"stage": {"kernels": g["whole_name"],
                                    "avg_launch_us": round(g["whole_ms"] * 1e3, 2),
                                    "algorithmic_bytes_per_launch": g["whole_bytes"],
