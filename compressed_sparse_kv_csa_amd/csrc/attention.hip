@@ -876,7 +876,8 @@ template <int NB>
 __global__ __launch_bounds__(kCombineThreads) void attention_combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml, int n_heads,
     int n_chunks, uint16_t* __restrict__ out) {
-  // With fewer than kCombineMaxBatch chunks there are at most NB maxima and sums.
+  // The launch picks NB < kCombineMaxBatch only for at most NB chunks, so NB slots then
+  // hold every chunk's maximum and sum.
   constexpr int kSlots = NB < kCombineMaxBatch ? NB : kMaxChunks;
   __shared__ float s_m[kSlots];
   __shared__ float s_l[kSlots];
