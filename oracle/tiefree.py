@@ -18,6 +18,17 @@ s_j + E_j >= min_{i in S}(s_i - E_i) has its source bf16 key row halved (exact i
 bf16; the ReLU form makes the score halve as well), the row is re-encoded in the
 cache format, and the check repeats until it holds.  The adjusted keys are then
 the test input for both the oracle and the GPU.
+
+Ties at zero.  With few indexer heads and k close to N_c the selection can reach the
+rows whose score is 0 (every head's dot product negative), which halving cannot
+separate.  A score is certainly 0 under any fp32 evaluation when each head with a
+nonzero weight has a dot product d with d + (d_I + 2) * 2**-23 * sum_c |q_hc k_jc| <= 0:
+the fp32 dot product is then <= 0, ReLU gives exactly 0, and the weighted sum of
+zeros is exactly 0.  Equal scores go to the lower index (reading R3), so once every
+row is either certainly positive (s_j - E_j > 0) or certainly 0, the set is the
+positive rows plus the lowest-index zero rows on any evaluation.  When the selection's
+lowest bound is not above 0, every other row (a score within its bound of 0) has its
+source key row set to zero, which makes it certainly 0.
 """
 from __future__ import annotations
 
@@ -40,6 +51,15 @@ def _decode_keys(bits: np.ndarray, fmt: str) -> np.ndarray:
     raise ValueError(fmt)
 
 
+def certainly_zero(q, w, kd) -> np.ndarray:
+    """Rows whose score is exactly 0 under any fp32 evaluation order (see above)."""
+    d_i = kd.shape[1]
+    dots = kd @ q.T
+    mags = np.abs(kd) @ np.abs(q).T
+    ok = (dots + (d_i + 2) * 2.0 ** -23 * mags <= 0.0) | (w[None, :] == 0.0)
+    return ok.all(axis=1)
+
+
 def make_tie_free(key_bits, q_idx, w_idx, top_k: int, fmt: str, max_iter: int = 64):
     """Return (adjusted key bf16 bits [B][N_c][d_I], certificates list).
 
@@ -60,7 +80,7 @@ def make_tie_free(key_bits, q_idx, w_idx, top_k: int, fmt: str, max_iter: int = 
         kd = _decode_keys(keys[b], fmt)
         s = indexer_scores(q, w, kd)
         t = (np.abs(kd) @ np.abs(q).T) @ np.abs(w)
-        halved = 0
+        halved = zeroed = 0
         for _ in range(max_iter):
             if n_c <= top_k:
                 break
@@ -69,16 +89,22 @@ def make_tie_free(key_bits, q_idx, w_idx, top_k: int, fmt: str, max_iter: int = 
             in_s[sel] = True
             e = c_err * t
             lo = np.min(s[in_s] - e[in_s])
-            bad = np.nonzero((~in_s) & (s + e >= lo))[0]
-            if bad.size == 0:
-                break
-            vals = formats.bf16_bits_to_f64(keys[b, bad]) * 0.5
-            keys[b, bad] = formats.f64_to_bf16_bits(vals)
+            if lo > 0.0:  # separate the unselected rows from the selected ones
+                bad = np.nonzero((~in_s) & (s + e >= lo))[0]
+                if bad.size == 0:
+                    break
+                keys[b, bad] = formats.f64_to_bf16_bits(formats.bf16_bits_to_f64(keys[b, bad]) * 0.5)
+                halved += bad.size
+            else:  # the selection reaches scores near 0: make every such row certainly 0
+                bad = np.nonzero(~certainly_zero(q, w, kd) & (s - e <= 0.0))[0]
+                if bad.size == 0:
+                    break
+                keys[b, bad] = 0
+                zeroed += bad.size
             kd_bad = _decode_keys(keys[b, bad], fmt)
             kd[bad] = kd_bad
             s[bad] = indexer_scores(q, w, kd_bad)
             t[bad] = (np.abs(kd_bad) @ np.abs(q).T) @ np.abs(w)
-            halved += bad.size
         else:
             raise RuntimeError(f"query {b}: no tie-free certificate after {max_iter} rounds")
         if n_c > top_k:
@@ -87,12 +113,19 @@ def make_tie_free(key_bits, q_idx, w_idx, top_k: int, fmt: str, max_iter: int = 
             in_s[sel] = True
             e = c_err * t
             lo = float(np.min(s[in_s] - e[in_s]))
-            hi = float(np.max(s[~in_s] + e[~in_s]))
-            if not lo > 0.0:
-                raise RuntimeError(f"query {b}: selection boundary not above zero")
-            certs.append({"query": b, "rows_halved": int(halved), "low_selected": lo,
-                          "high_unselected": hi})
+            if lo > 0.0:
+                hi = float(np.max(s[~in_s] + e[~in_s]))
+                certs.append({"query": b, "rows_halved": int(halved), "rows_zeroed": int(zeroed),
+                              "zero_ties": False, "low_selected": lo, "high_unselected": hi})
+            else:
+                pos = s > 0.0
+                if not (np.all(s[pos] - e[pos] > 0.0) and np.all(certainly_zero(q, w, kd)[~pos])):
+                    raise RuntimeError(f"query {b}: rows neither certainly positive nor certainly 0")
+                certs.append({"query": b, "rows_halved": int(halved), "rows_zeroed": int(zeroed),
+                              "zero_ties": True,
+                              "low_selected": float(np.min(s[pos] - e[pos])) if pos.any() else None,
+                              "high_unselected": 0.0})
         else:
-            certs.append({"query": b, "rows_halved": 0, "low_selected": None,
-                          "high_unselected": None})
+            certs.append({"query": b, "rows_halved": 0, "rows_zeroed": 0, "zero_ties": False,
+                          "low_selected": None, "high_unselected": None})
     return keys, certs

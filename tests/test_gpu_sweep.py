@@ -1,0 +1,73 @@
+"""A seeded sweep of small CSA and HCA decode configurations on the GPU against the oracle.
+
+The configurations are drawn once from a fixed generator over the whole supported
+range: batch sizes, compressed lengths that are not multiples of the 16-row tile,
+windows from none to 128, query heads 16..128, indexer heads 1..128, top-k from 1 to
+2048 (some beyond N_c), and every pairing of main-KV and indexer-key formats.  Each
+case is checked like the hand-picked ones: top-k index sets bit-exact (inputs made
+tie-free), outputs within 1e-2 max-abs."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import compressed_sparse_kv_csa_amd as ck
+import seedgen
+from cases import attention_error, bf16_bits, encode_kv, make_csa_case, oracle_hca, topk_sets_equal
+from gpu_helpers import run_csa, to_dev, upload_kv, workspace
+
+pytestmark = pytest.mark.gpu
+
+
+def _csa_specs(n=48):
+    g = np.random.default_rng(20261203)
+    specs = []
+    for i in range(n):
+        B = int(g.choice([1, 2, 3, 5]))
+        n_c = int(g.integers(1, 6000))
+        W = int(g.choice([0, 1, 37, 128]))
+        hq = int(g.choice([16, 32, 48, 64, 80, 128]))
+        hi = int(g.choice([1, 3, 16, 17, 33, 64, 128]))
+        k = int(g.choice([1, 5, 64, 333, 512, 1024, 2048]))
+        kv = str(g.choice(["bf16", "mixed", "fp4"]))
+        idx = str(g.choice(["bf16", "fp4", "fp4h"]))
+        specs.append((3000 + i, B, n_c, W, hq, hi, k, kv, idx))
+    return specs
+
+
+def _hca_specs(n=12):
+    g = np.random.default_rng(20261204)
+    return [(3100 + i, int(g.choice([1, 2, 3, 7])), int(g.integers(1, 5000)),
+             int(g.choice([16, 48, 64, 96, 128])), str(g.choice(["bf16", "mixed", "fp4"])))
+            for i in range(n)]
+
+
+@pytest.mark.parametrize("spec", _csa_specs(), ids=lambda s: "-".join(map(str, s)))
+def test_csa_sweep(spec):
+    seed, B, n_c, W, hq, hi, k, kvf, idf = spec
+    print(f"case: csa sweep seed={seed} B={B} Nc={n_c} W={W} Hq={hq} HI={hi} k={k} kv={kvf} idx={idf}",
+          flush=True)
+    case = make_csa_case(seed, B, n_c, W, hq, hi, k, kvf, idf)
+    topk, out = run_csa(case)
+    assert topk_sets_equal(topk, case.expect_topk)
+    err, ok = attention_error(out, case.expect_out)
+    assert ok, err
+
+
+@pytest.mark.parametrize("spec", _hca_specs(), ids=lambda s: "-".join(map(str, s)))
+def test_hca_sweep(spec):
+    seed, B, rows, hq, kvf = spec
+    print(f"case: hca sweep seed={seed} B={B} rows={rows} Hq={hq} kv={kvf}", flush=True)
+    T = seedgen.TID
+    q_bits = bf16_bits(seedgen.bf16_normal(seed, seedgen.tid(T.Q), (B, hq, 512)))
+    kv = encode_kv(bf16_bits(seedgen.kv_rows_bf16(seed, seedgen.tid(T.KV), (B, rows, 512))), kvf)
+    kvc, keep = upload_kv(kv)
+    out = torch.empty((B, hq, 512), dtype=torch.int16, device="cuda")
+    ws = workspace(ck.hca_decode_workspace_bytes(B, hq, rows))
+    scale = 1.0 / math.sqrt(512)
+    ck.hca_decode(B, hq, scale, kvc, to_dev(q_bits.view(np.int16)), out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().view(torch.bfloat16).double().numpy()
+    err, ok = attention_error(got, oracle_hca(q_bits, kv, scale))
+    assert ok, err

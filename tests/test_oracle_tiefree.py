@@ -39,7 +39,13 @@ def _check(fmt, seed, B, Nc, H, k):
             got = set(np.argsort(-s32, kind="stable")[:k].tolist())
             assert got == ref, (fmt, b, order)
         c = certs[b]
-        assert c["low_selected"] > c["high_unselected"]
+        if c["zero_ties"]:  # positives certainly above 0, every other row certainly 0
+            assert c["high_unselected"] == 0.0
+            assert c["low_selected"] is None or c["low_selected"] > 0.0
+            s32 = _fp32_scores(q[b], w[b], kd, "forward")
+            assert np.count_nonzero(s32 > 0) < k and np.all(s32 >= 0)
+        else:
+            assert c["low_selected"] > c["high_unselected"]
     return certs
 
 
@@ -57,3 +63,22 @@ def test_tie_free_few_heads_and_small_nc():
     bits, q, w = _inputs(24, 1, 100, 4)
     _, certs = tiefree.make_tie_free(bits, q, w, 512, "bf16")
     assert certs[0]["low_selected"] is None            # N_c <= k: everything is selected
+
+
+def test_tie_free_zero_ties_with_few_heads():
+    # Three indexer heads: about one row in eight scores exactly 0 (every head negative),
+    # and top-2048 of 2118 rows reaches them.  The set is the positive rows plus the
+    # lowest-index zero rows in every fp32 evaluation order.
+    for fmt, seed in (("bf16", 25), ("fp4", 26)):
+        certs = _check(fmt, seed, 2, 2118, 3, 2048)
+        assert all(c["zero_ties"] for c in certs), certs
+
+
+def test_certainly_zero_rows():
+    q = np.array([[1.0, -2.0], [0.5, 0.5]])
+    w = np.array([1.0, 0.0])
+    kd = np.array([[-1.0, 1.0],     # head 0: -3, clearly negative; head 1 has weight 0
+                   [0.0, 0.0],      # all products 0: exactly 0
+                   [2.0, 1.0],      # head 0: 0 exactly, from nonzero terms: not certain
+                   [1.0, 0.0]])     # head 0: +1
+    assert tiefree.certainly_zero(q, w, kd).tolist() == [True, True, False, False]
