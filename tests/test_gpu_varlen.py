@@ -12,7 +12,7 @@ import torch
 import compressed_sparse_kv_csa_amd as ck
 import seedgen
 from cases import (IDX_FMTS, KV_FMTS, attention_error, bf16_bits, encode_idx, encode_kv,
-                   topk_sets_equal)
+                   indexer_query_values, topk_sets_equal)
 from gpu_helpers import Guarded, to_dev, workspace
 from oracle import decode as OD, formats as OF, tiefree
 
@@ -29,11 +29,12 @@ def _varlen_case(seed, lens, cap, window, hq, hi, top_k, kv_fmt, idx_fmt):
     qi = seedgen.bf16_normal(seed, seedgen.tid(T.Q_IDX), (B, hi, DI))
     w = seedgen.uniform01(seed, seedgen.tid(T.W_IDX), (B, hi)).numpy().astype(np.float64)
     keys = bf16_bits(seedgen.bf16_normal(seed, seedgen.tid(T.IDX_KEYS), (B, cap, DI))).copy()
+    qv = indexer_query_values(bf16_bits(qi), idx_fmt)  # as the scores use them
     for b, n in enumerate(lens):
         m = max(0, min(n, cap))
         if m > 0:
-            kb, _ = tiefree.make_tie_free(keys[b:b + 1, :m].copy(), qi.double().numpy()[b:b + 1],
-                                          w[b:b + 1], top_k, idx_fmt)
+            kb, _ = tiefree.make_tie_free(keys[b:b + 1, :m].copy(), qv[b:b + 1], w[b:b + 1], top_k,
+                                          idx_fmt)
             keys[b, :m] = kb[0]
     kv_bits = bf16_bits(seedgen.kv_rows_bf16(seed, seedgen.tid(T.KV), (B, window + cap, D)))
     return dict(q=q, qi=bf16_bits(qi), w=w.astype(np.float32), kv=encode_kv(kv_bits, kv_fmt),
