@@ -12,7 +12,8 @@ import torch
 
 import compressed_sparse_kv_csa_amd as ck
 import seedgen
-from cases import DI, IDX_FMTS, bf16_bits, encode_idx, make_csa_case, topk_sets_equal
+from cases import (DI, IDX_FMTS, bf16_bits, encode_idx, indexer_query_values, make_csa_case,
+                   topk_sets_equal)
 from gpu_helpers import Guarded, to_dev, upload_idx, workspace
 from oracle import decode as OD, formats as OF, tiefree
 
@@ -36,7 +37,7 @@ def make_case(seed, B, n_c, hi, n_pool, top_k, fmt, n_empty=0, layer=1):
     qi = seedgen.bf16_normal(seed, seedgen.tid(T.Q_IDX, layer), (B, hi, DI))
     w = seedgen.uniform01(seed, seedgen.tid(T.W_IDX, layer), (B, hi)).numpy()
     pool = make_pool(seed, B, n_c, n_pool, n_empty)
-    qv, wv = qi.double().numpy(), w.astype(np.float64)
+    qv, wv = indexer_query_values(bf16_bits(qi), fmt), w.astype(np.float64)
     for b in range(B):  # tie-free inside the pool, for this query
         rows = np.unique(pool[b][(pool[b] >= 0) & (pool[b] < n_c)])
         adj, _ = tiefree.make_tie_free(keys[b][rows][None], qv[b][None], wv[b][None],

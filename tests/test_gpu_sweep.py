@@ -132,3 +132,26 @@ def test_paged_varlen_sweep(spec):
         ref = OD.attention(qv[b], OD.csa_rows(c["kv"].values[b, :W + n], W, sel), p.softmax_scale)
         err, ok = attention_error(out[b], ref)
         assert ok, (b, err)
+
+
+def _reindex_specs(n=12):
+    g = np.random.default_rng(20261206)
+    specs = []
+    for i in range(n):
+        n_pool = int(g.choice([1, 16, 333, 1024, 4096]))
+        n_c = int(g.integers(max(n_pool, 2), 9000))
+        specs.append((3300 + i, int(g.choice([1, 2, 3])), n_c, int(g.choice([1, 3, 16, 64, 128])),
+                      n_pool, int(g.choice([1, 20, 512, 2048])), str(g.choice(["bf16", "fp4", "fp4h"])),
+                      int(g.choice([0, 0, 1, 7]))))
+    return specs
+
+
+@pytest.mark.parametrize("spec", _reindex_specs(), ids=lambda s: "-".join(map(str, s)))
+def test_reindex_sweep(spec):
+    from test_gpu_reindex import check, make_case, run_reindex
+    seed, B, n_c, hi, n_pool, k, fmt, n_empty = spec
+    n_empty = min(n_empty, n_pool - 1)
+    print(f"case: reindex sweep seed={seed} B={B} Nc={n_c} HI={hi} pool={n_pool} k={k} {fmt} "
+          f"empty={n_empty}", flush=True)
+    c = make_case(seed, B, n_c, hi, n_pool, k, fmt, n_empty)
+    check(c, run_reindex(c))
