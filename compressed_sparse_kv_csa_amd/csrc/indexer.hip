@@ -578,6 +578,8 @@ __global__ __launch_bounds__(kReindexScoreThreads) void reindex_score_kernel(
   __shared__ u32x4 s_stage[HT * 4 * kWave];  // query fragments of the HT head tiles
   __shared__ float s_red[HT];
   __shared__ float s_w[16 * HT];
+  args_in_sgprs(codes, scales, seq_stride, pg.table, pg.page_shift, pg.table_stride, n_c_max, seq_rows,
+                q_idx, w_idx, n_heads, pool, n_pool, n_parts, keys);
   const int b = blockIdx.x / n_parts;
   const int part = blockIdx.x - b * n_parts;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -627,6 +629,7 @@ __global__ __launch_bounds__(kReindexThreads) void reindex_select_kernel(
   __shared__ uint64_t s_val[kMaxPool];
   __shared__ uint64_t s_list[kMergeListCap];
   __shared__ SelectSmem sm;
+  args_in_sgprs(keys, n_pool, top_k, topk);
   const int b = blockIdx.x;
   const uint64_t* kq = keys + (int64_t)b * n_pool;
   const int q0 = threadIdx.x * kPer;  // a contiguous run of slots keeps pool order
