@@ -21,12 +21,14 @@ __all__ = [
     "csa_reindex_topk_workspace_bytes", "hca_decode_workspace_bytes",
     "hca_decode", "rope_output", "kv_quantize_fp4", "kv_quantize_fp8", "idx_quantize_fp4_hadamard",
     "kv_cache_write", "kv_dequantize",
-    "kv_cache_bytes", "csakv_status_string", "EXPORTED_SYMBOLS",
+    "kv_cache_bytes", "kv_cache_spec_preset", "csakv_status_string", "EXPORTED_SYMBOLS",
+    "PRESET_V4_PRO_BF16", "PRESET_V4_PRO_MIXED", "PRESET_V4_FLASH", "PRESET_V3_MLA", "PRESET_V32_DSA",
 ]
 
 KV_BF16, KV_FP8_MIXED, KV_FP4 = 0, 1, 2
 IDX_BF16, IDX_FP4, IDX_FP4_HADAMARD = 0, 1, 2
 MODE_FULL, MODE_REUSE, MODE_REINDEX = 0, 1, 2
+PRESET_V4_PRO_BF16, PRESET_V4_PRO_MIXED, PRESET_V4_FLASH, PRESET_V3_MLA, PRESET_V32_DSA = 0, 1, 2, 3, 4
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 
@@ -36,7 +38,7 @@ EXPORTED_SYMBOLS = (
     "csa_select_topk", "csa_select_scan", "csa_select_merge", "csa_reindex_topk",
     "csa_reindex_topk_workspace_bytes",
     "hca_decode_workspace_bytes", "hca_decode", "rope_output", "kv_quantize_fp4", "kv_quantize_fp8", "idx_quantize_fp4_hadamard", "kv_cache_write",
-    "kv_dequantize", "kv_cache_bytes", "csakv_status_string",
+    "kv_dequantize", "kv_cache_bytes", "kv_cache_spec_preset", "csakv_status_string",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -134,6 +136,8 @@ def lib() -> ctypes.CDLL:
         L.kv_dequantize.restype = I32
         L.kv_cache_bytes.argtypes = [P(KvCacheSpec), I64, P(KvCacheBreakdown)]
         L.kv_cache_bytes.restype = ctypes.c_uint64
+        L.kv_cache_spec_preset.argtypes = [I32, P(KvCacheSpec)]
+        L.kv_cache_spec_preset.restype = I32
         L.csakv_status_string.argtypes = [I32]
         L.csakv_status_string.restype = ctypes.c_char_p
         _LIB = L
@@ -343,3 +347,10 @@ def kv_cache_bytes(spec: KvCacheSpec, seq_len: int) -> tuple[int, KvCacheBreakdo
     out = KvCacheBreakdown()
     total = int(lib().kv_cache_bytes(ctypes.byref(spec), int(seq_len), ctypes.byref(out)))
     return total, out
+
+
+def kv_cache_spec_preset(preset: int) -> KvCacheSpec:
+    """The library's KvCacheSpec for a PRESET_* model (raises CsakvError for an unknown one)."""
+    spec = KvCacheSpec()
+    _check(lib().kv_cache_spec_preset(int(preset), ctypes.byref(spec)), "kv_cache_spec_preset")
+    return spec

@@ -451,4 +451,51 @@ uint64_t kv_cache_bytes(const kv_cache_spec* sp, int64_t seq_len, kv_cache_break
   return r.total;
 }
 
+csakv_status kv_cache_spec_preset(int32_t preset, kv_cache_spec* out) {
+  if (!out) return CSAKV_ERR_INVALID;
+  kv_cache_spec s{};
+  // V4-Pro: 30 CSA + 31 HCA layers, 512-dim rows (64 of them RoPE), 128-dim indexer keys.
+  s.n_csa = 30;
+  s.n_hca = 31;
+  s.csa_ratio = 4;
+  s.hca_ratio = 128;
+  s.window = 128;
+  s.kv_dim = 512;
+  s.rope_dim = 64;
+  s.idx_dim = 128;
+  s.kv_fmt = CSAKV_KV_BF16;
+  s.idx_fmt = CSAKV_IDX_BF16;
+  s.count_window = 1;
+  switch (preset) {
+    case CSAKV_PRESET_V4_PRO_BF16:
+      break;
+    case CSAKV_PRESET_V4_PRO_MIXED:
+      s.kv_fmt = CSAKV_KV_FP8_MIXED;
+      s.idx_fmt = CSAKV_IDX_FP4;
+      break;
+    case CSAKV_PRESET_V4_FLASH:
+      s.n_csa = 21;
+      s.n_hca = 20;
+      s.n_swa = 2;
+      s.count_window = 0;
+      s.swa_layer_bytes = 2 * 128 * 2 * (128 + 256);  // K and V, one bf16 head, padded window
+      break;
+    case CSAKV_PRESET_V3_MLA:
+    case CSAKV_PRESET_V32_DSA:
+      s.n_csa = 61;  // every layer keeps one uncompressed row per token
+      s.n_hca = 0;
+      s.csa_ratio = 1;
+      s.window = 0;
+      s.kv_dim = 576;
+      s.rope_dim = 64;
+      s.idx_dim = preset == CSAKV_PRESET_V32_DSA ? 128 : 0;
+      s.count_window = 0;
+      break;
+    default:
+      return CSAKV_ERR_INVALID;
+  }
+  *out = s;
+  return CSAKV_OK;
+}
+
 }  // extern "C"

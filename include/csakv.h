@@ -337,6 +337,32 @@ typedef struct {
 
 uint64_t kv_cache_bytes(const kv_cache_spec* spec, int64_t seq_len, kv_cache_breakdown* out);
 
+/* Model presets for kv_cache_bytes, each as the pages account for it:
+ *   V4_PRO_BF16   30 CSA + 31 HCA layers (ratios 4 and 128), 512-dim bf16 rows, 128-dim bf16
+ *                 indexer keys, the 128-row window counted once per layer
+ *                 ("DeepSeek-V4 KV Cache 深度分析", 附录 calculator output, BF16 block; 八).
+ *   V4_PRO_MIXED  the same with FP8_MIXED rows and FP4 indexer keys of 64 bytes (scale bytes
+ *                 not counted) (the same appendix, mixed block; 六).
+ *   V4_FLASH      21 CSA + 20 HCA bf16 layers without window rows, plus 2 sliding-window
+ *                 layers of 196,608 bytes each (one 128-dim bf16 K/V head over a 128-token
+ *                 window padded by 256) ("DeepSeek V4 의 정확한 KV 캐시 사용량 분석", PS
+ *                 calculation, V4 Flash paragraphs).
+ *   V3_MLA        61 MLA layers: one 576-dim bf16 row per token, no window, no indexer
+ *                 (the same page, MLA paragraph).
+ *   V32_DSA       V3_MLA plus a 128-dim bf16 indexer key per token (the same page, V3.2
+ *                 paragraph).
+ * Fills *out and returns CSAKV_OK; an unknown preset or a NULL out returns CSAKV_ERR_INVALID.
+ * Pure host code. */
+typedef enum {
+  CSAKV_PRESET_V4_PRO_BF16 = 0,
+  CSAKV_PRESET_V4_PRO_MIXED = 1,
+  CSAKV_PRESET_V4_FLASH = 2,
+  CSAKV_PRESET_V3_MLA = 3,
+  CSAKV_PRESET_V32_DSA = 4
+} csakv_preset;
+
+csakv_status kv_cache_spec_preset(int32_t preset, kv_cache_spec* out);
+
 /* Static, NUL-terminated description of a status code. */
 const char* csakv_status_string(int32_t status);
 

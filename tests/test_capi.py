@@ -248,3 +248,41 @@ def test_rope_output_rejects_bad_arguments():
     assert call(base=float("inf")) == ck.ERR_INVALID
     assert call(out=0) == ck.ERR_INVALID
     assert call(pos=FAKE + 4) == ck.ERR_INVALID
+
+
+# Golden figures of whole-model totals, reproduced from the library's presets alone (the
+# printed figures come from the pages; the presets are the library's own table).
+_PRESET_OF = {"v3_mla": (ck.PRESET_V3_MLA, {}), "v32_dsa": (ck.PRESET_V32_DSA, {}),
+              "v4_pro_bf16": (ck.PRESET_V4_PRO_BF16, {}), "v4_pro_mixed": (ck.PRESET_V4_PRO_MIXED, {}),
+              "v4_pro_bf16_nowin": (ck.PRESET_V4_PRO_BF16, {"count_window": 0}),
+              "v4_flash_nowin": (ck.PRESET_V4_FLASH, {})}
+
+
+def _golden_totals():
+    import json
+    with open(os.path.join(os.path.dirname(__file__), "golden", "kv_cache_bytes.json"), encoding="utf-8") as f:
+        pins = json.load(f)["pins"]
+    return [p for p in pins if p["field"] == "total" and p["model"] in _PRESET_OF]
+
+
+@pytest.mark.parametrize("entry", _golden_totals(), ids=lambda e: f"{e['model']}:{e['figure']}")
+def test_kv_cache_presets_reproduce_the_printed_totals(entry):
+    preset, change = _PRESET_OF[entry["model"]]
+    spec = ck.kv_cache_spec_preset(preset)
+    for k, v in change.items():
+        setattr(spec, k, v)
+    total, _ = ck.kv_cache_bytes(spec, entry["seq_len"])
+    unit = {"B": 1, "MiB": 1 << 20, "GiB": 1 << 30}[entry["unit"]]
+    assert abs(total / unit - entry["value"]) <= 0.5 * 10.0 ** (-entry["decimals"]) + 1e-9, \
+        (entry["cite"], entry["figure"], total / unit)
+
+
+def test_kv_cache_presets_exact_and_invalid():
+    n = 1 << 20
+    assert ck.kv_cache_bytes(ck.kv_cache_spec_preset(ck.PRESET_V4_PRO_BF16), n)[0] == 10_334_371_840
+    assert ck.kv_cache_bytes(ck.kv_cache_spec_preset(ck.PRESET_V4_PRO_MIXED), n)[0] == 5_183_938_560
+    assert ck.kv_cache_bytes(ck.kv_cache_spec_preset(ck.PRESET_V3_MLA), n)[0] == 1152 * 61 * n
+    assert ck.kv_cache_bytes(ck.kv_cache_spec_preset(ck.PRESET_V32_DSA), n)[0] == (1152 + 256) * 61 * n
+    with pytest.raises(ck.CsakvError):
+        ck.kv_cache_spec_preset(5)
+    assert ck.lib().kv_cache_spec_preset(0, None) == ck.ERR_INVALID
