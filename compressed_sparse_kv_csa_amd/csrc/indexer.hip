@@ -45,7 +45,7 @@ namespace {
 constexpr int kIdxDim = 128;
 constexpr int kScanWaves = 8;
 constexpr int kScanThreads = kScanWaves * kWave;
-constexpr int kRing = 4;   // tiles in flight per wave; divides slice_rows / (16 * kScanWaves)
+constexpr int kRing = 4;   // tiles in flight per wave (a group); divides kSliceRows / 16
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeFirstPerThread = kMergeFirstSlots / kMergeThreads;  // first-round slots per thread
 
@@ -140,6 +140,30 @@ __device__ __forceinline__ f16x8 fp4x8_to_f16(uint32_t cw, uint32_t scale_code) 
   return as_f16x8(r);
 }
 
+// The bf16 indexer-query fragments wave w of NW converts: head tiles w, w + NW, ...; lane
+// (g, n) holds head 16 * ht + n's channels KT::q_channel(g, t) (zeros past n_heads).  Loaded
+// apart from their conversion so that a kernel can issue them ahead of its key loads and
+// wait for them alone.
+template <class KT, int HT, int NW>
+struct QueryRaw {
+  static constexpr int kPer = (HT + NW - 1) / NW;  // head tiles per wave
+  u32x4 v[kPer][4];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ q_idx, int b, int n_heads, int wave,
+                                       int g, int n) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int head = 16 * (wave + NW * i) + n;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        v[i][t] = u32x4{0u, 0u, 0u, 0u};
+        if (wave + NW * i < HT && head < n_heads)
+          v[i][t] = *reinterpret_cast<const u32x4*>(q_idx + ((int64_t)b * n_heads + head) * kIdxDim +
+                                                    KT::q_channel(g, t));
+      }
+    }
+  }
+};
+
 // Hadamard-rotated FP4 indexer queries (keys stored in the same form).  Wave w of the NW
 // waves prepares head tiles w, w + NW, ...; for head tile ht the 4 lanes g of head n's row hold its channels
 // 32g .. 32g+31 in fp64 and rotate the row together (stages h = 1..16 in registers, h = 32
@@ -149,18 +173,17 @@ __device__ __forceinline__ f16x8 fp4x8_to_f16(uint32_t cw, uint32_t scale_code) 
 // every wave takes its A operands.  `stage` holds HT * 4 * 64 fragments; it is free again
 // when this returns.
 template <int HT, int NW>
-__device__ __forceinline__ void query_frags_fp4h(const uint16_t* __restrict__ q_idx, int b,
-                                                 int n_heads, int wave, int g, int n,
+__device__ __forceinline__ void query_frags_fp4h(const QueryRaw<KeyTileFp4, HT, NW>& raw, int wave, int g,
                                                  f16x8 (&qa)[HT][4], f16x8* stage) {
   const int lane = threadIdx.x & (kWave - 1);
-  for (int ht = wave; ht < HT; ht += NW) {  // wave-uniform
-    const int head = 16 * ht + n;
+#pragma unroll
+  for (int i = 0; i < QueryRaw<KeyTileFp4, HT, NW>::kPer; ++i) {
+    const int ht = wave + NW * i;
+    if (ht >= HT) continue;  // wave-uniform
     double y[32];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (head < n_heads)
-        v = *reinterpret_cast<const u32x4*>(q_idx + ((int64_t)b * n_heads + head) * kIdxDim + 32 * g + 8 * k);
+      const u32x4 v = raw.v[i][k];  // channels 32g + 8k .. + 7
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         y[8 * k + 2 * j] = (double)bf16_to_f32(v[j] & 0xFFFFu);
@@ -202,34 +225,27 @@ __device__ __forceinline__ float query_weight_load(const float* __restrict__ w_i
   return (h < 16 * HT && h < n_heads) ? w_idx[(int64_t)b * n_heads + h] : 0.0f;
 }
 
-// The query fragments and head weights of query b; QH: Hadamard-rotated FP4 queries.
-// bf16 indexer queries, prepared once per workgroup: wave w of the NW waves loads head
-// tiles w, w + NW, ... and their largest magnitudes; all waves then agree on the query's
-// power-of-two scale (fp16 path), each wave converts its tiles' fragments into LDS, and
-// every wave takes all of them.  `red` holds HT floats, `stage` HT * 256 fragments; both
-// are free again when this returns.
+// The query fragments of query b, bf16 indexer queries, prepared once per workgroup from
+// `raw`: wave w of the NW waves takes the largest magnitudes of head tiles w, w + NW, ...;
+// all waves then agree on the query's power-of-two scale (fp16 path), each wave converts its
+// tiles' fragments into LDS, and every wave takes all of them.  `red` holds HT floats,
+// `stage` HT * 256 fragments; both are free again when this returns.
 template <class KT, int HT, int NW>
-__device__ __forceinline__ void query_frags_staged(const uint16_t* __restrict__ q_idx, int b,
-                                                   int n_heads, int wave, int g, int n,
+__device__ __forceinline__ void query_frags_staged(const QueryRaw<KT, HT, NW>& qr, int wave,
                                                    typename KT::Op (&qa)[HT][4], u32x4* stage,
                                                    float* red) {
   typedef typename KT::Op Op;
   const int lane = threadIdx.x & (kWave - 1);
-  constexpr int kPer = (HT + NW - 1) / NW;  // head tiles per wave
-  u32x4 raw[kPer][4];
+  constexpr int kPer = QueryRaw<KT, HT, NW>::kPer;
+  const auto& raw = qr.v;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int ht = wave + NW * i;
     if (ht < HT) {  // wave-uniform
-      const int head = 16 * ht + n;
       float qmax = 0.0f;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (head < n_heads)
-          v = *reinterpret_cast<const u32x4*>(q_idx + ((int64_t)b * n_heads + head) * kIdxDim +
-                                              KT::q_channel(g, t));
-        raw[i][t] = v;
+        const u32x4 v = raw[i][t];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           qmax = fmaxf(qmax, fmaxf(fabsf(bf16_to_f32(v[j] & 0xFFFFu)), fabsf(bf16_to_f32(v[j] >> 16))));
@@ -266,22 +282,21 @@ __device__ __forceinline__ void query_frags_staged(const uint16_t* __restrict__ 
 }
 
 // The query fragments and head weights of query b, prepared once per workgroup (every
-// wave must call this: it holds barriers).  QH: Hadamard-rotated FP4 queries.  `stage`:
-// LDS for HT * 256 fragments; `red`: LDS for HT floats; `s_w`: LDS for 16 * HT floats,
-// which the caller keeps until every wave has left this function.  `w_pre`: this
-// thread's query_weight_load.  wv gets the weights of the accumulator rows lane (g, n)
-// holds (heads 16*ht + 4g + i).
+// wave must call this: it holds barriers).  QH: Hadamard-rotated FP4 queries.  `raw`: this
+// wave's QueryRaw::load.  `stage`: LDS for HT * 256 fragments; `red`: LDS for HT floats;
+// `s_w`: LDS for 16 * HT floats, which the caller keeps until every wave has left this
+// function.  `w_pre`: this thread's query_weight_load.  wv gets the weights of the
+// accumulator rows lane (g, n) holds (heads 16*ht + 4g + i).
 template <class KT, int HT, bool QH, int NW>
-__device__ __forceinline__ void query_setup(const uint16_t* __restrict__ q_idx, float w_pre,
-                                            int b, int n_heads, int wave, int g, int n,
+__device__ __forceinline__ void query_setup(const QueryRaw<KT, HT, NW>& raw, float w_pre, int wave, int g,
                                             typename KT::Op (&qa)[HT][4], float (&wv)[HT][4],
                                             void* stage, float* red, float* s_w) {
   if (threadIdx.x < 16 * HT) s_w[threadIdx.x] = w_pre;  // ordered by the barriers below
   if constexpr (QH) {
     static_assert(KT::kScales, "rotated FP4 queries meet rotated FP4 keys");
-    query_frags_fp4h<HT, NW>(q_idx, b, n_heads, wave, g, n, qa, static_cast<f16x8*>(stage));
+    query_frags_fp4h<HT, NW>(raw, wave, g, qa, static_cast<f16x8*>(stage));
   } else {
-    query_frags_staged<KT, HT, NW>(q_idx, b, n_heads, wave, g, n, qa, static_cast<u32x4*>(stage), red);
+    query_frags_staged<KT, HT, NW>(raw, wave, qa, static_cast<u32x4*>(stage), red);
   }
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht)
@@ -326,9 +341,6 @@ __device__ __forceinline__ float tile_share(const typename KT::Op (&qa)[HT][4],
 
 // ------------------------------------------------------------------ scan kernel
 
-constexpr int kSubTiles = 16;                          // tiles per wave per unrolled pass
-constexpr int kSubRows = 16 * kScanWaves * kSubTiles;  // 2048 rows per pass
-constexpr int kPassesPerSlice = kSliceRows / kSubRows;
 
 // Per-call buffers of the indexer, carved from the caller's workspace.
 
@@ -345,6 +357,7 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
   __shared__ __attribute__((aligned(16))) float s_part[kSliceRows * 4];
   __shared__ uint32_t s_score[kSliceRows];  // order keys of the slice's scores
   __shared__ SelectSmem sm;
+  __shared__ uint32_t s_next;  // the next group of the current slice to hand out
 
   args_in_sgprs(codes, scales, seq_stride, page_table, page_shift, table_stride, n_c, seq_rows, q_idx,
                 w_idx, n_heads, n_slices, slices_per_wg, wg_per_query, prefix, cap, ws.cand, ws.bound,
@@ -359,7 +372,6 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
   const int64_t row_base = (int64_t)slice0 * kSliceRows;              // compressed row index
   const int64_t n_cb = seq_len(seq_rows, b, n_c);                     // this sequence's rows
   const int64_t rows_total = max(min((int64_t)n_sl * kSliceRows, n_cb - row_base), (int64_t)0);
-  const int n_pass = (int)((rows_total + kSubRows - 1) / kSubRows);
   const int64_t seq_row0 = (int64_t)b * seq_stride + row_base;
   // Slices of the run past the sequence's end send nothing.
   const int n_done = (int)((rows_total + kSliceRows - 1) / kSliceRows);
@@ -370,23 +382,28 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
   }
   if (n_done == 0) return;  // the whole workgroup: no barrier is left waiting
 
-  // The wave's tile sequence: slot k -> pass k / kSubTiles, tile wave + 8m of that pass
-  // (m = k % kSubTiles).  Every slot loads (rows past the end read zeros) and computes, so
-  // the loads are straight-line code and the ring keeps kRing tiles in flight across
-  // passes and slices.  A row past the end lands in its slice's buffer at or after the
-  // slice's last row, where nothing reads it.  A pass is unrolled whole so that the
-  // ring's waits are counted exactly.
-  const int total = n_pass * kSubTiles;
-  auto slot_tile = [&](int k) -> int {
-    const int ps = k / kSubTiles, m = k - ps * kSubTiles;
-    return ps * (kSubTiles * kScanWaves) + wave + kScanWaves * m;
-  };
+  // Work balancing.  A slice's rows are taken in groups of RING 16-row tiles, one ring's
+  // worth.  Each wave starts a slice on its own group (group `wave`) and takes further
+  // groups from a workgroup counter in LDS, so that waves the SIMD serves unequally (it
+  // favours the older of the two waves it holds) still finish a slice together.  The ring
+  // holds the current group's tiles and is refilled, tile by tile, with the next group's,
+  // which is known one group ahead (its counter value is fetched while the group before it
+  // runs).  Once a slice's groups are handed out, a wave's next group is its own group of
+  // the following slice, so the ring runs on across slices and starts every slice at slot
+  // 0.  Every refill loads (rows past the end read zeros); a row past the end lands in its
+  // slice's buffer at or after the slice's last row, where nothing reads it.  Groups are
+  // numbered across the workgroup's slices: group G belongs to slice G / kSliceGroups.
+  // With more than 64 heads the bf16 ring is halved: 128 heads' query fragments take 128
+  // registers.
+  constexpr int RING = (HT > 4 && !KT::kScales) ? 2 : kRing;
+  constexpr int kGroupRows = 16 * RING;
+  constexpr int kSliceGroups = kSliceRows / kGroupRows;
   const uint8_t* kcodes = codes + seq_row0 * KT::kRowBytes;
   const uint8_t* kscales = KT::kScales ? scales + seq_row0 * (kIdxDim / 16) : nullptr;
   const int lane_co = KT::code_offset(n, g), lane_so = KT::scale_offset(n, g);
   const int rows_wg = (int)rows_total;  // at most 512 slices of 4096 rows: 32-bit math
-  auto load_slot = [&](KT& kt, int k) {
-    const int r0 = slot_tile(k) * 16;  // wave-uniform (scalar)
+  auto load_tile = [&](KT& kt, int grp, int d) {
+    const int r0 = grp * kGroupRows + 16 * d;  // wave-uniform (scalar)
     // The resource covers the rows from r0 to the end of the workgroup's rows; the tile
     // reads at most 16 of them.
     const int live = max(rows_wg - r0, 0);
@@ -407,16 +424,19 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
     kt.load(rc, rs, lane_co, lane_so);
   };
 
+  // The query's raw fragments and head weights go out first, so that the set-up waits for
+  // them alone; the ring's first loads (the wave's group of the first slice) follow and
+  // overlap the set-up.
+  QueryRaw<KT, HT, kScanWaves> qraw;
+  qraw.load(q_idx, b, n_heads, wave, g, n);
   const float w_pre = query_weight_load<HT>(w_idx, b, n_heads);
-  // The ring's first loads go out before the query setup, which they overlap.  With more
-  // than 64 heads the bf16 ring is halved: 128 heads' query fragments take 128 registers.
-  constexpr int RING = (HT > 4 && !KT::kScales) ? 2 : kRing;
   KT ring[RING];
 #pragma unroll
   for (int d = 0; d < RING; ++d) {
     ring[d].set_lane(g);
-    load_slot(ring[d], d);
+    load_tile(ring[d], wave, d);
   }
+  if (threadIdx.x == 0) s_next = kScanWaves;  // the first slice's counter, ordered by the set-up's barriers
 
   // Indexer query fragments and head weights.
   Op qa[HT][4];
@@ -424,34 +444,47 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
   static_assert(sizeof(s_part) >= sizeof(f16x8) * HT * 4 * kWave, "query stage");
   static_assert(sizeof(sm.hist) >= sizeof(float) * 16 * HT, "weight stage");
   static_assert(sizeof(sm.red32) >= sizeof(float) * HT, "query maxima");
-  query_setup<KT, HT, QH, kScanWaves>(q_idx, w_pre, b, n_heads, wave, g, n, qa, wv, s_part,
+  query_setup<KT, HT, QH, kScanWaves>(qraw, w_pre, wave, g, qa, wv, s_part,
                                       reinterpret_cast<float*>(sm.red32), reinterpret_cast<float*>(sm.hist));
 
-  // Lane (g, n)'s share of tile row r of a pass goes to s_part[4 * r + g]: the slot of
-  // tile wave + 8m of pass ps is row (ps % kPassesPerSlice) * kSubRows + 16 * (wave + 8m)
-  // + n of the slice, so within a pass the address is a per-lane base plus a constant.
-  const int lane_part = 4 * (16 * wave + n) + g;
-  for (int ps = 0; ps < n_pass; ++ps) {
-    float* const pass_part = s_part + 4 * (ps % kPassesPerSlice) * kSubRows + lane_part;
-#pragma unroll
-    for (int m = 0; m < kSubTiles; ++m) {
-      const int d = m % RING;
-      const int k = ps * kSubTiles + m;
-      // Keep each tile's instructions together: hoisting a later tile's decode above
-      // this point would wait on that tile's key load, which is still in flight.
-      __builtin_amdgcn_sched_barrier(0);
-      Op kb[4];
-      ring[d].decode(kb);
-      load_slot(ring[d], k + RING);  // past the end: reads zeros
-      // Each lane stores its share; the shares are added when the slice is complete.
-      pass_part[4 * 16 * kScanWaves * m] = tile_share<KT, HT>(qa, kb, wv);
-    }
-    if ((ps + 1) % kPassesPerSlice != 0 && ps + 1 < n_pass) continue;  // more passes in this slice
-
-    // ---- slice complete: emit its candidates, its bound and its scores
-    const int j = ps / kPassesPerSlice;
+  // Lane (g, n)'s share of the score of slice row r goes to s_part[4 * r + g].
+  const int lane_part = 4 * n + g;
+  int gc = wave;  // the group in the ring
+  for (int j = 0;; ++j) {
     const int64_t srow0 = row_base + (int64_t)j * kSliceRows;
     const int rows = (int)min((int64_t)kSliceRows, n_cb - srow0);
+    const int n_groups = (rows + kGroupRows - 1) / kGroupRows;
+    // The group that follows counter value c of this slice.
+    auto group_after = [&](uint32_t c) -> int {
+      return (int)c < n_groups ? kSliceGroups * j + (int)c : kSliceGroups * (j + 1) + wave;
+    };
+    // The group after the wave's first of this slice (the counter was set before the last
+    // barrier every wave has passed).
+    uint32_t cv = 0u;
+    if (lane == 0) cv = atomicAdd(&s_next, 1u);
+    int gn = group_after(__builtin_amdgcn_readfirstlane(cv));
+    while (gc < kSliceGroups * (j + 1)) {  // the ring holds a group of slice j
+      const bool more = gn < kSliceGroups * (j + 1);
+      cv = 0u;
+      if (more && lane == 0) cv = atomicAdd(&s_next, 1u);  // the group after gn, read after this one
+      float* const gpart = s_part + 4 * kGroupRows * (gc - kSliceGroups * j) + lane_part;
+#pragma unroll
+      for (int d = 0; d < RING; ++d) {
+        // Keep each tile's instructions together: hoisting a later tile's decode above
+        // this point would wait on that tile's key load, which is still in flight.
+        __builtin_amdgcn_sched_barrier(0);
+        Op kb[4];
+        ring[d].decode(kb);
+        load_tile(ring[d], gn, d);  // past the end: reads zeros
+        // Each lane stores its share; the shares are added when the slice is complete.
+        gpart[4 * 16 * d] = tile_share<KT, HT>(qa, kb, wv);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      gc = gn;
+      gn = more ? group_after(__builtin_amdgcn_readfirstlane(cv)) : -1;
+    }
+
+    // ---- slice complete: emit its candidates, its bound and its scores
     const int64_t si = (int64_t)b * n_slices + slice0 + j;
     lds_barrier();  // every wave's shares of the slice are in
     // Thread t adds up the shares of rows t + 512r and keeps their keys in registers, on
@@ -536,8 +569,10 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
     if (threadIdx.x == 0) {
       ws.count[si] = emitted;
       ws.bound[si] = bound;
+      s_next = kScanWaves;  // the next slice's counter
     }
-    lds_barrier();  // s_score and sm are free for the next slice
+    lds_barrier();  // s_score and sm are free, the counter set, for the next slice
+    if (j + 1 >= n_done) break;
   }
 }
 
@@ -589,11 +624,12 @@ __global__ __launch_bounds__(kReindexScoreThreads) void reindex_score_kernel(
 
   const int pos = part * kReindexPartRows + 16 * wave + n;  // lane n's pool slot
   const int32_t r = pos < n_pool ? pool[(int64_t)b * n_pool + pos] : -1;
+  QueryRaw<KT, HT, kReindexScoreWaves> qraw;
+  qraw.load(q_idx, b, n_heads, wave, g, n);
   const float w_pre = query_weight_load<HT>(w_idx, b, n_heads);
   Op qa[HT][4];
   float wv[HT][4];
-  query_setup<KT, HT, QH, kReindexScoreWaves>(q_idx, w_pre, b, n_heads, wave, g, n, qa, wv, s_stage,
-                                              s_red, s_w);
+  query_setup<KT, HT, QH, kReindexScoreWaves>(qraw, w_pre, wave, g, qa, wv, s_stage, s_red, s_w);
 
   const int row = (r >= 0 && r < n_c) ? r : -1;
   const int at = row < 0 || !pg.table
