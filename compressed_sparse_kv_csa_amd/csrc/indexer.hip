@@ -143,22 +143,25 @@ __device__ __forceinline__ f16x8 fp4x8_to_f16(uint32_t cw, uint32_t scale_code) 
 // The bf16 indexer-query fragments wave w of NW converts: head tiles w, w + NW, ...; lane
 // (g, n) holds head 16 * ht + n's channels KT::q_channel(g, t) (zeros past n_heads).  Loaded
 // apart from their conversion so that a kernel can issue them ahead of its key loads and
-// wait for them alone.
+// wait for them alone: the loads go through a buffer resource over query b's rows (a head
+// past n_heads reads zeros), so none of them sits behind a per-lane branch, which would
+// make the compiler wait for the earlier ones before issuing the rest.
 template <class KT, int HT, int NW>
 struct QueryRaw {
   static constexpr int kPer = (HT + NW - 1) / NW;  // head tiles per wave
   u32x4 v[kPer][4];
   __device__ __forceinline__ void load(const uint16_t* __restrict__ q_idx, int b, int n_heads, int wave,
                                        int g, int n) {
+    const Rsrc rq = make_rsrc(q_idx + (int64_t)b * n_heads * kIdxDim, (uint32_t)(n_heads * kIdxDim * 2));
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int head = 16 * (wave + NW * i) + n;
+      const int row = 16 * (wave + NW * i) + n;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         v[i][t] = u32x4{0u, 0u, 0u, 0u};
-        if (wave + NW * i < HT && head < n_heads)
-          v[i][t] = *reinterpret_cast<const u32x4*>(q_idx + ((int64_t)b * n_heads + head) * kIdxDim +
-                                                    KT::q_channel(g, t));
+        if (wave + NW * i < HT)  // wave-uniform
+          v[i][t] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, (row * kIdxDim + KT::q_channel(g, t)) * 2, 0, 0));
       }
     }
   }
@@ -221,8 +224,9 @@ __device__ __forceinline__ void query_frags_fp4h(const QueryRaw<KeyTileFp4, HT, 
 template <int HT>
 __device__ __forceinline__ float query_weight_load(const float* __restrict__ w_idx, int b,
                                                    int n_heads) {
-  const int h = threadIdx.x;
-  return (h < 16 * HT && h < n_heads) ? w_idx[(int64_t)b * n_heads + h] : 0.0f;
+  // A buffer resource over query b's weights: a thread past n_heads reads zero, no branch.
+  const Rsrc rw = make_rsrc(w_idx + (int64_t)b * n_heads, (uint32_t)(n_heads * 4));
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, (int)threadIdx.x * 4, 0, 0));
 }
 
 // The query fragments of query b, bf16 indexer queries, prepared once per workgroup from
