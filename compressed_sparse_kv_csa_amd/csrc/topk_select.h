@@ -18,7 +18,7 @@ constexpr int kListCap = 256;    // boundary-bin keys resolved by direct ranking
 constexpr int kMergeListCap = 1024;  // the same in the merge
 
 struct SelectSmem {
-  uint32_t hist[kHistBins];
+  __attribute__((aligned(16))) uint32_t hist[kHistBins];
   uint64_t red[2 * 16];    // per-wave 64-bit minima / maxima
   uint32_t red32[2 * 16];  // per-wave 32-bit minima / maxima
   uint64_t res64[16];
@@ -297,33 +297,50 @@ __device__ void slice_threshold(const uint32_t (&key)[R], int n, int P, uint32_t
 // histogram of the keys' high words (2048 bins between their min and max) locates the
 // bin holding it; if that whole bin is needed the answer is its smallest key, otherwise
 // the bin's keys are ranked directly (general radix passes if the bin is very full).
-template <int NT>
-__device__ uint64_t block_kth_exact(const uint64_t* keys, int n, int k, SelectSmem& sm,
-                                    uint64_t* list) {
-  constexpr int nw = NT / kWave;
-  constexpr int bpt = kHistBins / NT;
-  const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  uint32_t mn = ~0u, mx = 0u;
-  for (int i = threadIdx.x; i < n; i += NT) {
-    const uint32_t h = (uint32_t)(keys[i] >> 32);
-    mn = h < mn ? h : mn;
-    mx = h > mx ? h : mx;
-  }
-  for (int i = threadIdx.x; i < kHistBins; i += NT) sm.hist[i] = 0;
-  if (threadIdx.x == 0) sm.bc[4] = 0;
-  wave_minmax_u32(mn, mx);
-  if (lane == 0) {
-    sm.red32[w] = mn;
-    sm.red32[16 + w] = mx;
-  }
-  lds_barrier();
-  mn = sm.red32[0];
-  mx = sm.red32[16];
+// The bin of a 2048-bin histogram (sm.hist, counts per bin, bins ascending) that holds
+// the k-th largest key (1 <= k <= the total), found by wave 0 alone: lane l sums bins
+// 2047 - 32l down to 2016 - 32l, a wave scan gives the keys above each lane's bins, and
+// the lane whose range holds rank k walks its bins.  Writes the bin to sm.bc[0] and the
+// keys in the bins above it to sm.bc[1]; the caller's next barrier publishes them.
+__device__ __forceinline__ void wave_find_bin(SelectSmem& sm, uint32_t k) {
+  static_assert(kHistBins == 32 * kWave, "one wave, 32 bins per lane");
+  if (threadIdx.x >= kWave) return;
+  const int lane = threadIdx.x;
+  const u32x4* h4 = reinterpret_cast<const u32x4*>(sm.hist + kHistBins - 32 * (lane + 1));
+  u32x4 v[8];
 #pragma unroll
-  for (int i = 1; i < nw; ++i) {
-    mn = sm.red32[i] < mn ? sm.red32[i] : mn;
-    mx = sm.red32[16 + i] > mx ? sm.red32[16 + i] : mx;
+  for (int i = 0; i < 8; ++i) v[i] = h4[i];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sum += v[i][0] + v[i][1] + v[i][2] + v[i][3];
+  const uint32_t incl = wave_incl_scan_add(sum);
+  uint32_t a = incl - sum;  // keys in the bins above this lane's
+  if (a < k && k <= incl) {
+#pragma unroll
+    for (int i = 7; i >= 0; --i)
+#pragma unroll
+      for (int e = 3; e >= 0; --e) {
+        const uint32_t h = v[i][e];
+        if (a < k && k <= a + h) {
+          sm.bc[0] = (uint32_t)(kHistBins - 32 * (lane + 1) + 4 * i + e);
+          sm.bc[1] = a;
+        }
+        a += h;
+      }
   }
+}
+
+// The k-th largest of n distinct nonzero 64-bit keys held in LDS (1 <= k <= n), given
+// the minimum mn and maximum mx of their high words, with sm.hist zeroed and sm.bc[4] = 0
+// before the caller's last barrier.  A histogram of the high words (2048 bins between mn
+// and mx) locates the bin holding it; if that whole bin is needed the answer is its
+// smallest key, otherwise the bin's keys are ranked directly (general radix passes if the
+// bin is very full).
+template <int NT>
+__device__ uint64_t block_kth_in_range(const uint64_t* keys, int n, int k, SelectSmem& sm,
+                                       uint64_t* list, uint32_t mn, uint32_t mx) {
+  constexpr int nw = NT / kWave;
+  const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   auto at = [&](int i) -> uint64_t { return keys[i]; };
   if (mn == mx) {  // one high word: rank by the low words
     uint64_t kmn, kmx;
@@ -334,26 +351,8 @@ __device__ uint64_t block_kth_exact(const uint64_t* keys, int n, int k, SelectSm
   auto bin_of = [&](uint64_t key) -> uint32_t { return ((uint32_t)(key >> 32) - mn) >> sh; };
   for (int i = threadIdx.x; i < n; i += NT) atomicAdd(&sm.hist[bin_of(keys[i])], 1u);
   lds_barrier();
-  const int b0 = threadIdx.x * bpt;
-  uint32_t own = 0;
-#pragma unroll
-  for (int j = 0; j < bpt; ++j) own += sm.hist[b0 + j];
-  uint32_t total;
-  const uint32_t below = block_exclusive_scan<NT>(own, sm.wsum, &total);
-  const uint32_t above = total - below - own;
   const uint32_t kk = (uint32_t)k;
-  if (above < kk && kk <= above + own) {
-    uint32_t a = above;
-#pragma unroll
-    for (int j = bpt - 1; j >= 0; --j) {
-      const uint32_t h = sm.hist[b0 + j];
-      if (a < kk && kk <= a + h) {
-        sm.bc[0] = b0 + j;
-        sm.bc[1] = a;
-      }
-      a += h;
-    }
-  }
+  wave_find_bin(sm, kk);
   lds_barrier();
   const uint32_t tb = sm.bc[0];
   const uint32_t need = kk - sm.bc[1];  // rank of the answer inside bin tb
@@ -397,6 +396,37 @@ __device__ uint64_t block_kth_exact(const uint64_t* keys, int n, int k, SelectSm
   uint64_t bmn, bmx;
   block_minmax<NT>(bin_at, n, sm, &bmn, &bmx);
   return block_kth_largest<NT>(bin_at, n, (int)need, sm, bmn, bmx);
+}
+
+// The k-th largest of n distinct nonzero 64-bit keys held in LDS (1 <= k <= n): the
+// high words' range, then block_kth_in_range.
+template <int NT>
+__device__ uint64_t block_kth_exact(const uint64_t* keys, int n, int k, SelectSmem& sm,
+                                    uint64_t* list) {
+  constexpr int nw = NT / kWave;
+  const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  uint32_t mn = ~0u, mx = 0u;
+  for (int i = threadIdx.x; i < n; i += NT) {
+    const uint32_t h = (uint32_t)(keys[i] >> 32);
+    mn = h < mn ? h : mn;
+    mx = h > mx ? h : mx;
+  }
+  for (int i = threadIdx.x; i < kHistBins; i += NT) sm.hist[i] = 0;
+  if (threadIdx.x == 0) sm.bc[4] = 0;
+  wave_minmax_u32(mn, mx);
+  if (lane == 0) {
+    sm.red32[w] = mn;
+    sm.red32[16 + w] = mx;
+  }
+  lds_barrier();
+  mn = sm.red32[0];
+  mx = sm.red32[16];
+#pragma unroll
+  for (int i = 1; i < nw; ++i) {
+    mn = sm.red32[i] < mn ? sm.red32[i] : mn;
+    mx = sm.red32[16 + i] > mx ? sm.red32[16 + i] : mx;
+  }
+  return block_kth_in_range<NT>(keys, n, k, sm, list, mn, mx);
 }
 
 __device__ __forceinline__ uint64_t compose_key(uint32_t score_key, uint32_t idx) {
@@ -479,7 +509,11 @@ __device__ void merge_query(const IndexerWs& ws, int64_t n_c, const int32_t* __r
     const int i = (int)threadIdx.x + NT * r;
     slot[r] = i < n_first ? ws.cand[(s0 + (i >> f_shift)) * cap + (i & (first - 1))] : 0ull;
   }
-  // Candidate counts -> offsets in the buffer (n_slices <= NT).
+  // Candidate counts -> offsets in the buffer (n_slices <= NT); on the way, the histogram
+  // of the k-th key search is cleared, and the high words' range of the placed keys taken.
+  for (int i = threadIdx.x; i < kHistBins; i += NT) sm.hist[i] = 0;
+  if (threadIdx.x == 0) sm.bc[4] = 0;
+  uint32_t hmn = ~0u, hmx = 0u;
   const uint32_t c = threadIdx.x < n_slices ? ws.count[s0 + threadIdx.x] : 0u;
   if (threadIdx.x < n_slices) s_bound[threadIdx.x] = ws.bound[s0 + threadIdx.x];
   uint32_t n_buf;
@@ -493,7 +527,12 @@ __device__ void merge_query(const IndexerWs& ws, int64_t n_c, const int32_t* __r
     if (i < n_first) {
       const int s = i >> f_shift, j = i & (first - 1);
       const uint32_t o = s_off[s];
-      if ((uint32_t)j < s_off[s + 1] - o) s_buf[o + j] = slot[r];
+      if ((uint32_t)j < s_off[s + 1] - o) {
+        s_buf[o + j] = slot[r];
+        const uint32_t h = (uint32_t)(slot[r] >> 32);
+        hmn = h < hmn ? h : hmn;
+        hmx = h > hmx ? h : hmx;
+      }
     }
   }
   // The rest of the slices that sent more than `first` keys, one wave per slice.
@@ -501,12 +540,30 @@ __device__ void merge_query(const IndexerWs& ws, int64_t n_c, const int32_t* __r
     const uint32_t o = s_off[s], m = s_off[s + 1] - o;
     if (m <= (uint32_t)first) continue;
     const uint64_t* src = ws.cand + (s0 + s) * cap;
-    for (uint32_t j = (uint32_t)first + lane; j < m; j += kWave) s_buf[o + j] = src[j];
+    for (uint32_t j = (uint32_t)first + lane; j < m; j += kWave) {
+      const uint64_t key = src[j];
+      s_buf[o + j] = key;
+      const uint32_t h = (uint32_t)(key >> 32);
+      hmn = h < hmn ? h : hmn;
+      hmx = h > hmx ? h : hmx;
+    }
+  }
+  wave_minmax_u32(hmn, hmx);
+  if (lane == 0) {
+    sm.red32[wave] = hmn;
+    sm.red32[16 + wave] = hmx;
   }
   lds_barrier();
+  hmn = sm.red32[0];
+  hmx = sm.red32[16];
+#pragma unroll
+  for (int i = 1; i < NT / kWave; ++i) {
+    hmn = sm.red32[i] < hmn ? sm.red32[i] : hmn;
+    hmx = sm.red32[16 + i] > hmx ? sm.red32[16 + i] : hmx;
+  }
 
   // The k1-th largest candidate; 1 (accept all) while there are fewer than k1.
-  uint64_t kth = (int)n_buf >= k1 ? block_kth_exact<NT>(s_buf, (int)n_buf, k1, sm, s_list) : 1ull;
+  uint64_t kth = (int)n_buf >= k1 ? block_kth_in_range<NT>(s_buf, (int)n_buf, k1, sm, s_list, hmn, hmx) : 1ull;
 
   // Slices whose bound lies above kth may hold winners among the keys they did not send.
   {
