@@ -18,7 +18,7 @@ constexpr int kListCap = 256;    // boundary-bin keys resolved by direct ranking
 constexpr int kMergeListCap = 1024;  // the same in the merge
 
 struct SelectSmem {
-  __attribute__((aligned(16))) uint32_t hist[kHistBins];
+  uint32_t hist[kHistBins];
   uint64_t red[2 * 16];    // per-wave 64-bit minima / maxima
   uint32_t red32[2 * 16];  // per-wave 32-bit minima / maxima
   uint64_t res64[16];
@@ -297,39 +297,6 @@ __device__ void slice_threshold(const uint32_t (&key)[R], int n, int P, uint32_t
 // histogram of the keys' high words (2048 bins between their min and max) locates the
 // bin holding it; if that whole bin is needed the answer is its smallest key, otherwise
 // the bin's keys are ranked directly (general radix passes if the bin is very full).
-// The bin of a 2048-bin histogram (sm.hist, counts per bin, bins ascending) that holds
-// the k-th largest key (1 <= k <= the total), found by wave 0 alone: lane l sums bins
-// 2047 - 32l down to 2016 - 32l, a wave scan gives the keys above each lane's bins, and
-// the lane whose range holds rank k walks its bins.  Writes the bin to sm.bc[0] and the
-// keys in the bins above it to sm.bc[1]; the caller's next barrier publishes them.
-__device__ __forceinline__ void wave_find_bin(SelectSmem& sm, uint32_t k) {
-  static_assert(kHistBins == 32 * kWave, "one wave, 32 bins per lane");
-  if (threadIdx.x >= kWave) return;
-  const int lane = threadIdx.x;
-  const u32x4* h4 = reinterpret_cast<const u32x4*>(sm.hist + kHistBins - 32 * (lane + 1));
-  u32x4 v[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = h4[i];
-  uint32_t sum = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) sum += v[i][0] + v[i][1] + v[i][2] + v[i][3];
-  const uint32_t incl = wave_incl_scan_add(sum);
-  uint32_t a = incl - sum;  // keys in the bins above this lane's
-  if (a < k && k <= incl) {
-#pragma unroll
-    for (int i = 7; i >= 0; --i)
-#pragma unroll
-      for (int e = 3; e >= 0; --e) {
-        const uint32_t h = v[i][e];
-        if (a < k && k <= a + h) {
-          sm.bc[0] = (uint32_t)(kHistBins - 32 * (lane + 1) + 4 * i + e);
-          sm.bc[1] = a;
-        }
-        a += h;
-      }
-  }
-}
-
 // The k-th largest of n distinct nonzero 64-bit keys held in LDS (1 <= k <= n), given
 // the minimum mn and maximum mx of their high words, with sm.hist zeroed and sm.bc[4] = 0
 // before the caller's last barrier.  A histogram of the high words (2048 bins between mn
@@ -352,7 +319,26 @@ __device__ uint64_t block_kth_in_range(const uint64_t* keys, int n, int k, Selec
   for (int i = threadIdx.x; i < n; i += NT) atomicAdd(&sm.hist[bin_of(keys[i])], 1u);
   lds_barrier();
   const uint32_t kk = (uint32_t)k;
-  wave_find_bin(sm, kk);
+  constexpr int bpt = kHistBins / NT;
+  const int b0 = threadIdx.x * bpt;
+  uint32_t own = 0;
+#pragma unroll
+  for (int j = 0; j < bpt; ++j) own += sm.hist[b0 + j];
+  uint32_t total;
+  const uint32_t below = block_exclusive_scan<NT>(own, sm.wsum, &total);
+  const uint32_t above = total - below - own;  // keys in bins >= b0 + bpt
+  if (above < kk && kk <= above + own) {
+    uint32_t a = above;
+#pragma unroll
+    for (int j = bpt - 1; j >= 0; --j) {
+      const uint32_t h = sm.hist[b0 + j];
+      if (a < kk && kk <= a + h) {
+        sm.bc[0] = b0 + j;
+        sm.bc[1] = a;
+      }
+      a += h;
+    }
+  }
   lds_barrier();
   const uint32_t tb = sm.bc[0];
   const uint32_t need = kk - sm.bc[1];  // rank of the answer inside bin tb
