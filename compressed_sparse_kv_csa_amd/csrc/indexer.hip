@@ -217,10 +217,10 @@ __device__ __forceinline__ void query_frags_fp4h(const QueryRaw<KeyTileFp4, HT, 
   lds_barrier();
 }
 
-// Head weight h = threadIdx.x of query b (threads below 16 * HT; zero past n_heads),
-// loaded at kernel entry ahead of the key loads.  The weights reach every lane through
-// LDS: loaded straight into the registers the tile loop reads, their completion would be
-// waited for behind the key prefetches at the top of every pass.
+// Head weight h = threadIdx.x of query b (zero past n_heads; threads from 16 * HT on are
+// not used), loaded at kernel entry ahead of the key loads.  The weights reach every lane
+// through LDS: loaded straight into the registers the tile loop reads, their completion
+// would be waited for behind the key prefetches in the tile loop.
 template <int HT>
 __device__ __forceinline__ float query_weight_load(const float* __restrict__ w_idx, int b,
                                                    int n_heads) {
