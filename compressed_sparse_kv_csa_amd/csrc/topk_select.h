@@ -293,10 +293,6 @@ __device__ void slice_threshold(const uint32_t (&key)[R], int n, int P, uint32_t
   *cnt = sm.bc[1];
 }
 
-// The k-th largest of n distinct nonzero 64-bit keys held in LDS (1 <= k <= n).  A
-// histogram of the keys' high words (2048 bins between their min and max) locates the
-// bin holding it; if that whole bin is needed the answer is its smallest key, otherwise
-// the bin's keys are ranked directly (general radix passes if the bin is very full).
 // The k-th largest of n distinct nonzero 64-bit keys held in LDS (1 <= k <= n), given
 // the minimum mn and maximum mx of their high words, with sm.hist zeroed and sm.bc[4] = 0
 // before the caller's last barrier.  A histogram of the high words (2048 bins between mn
