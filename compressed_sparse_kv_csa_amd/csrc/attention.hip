@@ -1084,6 +1084,7 @@ hipError_t launch_attention(int kv_fmt, bool csa, const uint8_t* codes, const ui
   if (plan.n_chunks <= 2) CSAKV_COMBINE(2);
   else if (plan.n_chunks <= 4) CSAKV_COMBINE(4);
   else if (plan.n_chunks <= 8) CSAKV_COMBINE(8);
+  else if (plan.n_chunks <= 12) CSAKV_COMBINE(12);
   else if (plan.n_chunks <= 16) CSAKV_COMBINE(16);
   else CSAKV_COMBINE(kCombineMaxBatch);
 #undef CSAKV_COMBINE

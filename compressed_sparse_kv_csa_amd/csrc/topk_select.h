@@ -494,7 +494,10 @@ __device__ void merge_query(const IndexerWs& ws, int64_t n_c, const int32_t* __r
   // Candidate counts -> offsets in the buffer (n_slices <= NT); on the way, the histogram
   // of the k-th key search is cleared, and the high words' range of the placed keys taken.
   for (int i = threadIdx.x; i < kHistBins; i += NT) sm.hist[i] = 0;
-  if (threadIdx.x == 0) sm.bc[4] = 0;
+  if (threadIdx.x == 0) {
+    sm.bc[4] = 0;
+    sm.bc[5] = 0;  // set below when a slice saturates
+  }
   uint32_t hmn = ~0u, hmx = 0u;
   const uint32_t c = threadIdx.x < n_slices ? ws.count[s0 + threadIdx.x] : 0u;
   if (threadIdx.x < n_slices) s_bound[threadIdx.x] = ws.bound[s0 + threadIdx.x];
@@ -548,8 +551,11 @@ __device__ void merge_query(const IndexerWs& ws, int64_t n_c, const int32_t* __r
   uint64_t kth = (int)n_buf >= k1 ? block_kth_in_range<NT>(s_buf, (int)n_buf, k1, sm, s_list, hmn, hmx) : 1ull;
 
   // Slices whose bound lies above kth may hold winners among the keys they did not send.
-  {
-    const uint32_t sat = threadIdx.x < n_slices && s_bound[threadIdx.x] > kth;
+  // Usually none does: a flag and one barrier settle that before any scan.
+  const uint32_t sat = threadIdx.x < n_slices && s_bound[threadIdx.x] > kth;
+  if (sat) sm.bc[5] = 1u;
+  lds_barrier();
+  if (sm.bc[5] != 0u) {
     uint32_t n_sat;
     const uint32_t pos = block_exclusive_scan<NT>(sat, sm.wsum, &n_sat);
     if (sat) s_sat[pos] = threadIdx.x;
