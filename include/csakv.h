@@ -21,7 +21,8 @@
  * Conventions shared by every entry point
  *   - All data pointers are DEVICE pointers into memory the caller owns (for
  *     example PyTorch tensors).  The library never allocates or frees device
- *     memory, keeps no pointer after a call returns and has no global state.
+ *     memory, keeps no pointer after a call returns and has no global state,
+ *     except the fixed device scratch that csa_decode_noalloc alone uses.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *     default stream).  No call synchronises.  Device faults surface at the
  *     caller's next synchronisation.
