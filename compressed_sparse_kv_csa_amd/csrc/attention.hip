@@ -214,6 +214,43 @@ struct StepRaw<2> {
   }
 };
 
+// ---------------------------------------------------------------- partial records
+
+// A chunk's partial output is stored divided by the chunk's own sum of probabilities: a
+// convex combination of the chunk's rows, so no element exceeds the rows' largest.  For
+// FP8 and FP4 rows, which reach the products as fp16 and meet fp16 probabilities, the
+// records are fp16 (rounded to nearest even; in range by the rows' bound below 65504);
+// for bf16 rows they stay fp32.  Four consecutive elements at a time.
+template <int KVFMT>
+struct PartialRecord {
+  static constexpr bool kHalf = KVFMT != 0;
+};
+
+template <bool H16>
+__device__ __forceinline__ void store_partial4(float* part_o, int64_t elem, f32x4 v) {
+  if constexpr (H16) {
+    const f16x2 lo = {(_Float16)v[0], (_Float16)v[1]};
+    const f16x2 hi = {(_Float16)v[2], (_Float16)v[3]};
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(part_o) + elem) =
+        u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+  } else {
+    *reinterpret_cast<f32x4*>(part_o + elem) = v;
+  }
+}
+
+template <bool H16>
+__device__ __forceinline__ f32x4 load_partial4(Rsrc r, uint32_t byte_off) {
+  if constexpr (H16) {
+    // The whole 8-byte load is reinterpreted at once: hipcc folded a bit-cast of the
+    // second element of a two-element vector into one of the first.
+    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+    const f16x4 h = __builtin_bit_cast(f16x4, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
+    return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+  } else {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+  }
+}
+
 // ---------------------------------------------------------------- narrow workgroups
 // Short row lists (CSA: window + top-k rows) run on narrow workgroups of 16 heads and 4
 // waves, which spread one query's list over more compute units; long lists (HCA) run on
@@ -599,17 +636,18 @@ __device__ __forceinline__ void narrow_chunk(
   }
   if (step < n_steps) run_step(raw0, step);
 
-  // ---- partial records: the 16 x 512 output block is staged through LDS so that each
-  // head's 2 KB record is written by consecutive lanes in whole cache lines; the
-  // (max, sum) pairs go to their own array.
+  // ---- partial records: the 16 x 512 output block, divided by each head's sum, is
+  // staged through LDS so that each head's record is written by consecutive lanes in
+  // whole cache lines; the (max, sum) pairs go to their own array.
   const int64_t rec0 = ((int64_t)b * n_chunks + chunk) * n_heads + 16 * hg;
   lds_barrier();  // every wave is done with the tiles and the query rows
   if (wave == 0 && g == 0)
     *reinterpret_cast<f32x2*>(part_ml + (rec0 + n) * 2) = f32x2{l_run > 0.0f ? m_run : -INFINITY, l_run};
   {
+    const float il = l_run > 0.0f ? 1.0f / l_run : 0.0f;
     float* orow = s_out + n * kOutPitch + kNarrowDims * wave + 4 * g;
 #pragma unroll
-    for (int i = 0; i < kNarrowDims / 16; ++i) *reinterpret_cast<f32x4*>(orow + 16 * i) = o[i];
+    for (int i = 0; i < kNarrowDims / 16; ++i) *reinterpret_cast<f32x4*>(orow + 16 * i) = o[i] * il;
   }
   lds_barrier();
   constexpr int kVecPerHead = kDim / 4;
@@ -617,8 +655,8 @@ __device__ __forceinline__ void narrow_chunk(
   for (int k = 0; k < 16 * kVecPerHead / kNarrowThreads; ++k) {
     const int i = threadIdx.x + k * kNarrowThreads;
     const int h = i / kVecPerHead, c4 = i - h * kVecPerHead;
-    *reinterpret_cast<f32x4*>(part_o + (rec0 + h) * kDim + 4 * c4) =
-        *reinterpret_cast<const f32x4*>(s_out + h * kOutPitch + 4 * c4);
+    store_partial4<PartialRecord<KVFMT>::kHalf>(part_o, (rec0 + h) * kDim + 4 * c4,
+                                                *reinterpret_cast<const f32x4*>(s_out + h * kOutPitch + 4 * c4));
   }
 }
 
@@ -855,24 +893,27 @@ __global__ __launch_bounds__(kWideThreads) void attention_wide_kernel(
     if (step + k < n_steps) run_step(raw[k], step + k);
   if (!active) return;
 
-  // ---- partial records: (max, sum) per head, and the wave's 256 dims of each head's
-  // unnormalised O (four lanes write 64 contiguous bytes of one head's record).
+  // ---- partial records: (max, sum) per head, and the wave's 256 dims of each head's O
+  // divided by the head's sum (four lanes write contiguous pieces of one head's record).
   const int64_t rec = ((int64_t)b * n_chunks + chunk) * n_heads + head0 + n;
   if (kh == 0 && g == 0)
     *reinterpret_cast<f32x2*>(part_ml + rec * 2) = f32x2{l_run > 0.0f ? m_run : -INFINITY, l_run};
-  float* orow = part_o + rec * kDim + kHalfDim * kh + 4 * g;
+  const float il = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+  const int64_t e0 = rec * kDim + kHalfDim * kh + 4 * g;
 #pragma unroll
-  for (int i = 0; i < kHalfDim / 16; ++i) *reinterpret_cast<f32x4*>(orow + 16 * i) = o[i];
+  for (int i = 0; i < kHalfDim / 16; ++i)
+    store_partial4<PartialRecord<KVFMT>::kHalf>(part_o, e0 + 16 * i, o[i] * il);
 }
 
-// One workgroup per (query, head): merges the chunks' (max, sum, O) records.  NB chunks
+// One workgroup per (query, head): merges the chunks' (max, sum, O / sum) records (fp16
+// records when H16).  NB chunks
 // (the launch picks the smallest power of two covering the chunk count, at most
 // kCombineMaxBatch) are read in a single round of independent loads; more chunks take
 // further rounds.
 constexpr int kCombineThreads = 128;   // 4 dims each
 constexpr int kCombineMaxBatch = 32;
 
-template <int NB>
+template <int NB, bool H16>
 __global__ __launch_bounds__(kCombineThreads) void attention_combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml, int n_heads,
     int n_chunks, uint16_t* __restrict__ out) {
@@ -888,17 +929,19 @@ __global__ __launch_bounds__(kCombineThreads) void attention_combine_kernel(
   // are read through buffer resources that end with the last chunk's, so every load of a
   // round is issued unconditionally (a chunk past the last one reads zeros) and the
   // round's loads are in flight together.  The largest resource, 4096 chunks of 128
-  // heads, spans 1 GiB; with no chunks (an empty row list) both are empty.
-  const uint32_t cstride = (uint32_t)n_heads * kDim * 4;
+  // heads of fp32 records, spans 1 GiB; with no chunks (an empty row list) both are empty.
+  constexpr uint32_t kElemBytes = H16 ? 2 : 4;
+  const uint32_t cstride = (uint32_t)n_heads * kDim * kElemBytes;
   const int64_t rec0 = (int64_t)b * n_chunks * n_heads + h;
-  const Rsrc ro = make_rsrc(part_o + rec0 * kDim, n_chunks > 0 ? (uint32_t)(n_chunks - 1) * cstride + kDim * 4 : 0u);
+  const Rsrc ro = make_rsrc(reinterpret_cast<const uint8_t*>(part_o) + rec0 * kDim * kElemBytes,
+                            n_chunks > 0 ? (uint32_t)(n_chunks - 1) * cstride + kDim * kElemBytes : 0u);
   const Rsrc rm = make_rsrc(part_ml + rec0 * 2, n_chunks > 0 ? (uint32_t)(n_chunks - 1) * n_heads * 8 + 8 : 0u);
   const uint32_t d0 = 4 * threadIdx.x;
 
   f32x4 v[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i)
-    v[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, 4 * d0 + i * cstride, 0, 0));
+    v[i] = load_partial4<H16>(ro, kElemBytes * d0 + i * cstride);
   for (int c = threadIdx.x; c < n_chunks; c += kCombineThreads) {
     const f32x2 ml =
         __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rm, (uint32_t)c * n_heads * 8, 0, 0));
@@ -916,14 +959,13 @@ __global__ __launch_bounds__(kCombineThreads) void attention_combine_kernel(
       if (c0 > 0) {
 #pragma unroll
         for (int i = 0; i < NB; ++i)
-          v[i] = __builtin_bit_cast(
-              f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, 4 * d0 + (uint32_t)(c0 + i) * cstride, 0, 0));
+          v[i] = load_partial4<H16>(ro, kElemBytes * d0 + (uint32_t)(c0 + i) * cstride);
       }
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         if (c0 + i < n_chunks) {
-          const float wt = exp2f(s_m[c0 + i] - mmax);  // 0 for empty chunks (max -inf)
-          den += s_l[c0 + i] * wt;
+          const float wt = s_l[c0 + i] * exp2f(s_m[c0 + i] - mmax);  // 0 for empty chunks
+          den += wt;
           acc += v[i] * wt;
         }
       }
@@ -1045,9 +1087,27 @@ bool attention_supported(const AttnPlan& plan, int kv_fmt, int64_t n_rows) {
          n_rows * row_bytes <= (int64_t)kAttnMaxSeqBytes;
 }
 
-// Workspace: O records [B][chunks][H][512] fp32, then (max, sum) pairs [B][chunks][H][2].
+// Workspace: O records [B][chunks][H][512] fp32 (fp16 records for FP8 and FP4 rows fill
+// the first half of the same space), then (max, sum) pairs [B][chunks][H][2].
 size_t attention_workspace_bytes(int batch, int n_heads, const AttnPlan& plan) {
   return (size_t)batch * plan.n_chunks * n_heads * (kDim + 2) * sizeof(float);
+}
+
+template <bool H16>
+void launch_combine(hipStream_t stream, int batch, int n_heads, int n_chunks, const float* part_o,
+                    const float* part_ml, uint16_t* out) {
+  // A round's loads past the last chunk read nothing but still pass through the address
+  // unit, so the round is as short as the chunk count allows.
+#define CSAKV_COMBINE(NB)                                                                       \
+  hipLaunchKernelGGL((attention_combine_kernel<NB, H16>), dim3(batch * n_heads), dim3(kCombineThreads), \
+                     0, stream, part_o, part_ml, n_heads, n_chunks, out)
+  if (n_chunks <= 2) CSAKV_COMBINE(2);
+  else if (n_chunks <= 4) CSAKV_COMBINE(4);
+  else if (n_chunks <= 8) CSAKV_COMBINE(8);
+  else if (n_chunks <= 12) CSAKV_COMBINE(12);
+  else if (n_chunks <= 16) CSAKV_COMBINE(16);
+  else CSAKV_COMBINE(kCombineMaxBatch);
+#undef CSAKV_COMBINE
 }
 
 hipError_t launch_attention(int kv_fmt, bool csa, const uint8_t* codes, const uint8_t* scales,
@@ -1076,18 +1136,10 @@ hipError_t launch_attention(int kv_fmt, bool csa, const uint8_t* codes, const ui
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // A round's loads past the last chunk read nothing but still pass through the address
-  // unit, so the round is as short as the chunk count allows.
-#define CSAKV_COMBINE(NB)                                                                       \
-  hipLaunchKernelGGL((attention_combine_kernel<NB>), dim3(batch * n_heads), dim3(kCombineThreads), \
-                     0, stream, part_o, part_ml, n_heads, plan.n_chunks, out)
-  if (plan.n_chunks <= 2) CSAKV_COMBINE(2);
-  else if (plan.n_chunks <= 4) CSAKV_COMBINE(4);
-  else if (plan.n_chunks <= 8) CSAKV_COMBINE(8);
-  else if (plan.n_chunks <= 12) CSAKV_COMBINE(12);
-  else if (plan.n_chunks <= 16) CSAKV_COMBINE(16);
-  else CSAKV_COMBINE(kCombineMaxBatch);
-#undef CSAKV_COMBINE
+  // The combine reads the records the chunk kernel wrote for this row format (FP8 and
+  // FP4 rows share the fp16 records).
+  if (kv_fmt == 0) launch_combine<PartialRecord<0>::kHalf>(stream, batch, n_heads, plan.n_chunks, part_o, part_ml, out);
+  else launch_combine<PartialRecord<1>::kHalf>(stream, batch, n_heads, plan.n_chunks, part_o, part_ml, out);
   return hipGetLastError();
 }
 
