@@ -46,8 +46,9 @@ constexpr int kIdxDim = 128;
 constexpr int kScanWaves = 8;
 constexpr int kScanThreads = kScanWaves * kWave;
 constexpr int kRing = 4;   // tiles in flight per wave (a group); divides kSliceRows / 16
-constexpr int kMergeThreads = 1024;
+constexpr int kMergeThreads = 512;  // one thread per slice count at most kMaxMergeSlices
 constexpr int kMergeFirstPerThread = kMergeFirstSlots / kMergeThreads;  // first-round slots per thread
+static_assert(kMaxMergeSlices <= kMergeThreads, "the merge reads one slice count per thread");
 
 // ------------------------------------------------------------------ key tiles
 
