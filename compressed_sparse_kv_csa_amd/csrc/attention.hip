@@ -906,10 +906,9 @@ __global__ __launch_bounds__(kWideThreads) void attention_wide_kernel(
 }
 
 // One workgroup per (query, head): merges the chunks' (max, sum, O / sum) records (fp16
-// records when H16).  NB chunks
-// (the launch picks the smallest power of two covering the chunk count, at most
-// kCombineMaxBatch) are read in a single round of independent loads; more chunks take
-// further rounds.
+// records when H16).  NB chunks (the launch picks the smallest of 2, 4, 8, 12, 16 and
+// kCombineMaxBatch that covers the chunk count) are read in a single round of
+// independent loads; more chunks take further rounds.
 constexpr int kCombineThreads = 128;   // 4 dims each
 constexpr int kCombineMaxBatch = 32;
 
