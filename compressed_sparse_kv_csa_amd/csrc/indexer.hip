@@ -168,18 +168,33 @@ struct QueryRaw {
   }
 };
 
+// Rotated FP4 queries: whether a second wave quantises half of each head tile, and the
+// LDS the preparation needs.
+template <int HT, int NW>
+constexpr bool kFp4hSplit = 2 * HT <= NW;
+
+template <int HT, int NW>
+constexpr size_t fp4h_stage_bytes() {
+  return sizeof(f16x8) * HT * 4 * kWave + (kFp4hSplit<HT, NW> ? sizeof(float) * HT * 16 * kWave : 0);
+}
+
 // Hadamard-rotated FP4 indexer queries (keys stored in the same form).  Wave w of the NW
 // waves prepares head tiles w, w + NW, ...; for head tile ht the 4 lanes g of head n's row hold its channels
 // 32g .. 32g+31 in fp64 and rotate the row together (stages h = 1..16 in registers, h = 32
 // and 64 across lanes g ^ 1 and g ^ 2; every sum is exact), round each value once to fp32
 // and scale it once, quantise their two 16-channel blocks with the FP4 codec, and leave the
 // decoded values (exact in fp16, in the FP4 key tile's channel order) in LDS, from where
-// every wave takes its A operands.  `stage` holds HT * 4 * 64 fragments; it is free again
-// when this returns.
+// every wave takes its A operands.  With at most NW / 2 head tiles, wave ht + NW / 2
+// quantises the second block of wave ht's lanes (handed over through LDS) while wave ht
+// quantises the first.  `stage` holds HT * 4 * 64 fragments, and then HT * 16 * 64 floats
+// when the blocks are split; it is free again when this returns.
 template <int HT, int NW>
 __device__ __forceinline__ void query_frags_fp4h(const QueryRaw<KeyTileFp4, HT, NW>& raw, int wave, int g,
                                                  f16x8 (&qa)[HT][4], f16x8* stage) {
+  constexpr bool kSplit = kFp4hSplit<HT, NW>;
+  float* const handover = reinterpret_cast<float*>(stage + HT * 4 * kWave);  // kSplit only
   const int lane = threadIdx.x & (kWave - 1);
+  float yf[32];
 #pragma unroll
   for (int i = 0; i < QueryRaw<KeyTileFp4, HT, NW>::kPer; ++i) {
     const int ht = wave + NW * i;
@@ -197,18 +212,39 @@ __device__ __forceinline__ void query_frags_fp4h(const QueryRaw<KeyTileFp4, HT, 
     hadamard_stages<32>(y);
     hadamard_lane_stage<32>(y, 16, (g & 1) != 0);  // h = 32: lanes g, g ^ 1
     hadamard_lane_stage<32>(y, 32, (g & 2) != 0);  // h = 64: lanes g, g ^ 2
-    float yf[32];
 #pragma unroll
     for (int j = 0; j < 32; ++j) yf[j] = hadamard_round_scale(y[j]);
-    u32x2 c0, c1;
-    uint32_t s0, s1;
-    fp4_block_f32(yf, &c0, &s0);
-    fp4_block_f32(yf + 16, &c1, &s1);
-    f16x8* out = stage + ht * 4 * kWave + lane;
-    out[0 * kWave] = fp4x8_to_f16(c0[0], s0);
-    out[1 * kWave] = fp4x8_to_f16(c0[1], s0);
-    out[2 * kWave] = fp4x8_to_f16(c1[0], s1);
-    out[3 * kWave] = fp4x8_to_f16(c1[1], s1);
+    if constexpr (kSplit) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) handover[(ht * 16 + j) * kWave + lane] = yf[16 + j];
+    } else {
+      u32x2 c0, c1;
+      uint32_t s0, s1;
+      fp4_block_f32(yf, &c0, &s0);
+      fp4_block_f32(yf + 16, &c1, &s1);
+      f16x8* out = stage + ht * 4 * kWave + lane;
+      out[0 * kWave] = fp4x8_to_f16(c0[0], s0);
+      out[1 * kWave] = fp4x8_to_f16(c0[1], s0);
+      out[2 * kWave] = fp4x8_to_f16(c1[0], s1);
+      out[3 * kWave] = fp4x8_to_f16(c1[1], s1);
+    }
+  }
+  if constexpr (kSplit) {  // kPer is 1: wave ht < HT holds its first block in yf
+    lds_barrier();
+    const int ht = wave < NW / 2 ? wave : wave - NW / 2;
+    if (ht < HT) {  // wave-uniform
+      const bool second = wave >= NW / 2;
+      if (second) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) yf[j] = handover[(ht * 16 + j) * kWave + lane];
+      }
+      u32x2 c;
+      uint32_t sc;
+      fp4_block_f32(yf, &c, &sc);
+      f16x8* out = stage + (ht * 4 + (second ? 2 : 0)) * kWave + lane;
+      out[0] = fp4x8_to_f16(c[0], sc);
+      out[kWave] = fp4x8_to_f16(c[1], sc);
+    }
   }
   lds_barrier();
 #pragma unroll
@@ -447,6 +483,7 @@ __global__ __launch_bounds__(kScanThreads) void indexer_scan_kernel(
   Op qa[HT][4];
   float wv[HT][4];
   static_assert(sizeof(s_part) >= sizeof(f16x8) * HT * 4 * kWave, "query stage");
+  static_assert(!QH || sizeof(s_part) >= fp4h_stage_bytes<HT, kScanWaves>(), "rotated query stage");
   static_assert(sizeof(sm.hist) >= sizeof(float) * 16 * HT, "weight stage");
   static_assert(sizeof(sm.red32) >= sizeof(float) * HT, "query maxima");
   query_setup<KT, HT, QH, kScanWaves>(qraw, w_pre, wave, g, qa, wv, s_part,
@@ -615,7 +652,10 @@ __global__ __launch_bounds__(kReindexScoreThreads) void reindex_score_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx, int n_heads,
     const int32_t* __restrict__ pool, int n_pool, int n_parts, uint64_t* __restrict__ keys) {
   typedef typename KT::Op Op;
-  __shared__ u32x4 s_stage[HT * 4 * kWave];  // query fragments of the HT head tiles
+  // Query fragments of the HT head tiles (and, for rotated queries split over two waves,
+  // the handed-over values).
+  constexpr size_t kStageBytes = QH ? fp4h_stage_bytes<HT, kReindexScoreWaves>() : sizeof(u32x4) * HT * 4 * kWave;
+  __shared__ u32x4 s_stage[kStageBytes / sizeof(u32x4)];
   __shared__ float s_red[HT];
   __shared__ float s_w[16 * HT];
   args_in_sgprs(codes, scales, seq_stride, pg.table, pg.page_shift, pg.table_stride, n_c_max, seq_rows,
